@@ -1,0 +1,467 @@
+"""Pins for the fp64 CPU oracle: it is checked against facts that do not come
+from itself -- published generator outputs, a library's float32 arithmetic,
+a library's bf16 widening and softmax, brute-force enumeration on tiny
+vocabularies, closed forms and the invariants the method must satisfy.
+
+Each mistake a plausible oracle bug would make (a dropped penalty term, a
+wrong tie-break, >= instead of > in the draw, renormalising between filters,
+measuring top-p against the kept mass instead of the full mass) fails at
+least one test here; ``test_planted_mistakes_are_caught`` plants some of
+them in the oracle and checks that a pin goes red.
+"""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+
+from oracle import sampler as o
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_params
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _p(**kw):
+    return make_params(1, **kw)[0]
+
+
+def _f32_row(vals):
+    return np.asarray(vals, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------
+# SplitMix64
+# --------------------------------------------------------------------------
+def test_splitmix64_published_outputs():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "splitmix64_seed0.txt")) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 10
+    for k, hexval in rows:
+        assert o.splitmix64_output(0, int(k)) == int(hexval, 16)
+
+
+def test_counter_keying_and_uniform():
+    # (seed, row, step) -> output number n + 1, n = step * 2**32 + row
+    assert o.uniform_bits(0, 0, 0) == o.splitmix64_output(0, 1)
+    assert o.uniform_bits(0, 1, 0) == o.splitmix64_output(0, 2)
+    assert o.uniform_bits(0, 5, 1) == o.splitmix64_output(0, (1 << 32) + 6)
+    # seed shifts the whole stream: state seed + k*gamma
+    assert o.uniform_bits(o.SPLITMIX_GAMMA, 0, 0) == o.splitmix64_output(0, 2)
+    u = o.uniform(0, 0, 0)
+    assert u == (0xE220A8397B1DCDAF >> 11) / 2.0 ** 53
+    assert 0.0 <= u < 1.0
+    # the 53-bit uniform is exact: scaling back gives the integer
+    for r in range(50):
+        x = o.uniform_bits(7, r, 3)
+        assert o.uniform(7, r, 3) * 2.0 ** 53 == float(x >> 11)
+
+
+def test_uniform_distribution_is_uniform():
+    us = np.array([o.uniform(123, r, s) for r in range(100) for s in range(200)])
+    assert scipy.stats.kstest(us, "uniform").pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------
+# widening (exhaustive over all bf16 patterns)
+# --------------------------------------------------------------------------
+def test_widen_bf16_exhaustive_against_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = o.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    visited = 0
+    for i in range(65536):
+        r = ref[i]
+        if np.isnan(r):
+            assert ours[i] == -np.inf
+        elif r == 0:
+            assert ours[i] == 0 and not np.signbit(ours[i])
+        else:
+            assert ours[i] == r
+        visited += 1
+    assert visited == 65536
+    # ordering of the widened values matches float ordering of torch's values
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.argsort(ours[finite], kind="stable"), np.argsort(np.where(ref[finite] == 0, 0, ref[finite]), kind="stable"))
+
+
+def test_widen_f32_rules():
+    z = o.widen(_f32_row([np.nan, -0.0, 0.0, -np.inf, np.inf, 1.5]), "f32")
+    assert z[0] == -np.inf and z[3] == -np.inf and z[4] == np.inf and z[5] == np.float32(1.5)
+    assert not np.signbit(z[1]) and not np.signbit(z[2])
+
+
+def test_bf16_rounding_generator_roundtrip():
+    x = np.random.default_rng(0).normal(0, 5, 10000).astype(np.float32)
+    b = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(bf16_bits_to_f32(b), ref)
+
+
+# --------------------------------------------------------------------------
+# penalties: binary32 emulation against numpy's float32 arithmetic
+# --------------------------------------------------------------------------
+def _np_penalty(z, c, pres, freq, rep):
+    z = np.float32(z)
+    if not (rep == 1.0 or rep == 0.0):
+        z = z / np.float32(rep) if z > 0 else z * np.float32(rep)
+    if freq != 0.0:
+        z = z - np.float32(freq) * np.float32(c)
+    if pres != 0.0:
+        z = z - np.float32(pres)
+    return np.float32(z)
+
+
+def test_penalty_matches_numpy_float32():
+    rng = np.random.default_rng(1)
+    for _ in range(20000):
+        z = float(np.float32(rng.normal(0, 8)))
+        c = int(rng.integers(1, 3000))
+        pres = float(np.float32(rng.choice([0.0, rng.uniform(-2, 2)])))
+        freq = float(np.float32(rng.choice([0.0, rng.uniform(-2, 2)])))
+        rep = float(np.float32(rng.choice([1.0, 0.0, rng.uniform(0.1, 3)])))
+        ours = np.float32(o.penalize_one(z, c, pres, freq, rep))
+        ref = _np_penalty(z, c, pres, freq, rep)
+        assert ours.view(np.uint32) == ref.view(np.uint32) or (ours == 0 and ref == 0), (z, c, pres, freq, rep)
+
+
+def test_penalty_hand_cases():
+    # repetition divides positive logits and multiplies the rest
+    assert o.penalize_one(2.2, 1, 0.0, 0.0, 1.1) == float(np.float32(2.2) / np.float32(1.1))
+    assert o.penalize_one(-2.0, 1, 0.0, 0.0, 2.0) == -4.0
+    assert o.penalize_one(0.0, 1, 0.0, 0.0, 2.0) == 0.0
+    # frequency scales with the count, presence does not
+    assert o.penalize_one(1.0, 3, 0.0, 0.5, 1.0) == -0.5
+    assert o.penalize_one(1.0, 3, 0.25, 0.0, 1.0) == 0.75
+    # order: repetition, then frequency, then presence
+    assert o.penalize_one(3.0, 2, 1.0, 0.5, 2.0) == 3.0 / 2.0 - 1.0 - 1.0
+
+
+def test_penalty_off_values_leave_logits_bit_identical():
+    rng = np.random.default_rng(2)
+    z = rng.normal(0, 4, 512).astype(np.float32)
+    hist = rng.integers(-5, 600, 300).astype(np.int32)
+    for pres, freq, rep in [(0.0, 0.0, 1.0), (0.0, 0.0, 0.0)]:
+        out = o.penalize(z, hist, pres, freq, rep)
+        assert np.array_equal(out.view(np.uint32), z.view(np.uint32))
+    # a multiplier-0 penalty is a no-op; a non-zero one is not
+    assert not np.array_equal(o.penalize(z, hist, 0.5, 0.0, 1.0), z)
+
+
+def test_penalty_counts_duplicates_and_skips_out_of_range():
+    z = np.zeros(8, dtype=np.float32) + 1.0
+    hist = np.array([3, 3, 3, 5, -1, 8, 100], dtype=np.int32)
+    out = o.penalize(z, hist, 0.0, 0.25, 1.0)
+    assert out[3] == 1.0 - 0.75 and out[5] == 0.75
+    assert np.all(out[[0, 1, 2, 4, 6, 7]] == 1.0)
+
+
+# --------------------------------------------------------------------------
+# argmax
+# --------------------------------------------------------------------------
+def _bf_argmax(z):
+    best = 0
+    for i in range(len(z)):
+        if z[i] > z[best]:
+            best = i
+    return best
+
+
+def test_argmax_bruteforce_with_ties():
+    rng = np.random.default_rng(3)
+    for _ in range(500):
+        V = int(rng.integers(1, 40))
+        raw = rng.integers(-3, 4, V).astype(np.float32)
+        z = o.widen(raw, "f32")
+        assert o.argmax_first(z) == _bf_argmax(z)
+
+
+def test_argmax_special_rows():
+    assert o.argmax_first(o.widen(_f32_row([1, 1, 1, 1]), "f32")) == 0
+    assert o.argmax_first(o.widen(_f32_row([0, 1, 2, 3]), "f32")) == 3
+    assert o.argmax_first(o.widen(_f32_row([-1, -0.0, 0.0, -2]), "f32")) == 1   # -0 == +0
+    assert o.argmax_first(o.widen(_f32_row([np.nan, -np.inf, np.nan]), "f32")) == 0
+    assert o.argmax_first(o.widen(_f32_row([np.nan, 5, np.inf, np.inf]), "f32")) == 2
+    r = o.sample_row(_f32_row([-np.inf] * 5), "f32", _p(temperature=1.0), None, 0, 0, 0)
+    assert r.id == 0
+
+
+# --------------------------------------------------------------------------
+# kept sets: brute force on tiny vocabularies
+# --------------------------------------------------------------------------
+def _prec(z, a, b):
+    return z[a] > z[b] or (z[a] == z[b] and a < b)
+
+
+def _prefix_closed(z, S):
+    V = len(z)
+    return all(_prec(z, a, b) for a in S for b in range(V) if b not in S)
+
+
+def _bf_topk(z, k):
+    sols = [set(C) for C in itertools.combinations(range(len(z)), k) if _prefix_closed(z, set(C))]
+    assert len(sols) == 1
+    return sols[0]
+
+
+def _softmax_w(z, T):
+    zz = z.astype(np.float64)
+    return np.exp((zz - zz.max()) / T)
+
+
+def _bf_topp(z, w, p):
+    V = len(z)
+    target = p * math.fsum(w)
+    for n in range(1, V + 1):
+        ok = [set(C) for C in itertools.combinations(range(V), n) if math.fsum(w[list(C)]) >= target]
+        if ok:
+            closed = [C for C in ok if _prefix_closed(z, C)]
+            assert len(closed) == 1
+            return closed[0]
+    return set(range(V))
+
+
+def test_topk_set_bruteforce():
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        V = int(rng.integers(2, 10))
+        z = o.widen(rng.integers(-2, 3, V).astype(np.float32), "f32")
+        k = int(rng.integers(2, V + 1))
+        r = o.sample_row(z, "f32", _p(temperature=1.0, top_k=k), None, 1, 0, 0)
+        want = _bf_topk(z, min(k, V))
+        assert set(r.kept.tolist()) == want
+
+
+def test_topp_set_bruteforce():
+    rng = np.random.default_rng(5)
+    checked = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 10))
+        z = o.widen((rng.integers(-3, 3, V) + rng.choice([0, 0.5], V)).astype(np.float32), "f32")
+        T = float(np.float32(rng.uniform(0.3, 2.0)))
+        p = float(np.float32(rng.uniform(0.05, 0.99)))
+        r = o.sample_row(z, "f32", _p(temperature=T, top_p=p), None, 1, 0, 0)
+        if r.margin_p < 1e-12:
+            continue
+        want = _bf_topp(z, _softmax_w(z, T), p)
+        assert set(r.kept.tolist()) == want
+        checked += 1
+    assert checked > 250
+
+
+def test_minp_set_against_softmax_definition():
+    rng = np.random.default_rng(6)
+    for _ in range(200):
+        V = int(rng.integers(2, 30))
+        z = o.widen(rng.normal(0, 2, V).astype(np.float32), "f32")
+        T = float(np.float32(rng.uniform(0.3, 2.0)))
+        mp = float(np.float32(rng.uniform(0.01, 0.9)))
+        r = o.sample_row(z, "f32", _p(temperature=T, min_p=mp), None, 1, 0, 0)
+        q = scipy.special.softmax(z.astype(np.float64) / T)
+        want = set(np.nonzero(q >= mp * q.max() * (1 - 1e-15))[0].tolist())
+        if r.margin_m < 1e-9:
+            continue
+        assert set(r.kept.tolist()) == want
+
+
+def test_combined_filters_take_the_shortest_prefix_without_renormalising():
+    # weights 0.4 0.3 0.2 0.1 (as logits).  top_p = 0.75 measured on the FULL
+    # mass needs 3 tokens (0.4+0.3 < 0.75); renormalising after the top_k=3
+    # cut would compare against 0.75*0.9 = 0.675 and keep only 2.
+    w = np.array([0.4, 0.3, 0.2, 0.1])
+    z = np.log(w).astype(np.float32)
+    r = o.sample_row(z, "f32", _p(temperature=1.0, top_k=3, top_p=0.65), None, 0, 0, 0)
+    assert set(r.kept.tolist()) == {0, 1}
+    r = o.sample_row(z, "f32", _p(temperature=1.0, top_k=3, top_p=0.75), None, 0, 0, 0)
+    assert set(r.kept.tolist()) == {0, 1, 2}
+    # min-p relative to the max: 0.2/0.4 = 0.5 kept at min_p 0.45, 0.1/0.4 dropped
+    r = o.sample_row(z, "f32", _p(temperature=1.0, min_p=0.45), None, 0, 0, 0)
+    assert set(r.kept.tolist()) == {0, 1, 2}
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def test_all_equal_logits_closed_forms():
+    V = 37
+    z = np.zeros(V, dtype=np.float32) + 0.5
+    for k in (1, 2, 5, 36):
+        r = o.sample_row(z, "f32", _p(temperature=1.0, top_k=k + (k == 1)), None, 0, 0, 0)
+        kk = k + (k == 1)
+        assert r.kept.tolist() == list(range(kk))
+    for p in (0.1, 0.33, 0.5, 0.77, 0.99):
+        assert (p * V) % 1 != 0
+        r = o.sample_row(z, "f32", _p(temperature=0.8, top_p=p), None, 0, 0, 0)
+        assert r.L == math.ceil(np.float32(p) * V)
+        assert r.kept.tolist() == list(range(r.L))
+
+
+def test_two_level_row_probabilities():
+    # a logits, b logits, delta = a - b: each top token has q = 1 / (na + nb * e^(-delta/T))
+    na, nb, delta, T = 3, 5, 1.25, 0.7
+    z = np.array([0.0] * nb + [delta] * na, dtype=np.float32)
+    r = o.sample_row(z, "f32", _p(temperature=T), None, 0, 0, 0, want_probs=True)
+    qa = 1.0 / (na + nb * math.exp(-delta / T))
+    qb = math.exp(-delta / T) * qa
+    assert np.allclose(r.probs[nb:], qa, rtol=1e-14) and np.allclose(r.probs[:nb], qb, rtol=1e-14)
+
+
+def test_no_filter_probs_equal_library_softmax():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        V = int(rng.integers(2, 3000))
+        z = o.widen(rng.normal(0, 3, V).astype(np.float32), "f32")
+        T = float(np.float32(rng.uniform(0.2, 2.0)))
+        r = o.sample_row(z, "f32", _p(temperature=T, top_k=-1, top_p=1.0, min_p=0.0), None, 0, 0, 0,
+                         want_probs=True)
+        assert r.L == V
+        ref = scipy.special.softmax(z.astype(np.float64) / T)
+        assert np.allclose(r.probs, ref, rtol=1e-12, atol=0)
+        assert abs(math.fsum(r.probs.tolist()) - 1.0) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# the draw
+# --------------------------------------------------------------------------
+def test_draw_crafted_uniforms():
+    z = np.zeros(4, dtype=np.float32)
+    p = _p(temperature=1.0)
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.25).id == 1    # t = 1.0, strict >
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.0).id == 0
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=1 - 2 ** -53).id == 3
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.2499999).id == 0
+    # the draw walks kept ids in id order, not in value order
+    z = np.array([0.0, 5.0, 0.0, 5.0], dtype=np.float32)
+    p = _p(temperature=1.0, top_k=2)
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.1).id == 1
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.9).id == 3
+
+
+def _chisq(counts, expected):
+    keep = expected >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    exp = np.append(expected[keep], expected[~keep].sum())
+    if exp[-1] == 0:
+        obs, exp = obs[:-1], exp[:-1]
+    return scipy.stats.chisquare(obs, exp * obs.sum() / exp.sum()).pvalue
+
+
+def test_chi_square_one_million_seeded_draws():
+    rng = np.random.default_rng(8)
+    V = 48
+    z = o.widen(rng.normal(0, 1.5, V).astype(np.float32), "f32")
+    p = _p(temperature=0.9, top_k=30, top_p=0.93, min_p=0.01)
+    base = o.sample_row(z, "f32", p, None, 11, 0, 0, want_probs=True)
+    N = 1_000_000
+    us = np.fromiter(((o.uniform_bits(11, 0, s) >> 11) * 2.0 ** -53 for s in range(N)), dtype=np.float64, count=N)
+    ids, _ = o.draw(base.kept, base.probs[base.kept], us)
+    counts = np.bincount(ids, minlength=V).astype(np.float64)
+    assert counts[np.setdiff1d(np.arange(V), base.kept)].sum() == 0
+    pval = _chisq(counts[base.kept], base.probs[base.kept] * N)
+    assert pval > 1e-3, pval
+    # spot-check that the vectorised draw is the per-row draw
+    for s in (0, 1, 2, 999_999):
+        assert o.sample_row(z, "f32", p, None, 11, 0, s).id == ids[s]
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+def test_argmax_equals_topk1_equals_temperature_to_zero():
+    rng = np.random.default_rng(9)
+    for i in range(100):
+        V = int(rng.integers(2, 500))
+        z = o.widen(rng.normal(0, 2, V).astype(np.float32), "f32")
+        am = o.argmax_first(z)
+        for u in (0.0, 0.3, 0.999):
+            assert o.sample_row(z, "f32", _p(temperature=1.3, top_k=1), None, 0, i, 0, u_override=u).id == am
+        assert o.sample_row(z, "f32", _p(temperature=0.0), None, 0, i, 0).id == am
+        if np.count_nonzero(z == z[am]) == 1:
+            assert o.sample_row(z, "f32", _p(temperature=1e-6), None, 0, i, 0).id == am
+
+
+def test_temperature_to_zero_with_tied_maximum_is_uniform_over_ties():
+    z = np.array([1.0, 3.0, 0.5, 3.0, 3.0, 2.9], dtype=np.float32)
+    p = _p(temperature=1e-4)
+    ids = [o.sample_row(z, "f32", p, None, 5, 0, s).id for s in range(30000)]
+    counts = np.bincount(ids, minlength=6)
+    assert counts[[0, 2, 5]].sum() == 0
+    assert scipy.stats.chisquare(counts[[1, 3, 4]]).pvalue > 1e-3
+
+
+def test_sort_skip_does_not_move_the_token():
+    # top_k=-1, top_p=1, min_p=0 is inert: a filter that is active but keeps
+    # every token (top_k >= V, min_p below every weight) draws the same token.
+    rng = np.random.default_rng(10)
+    for i in range(50):
+        V = int(rng.integers(2, 2000))
+        z = o.widen(rng.normal(0, 2, V).astype(np.float32), "f32")
+        a = o.sample_row(z, "f32", _p(temperature=0.8), None, 3, i, 0)
+        b = o.sample_row(z, "f32", _p(temperature=0.8, top_k=V + 3), None, 3, i, 0)
+        c = o.sample_row(z, "f32", _p(temperature=0.8, top_p=1.0, min_p=1e-38), None, 3, i, 0)
+        assert a.L == V and a.id == b.id
+        if c.L == V:
+            assert c.id == a.id
+
+
+def test_invalid_params_give_status_and_minus_one():
+    z = np.zeros(4, dtype=np.float32)
+    cases = [(dict(temperature=-1.0), o.ROW_BAD_TEMPERATURE), (dict(temperature=np.nan), o.ROW_BAD_TEMPERATURE),
+             (dict(top_p=0.0), o.ROW_BAD_TOP_P), (dict(top_p=np.nan), o.ROW_BAD_TOP_P),
+             (dict(min_p=-0.1), o.ROW_BAD_MIN_P), (dict(min_p=1.5), o.ROW_BAD_MIN_P),
+             (dict(repetition=-1.0), o.ROW_BAD_PENALTY), (dict(presence=np.inf), o.ROW_BAD_PENALTY),
+             (dict(flags=1), o.ROW_BAD_FLAGS)]
+    for kw, code in cases:
+        r = o.sample_row(z, "f32", _p(**kw), None, 0, 0, 0)
+        assert r.status == code and r.id == -1
+
+
+# --------------------------------------------------------------------------
+# anti-vacuity: planted mistakes must turn a pin red
+# --------------------------------------------------------------------------
+def _red(test_fn):
+    try:
+        test_fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    # highest-index tie-break in argmax
+    with monkeypatch.context() as m:
+        m.setattr(o, "argmax_first", lambda z: int(len(z) - 1 - np.argmax(z[::-1])))
+        assert _red(test_argmax_bruteforce_with_ties)
+    # >= instead of > in the draw
+    with monkeypatch.context() as m:
+        real = o.draw
+
+        def draw_ge(kept, wk, u):
+            u = np.atleast_1d(np.asarray(u, dtype=np.float64))
+            C = np.cumsum(wk.astype(np.longdouble))
+            t = u * math.fsum(wk.tolist())
+            pos = np.minimum(np.searchsorted(C, t, side="left"), len(C) - 1)
+            return kept[pos], np.ones_like(u)
+        m.setattr(o, "draw", draw_ge)
+        assert _red(test_draw_crafted_uniforms)
+        m.setattr(o, "draw", real)
+    # dropped frequency term
+    with monkeypatch.context() as m:
+        real_pen = o.penalize_one
+        m.setattr(o, "penalize_one", lambda z, c, pr, fr, rp: real_pen(z, c, pr, 0.0, rp))
+        assert _red(test_penalty_hand_cases)
+    # top-p measured against the mass kept by top-k (renormalisation)
+    with monkeypatch.context() as m:
+        real_cut = o.cutoff
+
+        def renorm(z, w, k, p, mp):
+            c = real_cut(z, w, k, 1.0, mp)
+            kept = c.order[: c.L]
+            c2 = real_cut(z[kept], w[kept], -1, p, 0.0)
+            c.L = min(c.L, c2.L)
+            return c
+        m.setattr(o, "cutoff", renorm)
+        assert _red(test_combined_filters_take_the_shortest_prefix_without_renormalising)
