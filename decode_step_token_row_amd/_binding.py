@@ -1,0 +1,230 @@
+"""ctypes binding of libarcs.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module checks
+tensor shapes, dtypes and devices, takes raw device pointers and the current
+HIP stream from PyTorch, and calls the C ABI of include/arcs.h with the same
+names.  It never falls back to any other implementation: if the library is
+missing or a call fails, it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libarcs.so")
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+# C enum values of include/arcs.h
+OK = 0
+ROW_OK = 0
+ROW_BAD_TEMPERATURE = 1
+ROW_BAD_TOP_P = 2
+ROW_BAD_MIN_P = 3
+ROW_BAD_PENALTY = 4
+ROW_BAD_FLAGS = 5
+ROW_HISTORY_TOO_LONG = 6
+ROW_VOCAB_TOO_LARGE = 7
+MAX_HISTORY = 4096
+MAX_PENALTY_VOCAB = 262144
+
+PATH_GREEDY = 1
+PATH_SORT_SKIP = 2
+PATH_CUTOFF = 4
+PATH_MINP_FLOOR = 8
+PATH_TIE_SPLIT = 16
+PATH_PENALTY = 32
+PATH_SPECIAL = 64
+
+# struct arcs_row_params (32 bytes)
+ROW_PARAMS_DTYPE = np.dtype(
+    [("temperature", "<f4"), ("top_k", "<i4"), ("top_p", "<f4"), ("min_p", "<f4"),
+     ("presence", "<f4"), ("frequency", "<f4"), ("repetition", "<f4"), ("flags", "<i4")]
+)
+# struct arcs_row_stats (64 bytes)
+ROW_STATS_DTYPE = np.dtype(
+    [("id", "<i4"), ("argmax", "<i4"), ("kept", "<i4"), ("cut_index", "<i4"),
+     ("cut_value", "<f4"), ("max_logit", "<f4"), ("status", "<i4"), ("path", "<u4"),
+     ("mass_total", "<f8"), ("mass_kept", "<f8"), ("uniform", "<f8"), ("reserved", "<u8")]
+)
+assert ROW_PARAMS_DTYPE.itemsize == 32 and ROW_STATS_DTYPE.itemsize == 64
+
+
+class ArcsError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: arcs status {code} ({status_string(code)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libarcs.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        c_i64, c_u64, c_p, c_i = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int
+        lib.arcs_argmax.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p]
+        lib.arcs_argmax.restype = c_i
+        lib.arcs_sample.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
+                                    c_p, c_p, c_p, ctypes.c_size_t, c_p]
+        lib.arcs_sample.restype = c_i
+        lib.arcs_sample_debug.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
+                                          c_p, c_p, c_p, ctypes.c_size_t, c_p, c_p, c_p, c_p]
+        lib.arcs_sample_debug.restype = c_i
+        lib.arcs_sample_workspace_bytes.argtypes = [c_i64, c_i64, c_i]
+        lib.arcs_sample_workspace_bytes.restype = ctypes.c_size_t
+        lib.arcs_status_string.argtypes = [c_i]
+        lib.arcs_status_string.restype = ctypes.c_char_p
+        lib.arcs_version.argtypes = []
+        lib.arcs_version.restype = c_i
+        _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return library().arcs_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return int(library().arcs_version())
+
+
+def workspace_bytes(B: int, V: int, dtype: int) -> int:
+    return int(library().arcs_sample_workspace_bytes(int(B), int(V), int(dtype)))
+
+
+# --------------------------------------------------------------------------
+# torch-facing helpers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_logits(logits):
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous (stride(1) == 1)")
+    return logits.shape[0], logits.shape[1], logits.stride(0)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def params_to_device(params: np.ndarray, device="cuda"):
+    """Copy a structured array of arcs_row_params records to the device (uint8 [B, 32])."""
+    torch = _torch()
+    arr = np.ascontiguousarray(params).view(np.uint8).reshape(len(params), 32)
+    return torch.from_numpy(arr.copy()).to(device)
+
+
+def argmax(logits, out=None, stream=None):
+    """out[b] = lowest index of the row maximum of logits[b] (int32, on device)."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    if out.dtype != torch.int32 or out.numel() != B or not out.is_cuda:
+        raise ValueError("out must be a device int32 tensor of B elements")
+    st = library().arcs_argmax(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(out), _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_argmax")
+    return out
+
+
+def _check_params(params, B):
+    torch = _torch()
+    if not params.is_cuda or params.dtype != torch.uint8 or params.numel() != 32 * B or not params.is_contiguous():
+        raise ValueError("params must be a contiguous device uint8 tensor of B * 32 bytes")
+
+
+def _check_hist(hist_ids, hist_offsets, B):
+    torch = _torch()
+    if (hist_ids is None) != (hist_offsets is None):
+        raise ValueError("hist_ids and hist_offsets go together")
+    if hist_ids is not None:
+        if hist_ids.dtype != torch.int32 or not hist_ids.is_cuda or not hist_ids.is_contiguous():
+            raise ValueError("hist_ids must be a contiguous device int32 tensor")
+        if hist_offsets.dtype != torch.int64 or not hist_offsets.is_cuda or hist_offsets.numel() != B + 1:
+            raise ValueError("hist_offsets must be a device int64 tensor of B + 1 elements")
+
+
+def sample(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step: int = 0,
+           out=None, out_status=None, workspace=None, stream=None):
+    """One token per row (int32, on device); see arcs_sample in include/arcs.h."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    _check_params(params, B)
+    _check_hist(hist_ids, hist_offsets, B)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=logits.device)
+        ws_bytes = ws_need
+    st = library().arcs_sample(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),
+                               _ptr(hist_ids), _ptr(hist_offsets), int(seed) & (2**64 - 1),
+                               int(step) & (2**64 - 1), _ptr(out), _ptr(out_status), _ptr(workspace),
+                               ws_bytes, _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample")
+    return out
+
+
+def sample_debug(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step: int = 0,
+                 uniforms=None, want_probs: bool = False, stream=None):
+    """arcs_sample_debug: returns (ids, status, stats[B] numpy structured, probs or None)."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    _check_params(params, B)
+    _check_hist(hist_ids, hist_offsets, B)
+    dev = logits.device
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    stats = torch.zeros(B * ROW_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    probs = torch.empty((B, V), dtype=torch.float32, device=dev) if want_probs else None
+    if uniforms is not None:
+        if uniforms.dtype != torch.float64 or not uniforms.is_cuda or uniforms.numel() != B:
+            raise ValueError("uniforms must be a device float64 tensor of B elements")
+    ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev) if ws_need else None
+    st = library().arcs_sample_debug(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),
+                                     _ptr(hist_ids), _ptr(hist_offsets), int(seed) & (2**64 - 1),
+                                     int(step) & (2**64 - 1), _ptr(out), _ptr(status), _ptr(workspace),
+                                     ws_need, _ptr(uniforms), _ptr(probs), _ptr(stats), _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample_debug")
+    torch.cuda.synchronize(dev)
+    st_np = stats.cpu().numpy().view(ROW_STATS_DTYPE)
+    return out, status, st_np, probs

@@ -1,0 +1,145 @@
+// C ABI of libarcs (declared in include/arcs.h): argument validation, launch
+// configuration and nothing else.  No allocation, no synchronisation, no
+// host reads of device memory: every call only enqueues kernels on the
+// caller's stream (Arc PR #217, "What this does" and "Layering": the
+// sampling step must not put a host round trip between decode steps).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arcs.h"
+#include "launch.hpp"
+
+
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647;
+
+int check_common(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                 const void* out_ids) {
+  if (logits == nullptr || out_ids == nullptr) return ARCS_ERR_NULL_POINTER;
+  if (dtype != ARCS_DTYPE_BF16 && dtype != ARCS_DTYPE_F32) return ARCS_ERR_BAD_DTYPE;
+  if (B <= 0 || B > kMaxDim) return ARCS_ERR_BAD_BATCH;
+  if (V <= 0 || V > kMaxDim) return ARCS_ERR_BAD_VOCAB;
+  if (row_stride < V) return ARCS_ERR_BAD_STRIDE;
+  const int64_t es = dtype == ARCS_DTYPE_BF16 ? 2 : 4;
+  if (((uintptr_t)logits) % (uintptr_t)es != 0) return ARCS_ERR_MISALIGNED;
+  return ARCS_OK;
+}
+
+// Rows start on a 16-byte boundary: the vector-load path applies.
+bool rows_16b_aligned(const void* logits, int dtype, int64_t row_stride) {
+  const int64_t es = dtype == ARCS_DTYPE_BF16 ? 2 : 4;
+  return ((uintptr_t)logits % 16u) == 0 && ((row_stride * es) % 16) == 0;
+}
+
+// Fixed-point fraction bits: V * 2^F < 2^63 so any sum of weights in [0, 1]
+// fits an unsigned 64-bit integer.
+int fixed_bits(int64_t V) {
+  int lg = 0;
+  while ((int64_t(1) << (lg + 1)) <= V) ++lg;  // floor(log2 V)
+  int F = 62 - lg;
+  return F > 62 ? 62 : F;
+}
+
+int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status,
+                void* workspace, size_t workspace_bytes, const double* uniforms, float* out_probs,
+                arcs_row_stats* out_stats, void* stream) {
+  int st = check_common(logits, dtype, B, V, row_stride, out_ids);
+  if (st != ARCS_OK) return st;
+  if (params == nullptr) return ARCS_ERR_NULL_POINTER;
+  if ((hist_ids == nullptr) != (hist_offsets == nullptr)) return ARCS_ERR_BAD_HISTORY;
+  if (workspace_bytes < arcs_sample_workspace_bytes(B, V, dtype)) return ARCS_ERR_WORKSPACE_TOO_SMALL;
+  (void)workspace;
+  arcs::SampleArgs a;
+  a.logits = logits;
+  a.V = V;
+  a.stride = row_stride;
+  a.params = params;
+  a.hist_ids = hist_ids;
+  a.hist_offsets = hist_offsets;
+  a.seed = seed;
+  a.step = step;
+  a.out_ids = out_ids;
+  a.out_status = out_status;
+  a.uniforms = uniforms;
+  a.out_probs = out_probs;
+  a.stats = out_stats;
+  a.F = fixed_bits(V);
+  a.scale = (float)((double)(int64_t(1) << a.F));
+  a.pen_tables = (hist_ids != nullptr && V <= ARCS_MAX_PENALTY_VOCAB) ? 1 : 0;
+  a.bitmap_words = a.pen_tables ? (uint32_t)((V + 31) / 32) : 0u;
+  hipError_t e = arcs::launch_sample(a, dtype, B, rows_16b_aligned(logits, dtype, row_stride),
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arcs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                int32_t* out_ids, void* stream) {
+  int st = check_common(logits, dtype, B, V, row_stride, out_ids);
+  if (st != ARCS_OK) return st;
+  hipError_t e = arcs::launch_argmax(logits, dtype, B, V, row_stride,
+                                     rows_16b_aligned(logits, dtype, row_stride), out_ids,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
+}
+
+int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step,
+                     out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                     stream);
+}
+
+int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const arcs_row_params* params, const int32_t* hist_ids,
+                      const int64_t* hist_offsets, uint64_t seed, uint64_t step,
+                      int32_t* out_ids, int32_t* out_status, void* workspace,
+                      size_t workspace_bytes, const double* uniforms, float* out_probs,
+                      arcs_row_stats* out_stats, void* stream) {
+  return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step,
+                     out_ids, out_status, workspace, workspace_bytes, uniforms, out_probs,
+                     out_stats, stream);
+}
+
+size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype) {
+  (void)B;
+  (void)V;
+  (void)dtype;
+  return 0;
+}
+
+const char* arcs_status_string(int code) {
+  switch (code) {
+    case ARCS_OK: return "ok";
+    case ARCS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case ARCS_ERR_BAD_BATCH: return "batch size B must be in [1, 2^31-1]";
+    case ARCS_ERR_BAD_VOCAB: return "vocabulary size V must be in [1, 2^31-1]";
+    case ARCS_ERR_BAD_STRIDE: return "row_stride must be >= V";
+    case ARCS_ERR_BAD_DTYPE: return "dtype must be ARCS_DTYPE_BF16 or ARCS_DTYPE_F32";
+    case ARCS_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than arcs_sample_workspace_bytes()";
+    case ARCS_ERR_LAUNCH: return "kernel launch failed";
+    case ARCS_ERR_MISALIGNED: return "logits pointer not aligned to its element size";
+    case ARCS_ERR_BAD_HISTORY: return "hist_ids and hist_offsets must both be NULL or both be set";
+    case ARCS_ROW_BAD_TEMPERATURE: return "row: temperature is NaN or negative";
+    case ARCS_ROW_BAD_TOP_P: return "row: top_p is NaN or <= 0";
+    case ARCS_ROW_BAD_MIN_P: return "row: min_p is NaN or outside [0, 1]";
+    case ARCS_ROW_BAD_PENALTY: return "row: a penalty is not finite or repetition < 0";
+    case ARCS_ROW_BAD_FLAGS: return "row: flags must be 0";
+    case ARCS_ROW_HISTORY_TOO_LONG: return "row: penalties need at most ARCS_MAX_HISTORY history ids";
+    case ARCS_ROW_VOCAB_TOO_LARGE: return "row: penalties need V <= ARCS_MAX_PENALTY_VOCAB";
+    default: return "unknown status";
+  }
+}
+
+int arcs_version(void) { return 100; }
+
+}  // extern "C"

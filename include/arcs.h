@@ -1,0 +1,194 @@
+/*
+ * arcs.h -- on-device batched token sampling for AMD Instinct MI355X (gfx950).
+ *
+ * The library turns a [B, V] logits tensor that already lives in GPU memory
+ * into one token id per row, without copying the logits to the host.  The
+ * pages it follows (the Arc engine's pull requests) price the host path it
+ * replaces: Arc PR #222 ("ARC_SAMPLE_ON_DEVICE", section 2) copies the whole
+ * [B, 1, vocab] logits tensor to the host every step and samples every row
+ * there; Arc PR #217 ("device decode loop", "What this does") keeps the
+ * greedy token in an i32[batch] device buffer instead.
+ *
+ * Conventions shared by every call:
+ *  - All array arguments are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing, keeps no state between calls, never
+ *    synchronises and never reads device memory from the host.  Work is
+ *    enqueued on `stream` (a hipStream_t; NULL means the default stream) and
+ *    the call returns.
+ *  - Logits are row-major: row b starts `b * row_stride` elements after
+ *    `logits`, `row_stride >= V`.  dtype ARCS_DTYPE_BF16 (raw bfloat16) or
+ *    ARCS_DTYPE_F32.  `logits` must be aligned to its element size; rows
+ *    whose start is 16-byte aligned take the vector-load path.
+ *  - Host-checkable argument errors are returned as a negative arcs_status
+ *    before anything is launched; nothing is written in that case.
+ *  - Launch failures are reported as ARCS_ERR_LAUNCH (from hipGetLastError,
+ *    without synchronising).
+ *  - Calls are reentrant; concurrent calls on different streams are safe.
+ */
+#ifndef ARCS_H
+#define ARCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum arcs_dtype {
+  ARCS_DTYPE_BF16 = 0,
+  ARCS_DTYPE_F32 = 1
+} arcs_dtype;
+
+typedef enum arcs_status {
+  ARCS_OK = 0,
+  ARCS_ERR_NULL_POINTER = -1,        /* a required pointer is NULL              */
+  ARCS_ERR_BAD_BATCH = -2,           /* B <= 0 or B > 2^31 - 1                  */
+  ARCS_ERR_BAD_VOCAB = -3,           /* V <= 0 or V > 2^31 - 1                  */
+  ARCS_ERR_BAD_STRIDE = -4,          /* row_stride < V                          */
+  ARCS_ERR_BAD_DTYPE = -5,           /* dtype is not an arcs_dtype              */
+  ARCS_ERR_WORKSPACE_TOO_SMALL = -6, /* workspace_bytes < arcs_sample_workspace_bytes() */
+  ARCS_ERR_LAUNCH = -7,              /* the HIP runtime rejected a launch       */
+  ARCS_ERR_MISALIGNED = -8,          /* logits not aligned to the element size  */
+  ARCS_ERR_BAD_HISTORY = -9          /* exactly one of hist_ids/hist_offsets is NULL */
+} arcs_status;
+
+/* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
+enum {
+  ARCS_ROW_OK = 0,
+  ARCS_ROW_BAD_TEMPERATURE = 1,      /* temperature NaN or < 0                  */
+  ARCS_ROW_BAD_TOP_P = 2,            /* top_p NaN or <= 0                       */
+  ARCS_ROW_BAD_MIN_P = 3,            /* min_p NaN, < 0 or > 1                   */
+  ARCS_ROW_BAD_PENALTY = 4,          /* non-finite penalty, or repetition < 0   */
+  ARCS_ROW_BAD_FLAGS = 5,            /* flags != 0                              */
+  ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY ids */
+  ARCS_ROW_VOCAB_TOO_LARGE = 7       /* penalties active and V > ARCS_MAX_PENALTY_VOCAB */
+};
+
+/* Limits of the penalty tables kept in LDS (per row). */
+#define ARCS_MAX_HISTORY 4096
+#define ARCS_MAX_PENALTY_VOCAB 262144
+
+/*
+ * Per-row sampling parameters, 32 bytes, device array of B records.
+ * Filters follow Arc PR #222 section 3(b): the host sampler's sorted list
+ * feeds zero-the-rest (top-k), the top-p walk and the min-p scan, all three
+ * inert under top_k = -1, top_p = 1, min_p = 0, in which case no cutoff is
+ * computed at all.
+ *   temperature  0 => greedy (argmax); > 0 => q ~ exp(z'/T)
+ *   top_k        <= 0 or >= V => off; 1 => greedy; else keep the k first ids
+ *                of the order (value desc, id asc)
+ *   top_p        >= 1 => off; else keep the shortest prefix of that order
+ *                whose mass reaches top_p of the FULL mass
+ *   min_p        0 => off; keep ids with q_v >= min_p * q_max
+ *   presence     0 => off; z -= presence for ids in the history
+ *   frequency    0 => off; z -= frequency * count for ids in the history
+ *   repetition   1 (or 0) => off; z = z > 0 ? z / r : z * r for history ids
+ *                (applied first, then frequency, then presence; each an
+ *                IEEE binary32 operation without fused multiply-add)
+ *   flags        must be 0
+ * The kept set is the shortest of the three prefixes (no renormalisation
+ * between filters).
+ */
+typedef struct arcs_row_params {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float min_p;
+  float presence;
+  float frequency;
+  float repetition;
+  int32_t flags;
+} arcs_row_params;
+
+/* Per-row diagnostics written by arcs_sample_debug only. */
+typedef struct arcs_row_stats {
+  int32_t id;          /* the sampled token (or -1)                         */
+  int32_t argmax;      /* argmax of the penalised logits, lowest index      */
+  int32_t kept;        /* size L of the kept set (0 for greedy rows)        */
+  int32_t cut_index;   /* last kept id in (value desc, id asc) order        */
+  float cut_value;     /* its penalised logit                               */
+  float max_logit;     /* max of the penalised logits                       */
+  int32_t status;      /* per-row status code                               */
+  uint32_t path;       /* ARCS_PATH_* bits: which stages ran                */
+  double mass_total;   /* S   = sum of weights exp((z' - max)/T), as used   */
+  double mass_kept;    /* S_K = sum over the kept set, as used              */
+  double uniform;      /* the uniform u that drove the draw                 */
+  uint64_t reserved;
+} arcs_row_stats;
+
+enum {
+  ARCS_PATH_GREEDY = 1u,      /* argmax only                                   */
+  ARCS_PATH_SORT_SKIP = 2u,   /* no filter active: no cutoff computed          */
+  ARCS_PATH_CUTOFF = 4u,      /* radix-select cutoff ran                       */
+  ARCS_PATH_MINP_FLOOR = 8u,  /* the min-p threshold bounded the kept set      */
+  ARCS_PATH_TIE_SPLIT = 16u,  /* the boundary value's ties were split by id    */
+  ARCS_PATH_PENALTY = 32u,    /* penalties applied                             */
+  ARCS_PATH_SPECIAL = 64u     /* special values (all -inf, +inf or NaN) seen   */
+};
+
+/*
+ * arcs_argmax: out_ids[b] = argmax_v logits[b, v], lowest index among equal
+ * values (bit-exact with a host argmax; Arc PR #217, "What this does", step 2).
+ * NaN counts as -inf and -0 equals +0; a row of all -inf/NaN gives 0.
+ *   logits     device, [B, row_stride] of dtype
+ *   out_ids    device, int32[B]
+ * Returns ARCS_OK or a negative arcs_status.
+ */
+int arcs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                int32_t* out_ids, void* stream);
+
+/*
+ * arcs_sample: one token per row (Arc PR #222, sections 2 and 3; penalties
+ * per the parameter record above).  Per row b:
+ *   z'   = logits widened to float32 (NaN -> -inf), penalties applied to the
+ *          ids in hist_ids[hist_offsets[b] .. hist_offsets[b+1]) (ids outside
+ *          [0, V) are skipped; duplicates count);
+ *   greedy rows (T == 0 or top_k == 1): argmax of z';
+ *   else K = the kept prefix, and the token is the first id of K, in id
+ *   order, whose running weight exceeds u * S_K, with u the SplitMix64
+ *   uniform of counter step * 2^32 + b under `seed` (Arc PR #217, "Default
+ *   OFF", names SplitMix64 for the device sampler).
+ *   params         device, arcs_row_params[B]
+ *   hist_ids       device int32 ids, or NULL (no penalties anywhere)
+ *   hist_offsets   device int64[B + 1] CSR offsets into hist_ids, or NULL
+ *   seed, step     RNG key, by value
+ *   out_ids        device int32[B]; -1 for rows with invalid parameters
+ *   out_status     device int32[B] per-row codes, or NULL
+ *   workspace      device scratch of workspace_bytes (may be NULL when
+ *                  arcs_sample_workspace_bytes() returns 0)
+ * Returns ARCS_OK or a negative arcs_status.
+ */
+int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                const arcs_row_params* params, const int32_t* hist_ids,
+                const int64_t* hist_offsets, uint64_t seed, uint64_t step, int32_t* out_ids,
+                int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace arcs_sample needs for this shape (may be 0). */
+size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype);
+
+/* Human-readable text for an arcs_status or ARCS_ROW_* code. */
+const char* arcs_status_string(int code);
+
+/*
+ * arcs_sample_debug: arcs_sample plus test hooks, kept off the hot path.
+ *   uniforms    device double[B] in [0, 1) replacing the SplitMix64 draw, or NULL
+ *   out_probs   device float[B, V]: the filtered distribution q (0 outside
+ *               the kept set; greedy rows get a one-hot), or NULL
+ *   out_stats   device arcs_row_stats[B], or NULL
+ */
+int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const arcs_row_params* params, const int32_t* hist_ids,
+                      const int64_t* hist_offsets, uint64_t seed, uint64_t step,
+                      int32_t* out_ids, int32_t* out_status, void* workspace,
+                      size_t workspace_bytes, const double* uniforms, float* out_probs,
+                      arcs_row_stats* out_stats, void* stream);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int arcs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARCS_H */

@@ -1,0 +1,70 @@
+"""The C-ABI library loads, exports every symbol include/arcs.h declares, and
+rejects bad host arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+from _util import ensure_built, header_functions
+
+
+@pytest.fixture(scope="module")
+def arcs():
+    return ensure_built()
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("arcs_argmax", "arcs_sample", "arcs_sample_workspace_bytes", "arcs_status_string",
+                 "arcs_sample_debug", "arcs_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(arcs):
+    lib = arcs.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", arcs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert name in exported, name
+
+
+def test_status_strings_and_version(arcs):
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 1, 2, 3, 4, 5, 6, 7]:
+        assert arcs.status_string(code) != "unknown status", code
+    assert arcs.status_string(12345) == "unknown status"
+    assert arcs.version() >= 100
+    assert arcs.workspace_bytes(256, 129280, arcs.DTYPE_BF16) >= 0
+
+
+def test_struct_layouts_match_the_header(arcs):
+    from workloads import PARAMS_DTYPE
+    assert arcs.ROW_PARAMS_DTYPE == PARAMS_DTYPE
+    assert arcs.ROW_PARAMS_DTYPE.itemsize == 32 and arcs.ROW_STATS_DTYPE.itemsize == 64
+
+
+def test_host_validation_rejects_before_launch(arcs):
+    lib = arcs.library()
+    buf = (ctypes.c_uint8 * 4096)()
+    base = (ctypes.addressof(buf) + 63) // 64 * 64  # aligned dummy address, never dereferenced
+    p = ctypes.c_void_p(base)
+    # argmax
+    assert lib.arcs_argmax(None, 0, 4, 10, 10, p, None) == -1
+    assert lib.arcs_argmax(p, 0, 4, 10, 10, None, None) == -1
+    assert lib.arcs_argmax(p, 7, 4, 10, 10, p, None) == -5
+    assert lib.arcs_argmax(p, 0, 0, 10, 10, p, None) == -2
+    assert lib.arcs_argmax(p, 0, -3, 10, 10, p, None) == -2
+    assert lib.arcs_argmax(p, 0, 4, 0, 10, p, None) == -3
+    assert lib.arcs_argmax(p, 0, 4, 2**31, 2**31, p, None) == -3
+    assert lib.arcs_argmax(p, 0, 4, 10, 9, p, None) == -4
+    assert lib.arcs_argmax(ctypes.c_void_p(base + 1), 0, 4, 10, 10, p, None) == -8
+    assert lib.arcs_argmax(ctypes.c_void_p(base + 2), 1, 4, 10, 10, p, None) == -8
+    # sample
+    S = lib.arcs_sample
+    assert S(p, 0, 4, 10, 10, None, None, None, 0, 0, p, None, None, 0, None) == -1
+    assert S(p, 0, 4, 10, 10, p, p, None, 0, 0, p, None, None, 0, None) == -9
+    assert S(p, 0, 4, 10, 10, p, None, p, 0, 0, p, None, None, 0, None) == -9
+    assert S(p, 0, 4, 10, 5, p, None, None, 0, 0, p, None, None, 0, None) == -4
+    assert S(p, 3, 4, 10, 10, p, None, None, 0, 0, p, None, None, 0, None) == -5
