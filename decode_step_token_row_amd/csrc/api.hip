@@ -134,7 +134,7 @@ const char* arcs_status_string(int code) {
     case ARCS_ROW_BAD_MIN_P: return "row: min_p is NaN or outside [0, 1]";
     case ARCS_ROW_BAD_PENALTY: return "row: a penalty is not finite or repetition < 0";
     case ARCS_ROW_BAD_FLAGS: return "row: flags must be 0";
-    case ARCS_ROW_HISTORY_TOO_LONG: return "row: penalties need at most ARCS_MAX_HISTORY history ids";
+    case ARCS_ROW_HISTORY_TOO_LONG: return "row: penalties need at most ARCS_MAX_HISTORY distinct history ids";
     case ARCS_ROW_VOCAB_TOO_LARGE: return "row: penalties need V <= ARCS_MAX_PENALTY_VOCAB";
     default: return "unknown status";
   }

@@ -135,4 +135,81 @@ __device__ __forceinline__ uint64_t to_fixed(float w, float scale) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
+// ---------------------------------------------------------------------------
+// DPP wave primitives (wave64, gfx9 DPP controls): register-to-register
+// cross-lane moves, no LDS traffic.  Totals are taken from lane 63 and
+// broadcast with v_readlane.
+//   0xB1 quad_perm[1,0,3,2]  0x4E quad_perm[2,3,0,1]  0x141 row_half_mirror
+//   0x140 row_mirror  0x111/0x112/0x114/0x118 row_shr 1/2/4/8
+//   0x142 row_bcast:15 (rows 1,3 via row_mask 0xA)  0x143 row_bcast:31 (rows 2,3 via 0xC)
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROWMASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const uint64_t o = __builtin_bit_cast(uint64_t, old), x = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)o, (uint32_t)x);
+  const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(o >> 32), (uint32_t)(x >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane63_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, 63), hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double dpp_wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(0.0, v);
+  v += dpp_f64<0x4E>(0.0, v);
+  v += dpp_f64<0x141>(0.0, v);
+  v += dpp_f64<0x140>(0.0, v);
+  v += dpp_f64<0x142, 0xA>(0.0, v);
+  v += dpp_f64<0x143, 0xC>(0.0, v);
+  return readlane63_f64(v);
+}
+__device__ __forceinline__ float dpp_wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(0.0f, v);
+  v += dpp_f32<0x4E>(0.0f, v);
+  v += dpp_f32<0x141>(0.0f, v);
+  v += dpp_f32<0x140>(0.0f, v);
+  v += dpp_f32<0x142, 0xA>(0.0f, v);
+  v += dpp_f32<0x143, 0xC>(0.0f, v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+__device__ __forceinline__ float dpp_wave_max_f32(float v) {
+  const float ni = -__builtin_inff();
+  float t;
+  t = dpp_f32<0xB1>(ni, v); v = v > t ? v : t;
+  t = dpp_f32<0x4E>(ni, v); v = v > t ? v : t;
+  t = dpp_f32<0x141>(ni, v); v = v > t ? v : t;
+  t = dpp_f32<0x140>(ni, v); v = v > t ? v : t;
+  t = dpp_f32<0x142, 0xA>(ni, v); v = v > t ? v : t;
+  t = dpp_f32<0x143, 0xC>(ni, v); v = v > t ? v : t;
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+// inclusive prefix sums across the wave (lane order)
+__device__ __forceinline__ double dpp_wave_incl_scan_f64(double v) {
+  v += dpp_f64<0x111>(0.0, v);
+  v += dpp_f64<0x112>(0.0, v);
+  v += dpp_f64<0x114>(0.0, v);
+  v += dpp_f64<0x118>(0.0, v);
+  v += dpp_f64<0x142, 0xA>(0.0, v);
+  v += dpp_f64<0x143, 0xC>(0.0, v);
+  return v;
+}
+__device__ __forceinline__ uint32_t dpp_wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<0x111>(0u, v);
+  v += dpp_u32<0x112>(0u, v);
+  v += dpp_u32<0x114>(0u, v);
+  v += dpp_u32<0x118>(0u, v);
+  v += dpp_u32<0x142, 0xA>(0u, v);
+  v += dpp_u32<0x143, 0xC>(0u, v);
+  return v;
+}
+
 }  // namespace arcs

@@ -61,11 +61,12 @@ enum {
   ARCS_ROW_BAD_MIN_P = 3,            /* min_p NaN, < 0 or > 1                   */
   ARCS_ROW_BAD_PENALTY = 4,          /* non-finite penalty, or repetition < 0   */
   ARCS_ROW_BAD_FLAGS = 5,            /* flags != 0                              */
-  ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY ids */
+  ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY distinct ids */
   ARCS_ROW_VOCAB_TOO_LARGE = 7       /* penalties active and V > ARCS_MAX_PENALTY_VOCAB */
 };
 
-/* Limits of the penalty tables kept in LDS (per row). */
+/* Limits of the penalty tables kept in LDS (per row): distinct history ids
+ * in [0, V) (the number of history entries itself is not limited) and V. */
 #define ARCS_MAX_HISTORY 4096
 #define ARCS_MAX_PENALTY_VOCAB 262144
 
@@ -124,7 +125,8 @@ enum {
   ARCS_PATH_MINP_FLOOR = 8u,  /* the min-p threshold bounded the kept set      */
   ARCS_PATH_TIE_SPLIT = 16u,  /* the boundary value's ties were split by id    */
   ARCS_PATH_PENALTY = 32u,    /* penalties applied                             */
-  ARCS_PATH_SPECIAL = 64u     /* special values (all -inf, +inf or NaN) seen   */
+  ARCS_PATH_SPECIAL = 64u,    /* special values (all -inf, +inf or NaN) seen   */
+  ARCS_PATH_RESIDENT = 128u   /* the row was kept in registers (single HBM read) */
 };
 
 /*

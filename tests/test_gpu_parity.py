@@ -178,8 +178,12 @@ def _mixed_params(B, rng):
     return p
 
 
+# (V, stride): bf16 rows with V % 8 == 0, V <= 131072 and 16-byte aligned rows
+# run the register-resident kernel; the others the general pipeline.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("V,stride", [(20_005, None), (20_005, 20_011), (4_099, None), (129_280, None)])
+@pytest.mark.parametrize("V,stride", [(20_005, None), (20_005, 20_011), (4_099, None), (129_280, None),
+                                      (20_000, None), (20_000, 20_008), (4_096, None), (64, None),
+                                      (8, None), (131_072, None), (100_000, 100_004)])
 def test_sample_all_modes_small_batch(arcs, dtype, V, stride):
     rng = np.random.default_rng(V + (dtype == "f32"))
     B = 24 if V > 100_000 else 48
@@ -189,6 +193,21 @@ def test_sample_all_modes_small_batch(arcs, dtype, V, stride):
     ids, status, stats, _ = _run_debug(arcs, w, stride=stride)
     refs = _oracle(w)
     _compare_rows(ids, stats, refs, f"{dtype} V={V}")
+    resident = dtype == "bf16" and V % 8 == 0 and V <= 131_072 and ((stride or V) * 2) % 16 == 0
+    flags = stats["path"] & arcs.PATH_RESIDENT
+    if resident:
+        # every mode stays on the resident path except rows whose candidate
+        # set can exceed the LDS capacity: mode 3 (top-p alone, up to 0.97,
+        # on flat rows) and mode 7 (top_k in [1000, 5000))
+        modes = np.arange(B) % 8
+        off = np.nonzero((flags == 0) & (modes != 3) & (modes != 7))[0]
+        assert len(off) == 0, [(int(b), int(modes[b]), int(stats[b]["path"])) for b in off]
+    else:
+        assert np.all(flags == 0)
+    # the production entry point agrees with the debug entry point
+    logits = to_device_logits(w.logits, w.dtype, stride=stride)
+    got = arcs.sample(logits, arcs.params_to_device(w.params), seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
 
 
 def test_sample_penalties_small(arcs):
