@@ -211,5 +211,21 @@ __device__ __forceinline__ uint32_t dpp_wave_incl_scan_u32(uint32_t v) {
   v += dpp_u32<0x143, 0xC>(0u, v);
   return v;
 }
+// minimum across the wave (same value in every lane)
+__device__ __forceinline__ uint32_t dpp_wave_min_u32(uint32_t v) {
+  const uint32_t id = 0xFFFFFFFFu;
+  uint32_t t;
+  t = dpp_u32<0xB1>(id, v); v = v < t ? v : t;
+  t = dpp_u32<0x4E>(id, v); v = v < t ? v : t;
+  t = dpp_u32<0x141>(id, v); v = v < t ? v : t;
+  t = dpp_u32<0x140>(id, v); v = v < t ? v : t;
+  t = dpp_u32<0x142, 0xA>(id, v); v = v < t ? v : t;
+  t = dpp_u32<0x143, 0xC>(id, v); v = v < t ? v : t;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// sum across the wave (same value in every lane)
+__device__ __forceinline__ uint32_t dpp_wave_sum_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)dpp_wave_incl_scan_u32(v), 63);
+}
 
 }  // namespace arcs

@@ -19,33 +19,42 @@ constexpr int kMaxDistinct = ARCS_MAX_HISTORY;  // distinct history ids per row
 constexpr int kMaxBins = 2048;
 constexpr int kTileUnroll = 4;
 constexpr int kCandCap = 4096;                 // LDS candidates of the summary path
-constexpr int kGroupCap = 4096;                // groups re-read for candidates (summary path)
 constexpr int kMaxGroups = 16384;              // summary path: V <= 8 * kMaxGroups
-constexpr int kSmallSort = 64;                 // candidate sets up to this size are rank-sorted by one wave
+constexpr int kSmallSort = 64;                 // candidate sets up to this size are handled by one wave
+constexpr int kBins = 256;                     // summary path: bound histogram bins
 // Start of dynamic LDS ("union area"), used differently by the two paths:
 //   general path: radix histograms, counts [kMaxBins] u32 + masses [kMaxBins] u64;
-//   summary path: per-thread reference exponents [kNT] f32, the list of groups
-//     to re-read [kGroupCap] i32, candidates (keys u64, weights f32)
-//     [kCandCap], and a sorted copy of small candidate sets.
+//   summary path: one f32 per group of the row, [kMaxGroups] (group j at
+//     j): its weight sum (rows without filters) or its maximum (filter
+//     rows); each thread's reference exponent [kNT] f32; candidates (keys
+//     u64, weights f32) [kCandCap]; a bound histogram (counts u32, masses
+//     f32) [kBins]; a sorted copy of small candidate sets; each thread's
+//     largest group (16 B) [kNT].
 constexpr size_t kUnionGeneric = (size_t)kMaxBins * 12;
-constexpr size_t kOffKref = 0;
-constexpr size_t kOffGlist = kOffKref + (size_t)kNT * 4;
-constexpr size_t kOffCand = kOffGlist + (size_t)kGroupCap * 4;
-constexpr size_t kOffSort = kOffCand + (size_t)kCandCap * 12;
-constexpr size_t kUnionSummary = kOffSort + (size_t)kSmallSort * 12;
-static_assert(kOffCand % 16 == 0 && kOffSort % 16 == 0, "summary LDS layout");
+constexpr size_t kOffTsum = 0;
+constexpr size_t kOffKref = kOffTsum + (size_t)kMaxGroups * 4;
+constexpr size_t kOffCand = kOffKref + (size_t)kNT * 4;
+constexpr size_t kOffHist = kOffCand + (size_t)kCandCap * 12;
+constexpr size_t kOffSort = kOffHist + (size_t)kBins * 8;
+constexpr size_t kOffBdat = kOffSort + (size_t)kSmallSort * 12;
+constexpr size_t kUnionSummary = kOffBdat + (size_t)kNT * 16;
+static_assert(kOffCand % 16 == 0 && kOffHist % 16 == 0 && kOffSort % 16 == 0 && kOffBdat % 16 == 0,
+              "summary LDS layout");
 constexpr int64_t kMaxPenVocab = ARCS_MAX_PENALTY_VOCAB;
 
 // Dynamic LDS layout.
 struct Smem {
   uint32_t* hcnt;      // [kMaxBins]               (general path)
   uint64_t* hmass;     // [kMaxBins]               (general path)
-  float* kref;         // [kNT] per-thread reference exponent, negated (summary path)
-  int32_t* glist;      // [kGroupCap] groups to re-read    (summary path)
+  float* tsum;         // [kMaxGroups] group weight sums or maxima (summary path)
+  float* kref;         // [kNT] per-thread reference exponents (summary path, no filter)
   uint64_t* ckey;      // [kCandCap] candidate sort keys   (summary path)
   float* cw;           // [kCandCap] candidate weights     (summary path)
+  uint32_t* bcnt;      // [kBins] bound histogram counts   (summary path)
+  float* bmass;        // [kBins] bound histogram masses   (summary path)
   uint64_t* skey;      // [kSmallSort] rank-sorted keys    (summary path)
   float* sw;           // [kSmallSort] rank-sorted weights (summary path)
+  u32x4* bdat;         // [kNT] each thread's largest group (summary path)
   // penalty tables: history ids as a bitmap over V, the number of set bits
   // before each bitmap word, and per distinct id (in id order) its
   // occurrence count and its penalised logit
@@ -57,12 +66,16 @@ struct Smem {
 
 __host__ __device__ inline size_t pen_prefix_bytes(uint32_t bitmap_words) { return ((size_t)bitmap_words * 2 + 15) / 16 * 16; }
 
+// The penalty tables follow the general path's union area; rows that use
+// them (active penalties) run the general path, the others may use the
+// summary path's larger union area, which overlaps the tables.
 inline size_t sample_lds_bytes(bool summary, bool pen_tables, int64_t V) {
-  size_t b = summary ? kUnionSummary : kUnionGeneric;
+  size_t b = kUnionGeneric;
   if (pen_tables) {
     const uint32_t bw = (uint32_t)((V + 31) / 32);
     b += (size_t)bw * 4 + pen_prefix_bytes(bw) + (size_t)kMaxDistinct * 8;
   }
+  if (summary && b < kUnionSummary) b = kUnionSummary;
   return b;
 }
 
@@ -292,18 +305,24 @@ __device__ __forceinline__ bool is_kept(float z, int64_t idx, const KeptCtx& kc)
 
 // Block-shared scalars of one row.  u64 slots: 0-1 pass A, 2 min-p floor,
 // 3-6 radix levels, 7 tie split, 8 draw, 9 debug stats, 10-15 resident path.
-// Carve the dynamic LDS block (union area of `union_bytes`, then the penalty tables).
+// Carve the dynamic LDS block: the union area (the general path uses its
+// first kUnionGeneric bytes, the summary path up to kUnionSummary), and the
+// penalty tables after the general part of the union area.
 __device__ __forceinline__ Smem carve_smem(unsigned char* raw, size_t union_bytes, uint32_t bitmap_words) {
   Smem sm;
   sm.hcnt = (uint32_t*)raw;
   sm.hmass = (uint64_t*)(raw + (size_t)kMaxBins * 4);
+  sm.tsum = (float*)(raw + kOffTsum);
   sm.kref = (float*)(raw + kOffKref);
-  sm.glist = (int32_t*)(raw + kOffGlist);
   sm.ckey = (uint64_t*)(raw + kOffCand);
   sm.cw = (float*)(raw + kOffCand + (size_t)kCandCap * 8);
+  sm.bcnt = (uint32_t*)(raw + kOffHist);
+  sm.bmass = (float*)(raw + kOffHist + (size_t)kBins * 4);
   sm.skey = (uint64_t*)(raw + kOffSort);
   sm.sw = (float*)(raw + kOffSort + (size_t)kSmallSort * 8);
-  unsigned char* pen_base = raw + union_bytes;
+  sm.bdat = (u32x4*)(raw + kOffBdat);
+  (void)union_bytes;
+  unsigned char* pen_base = raw + kUnionGeneric;
   sm.bitmap = (uint32_t*)pen_base;
   sm.wprefix = (uint16_t*)(pen_base + (size_t)bitmap_words * 4);
   sm.pcount = (uint32_t*)(pen_base + (size_t)bitmap_words * 4 + pen_prefix_bytes(bitmap_words));
@@ -317,9 +336,20 @@ struct Shared {
   uint64_t u64[16];
   float f32[8];
   double f64[kNW + 4];
-  double qt[16 * kNW];   // summary path, no-filter rows: weight per (group round, wave)
-  uint32_t cnt2[2];      // summary path bisection: group counts (double-buffered)
-  float mass2[2];        // summary path bisection: group-maximum masses (double-buffered)
+  // summary path, one record per wave: maximum, reference exponent (negated),
+  // weight total, group count bound, argmax candidate, flags
+  float w_max[kNW];
+  float w_negk[kNW];
+  double w_sum[kNW];
+  uint32_t w_cnt[kNW];
+  uint32_t w_arg[kNW];
+  uint32_t w_flags[kNW];
+  double rtot[kNW];      // summary path, no-filter rows: weight per group round
+  // summary path: the row's values, computed by one wave and broadcast
+  float r_m, r_negks, r_zt, r_zc;
+  double r_S, r_Pm;
+  int32_t r_mode;
+  uint32_t r_arg;
 };
 
 // Parameter validation and penalty tables.  Returns false when the row is
@@ -335,8 +365,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
                                              arcs_row_params& P, PenCtx& pc, uint32_t& path) {
   const int tid = threadIdx.x;
   const int64_t V = a.V;
-  // ---- 0. parameters ------------------------------------------------------
-  P = a.params[row];
+  // ---- 0. parameters (P holds the row's record, loaded by the caller) ------
   int status = ARCS_ROW_OK;
   if (!(P.temperature >= 0.0f)) status = ARCS_ROW_BAD_TEMPERATURE;
   else if (!(P.top_p > 0.0f)) status = ARCS_ROW_BAD_TOP_P;

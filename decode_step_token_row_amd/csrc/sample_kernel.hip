@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SampleArgs a) {
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
   const Smem sm = carve_smem(smem_raw, kUnionGeneric, a.bitmap_words);
-  arcs_row_params P;
+  arcs_row_params P = a.params[row];
   PenCtx pc;
   uint32_t path;
   if (!row_prologue<BF16, PEN>(a, row, sm, sh, P, pc, path)) return;
@@ -77,14 +77,24 @@ __device__ __forceinline__ float max2f(float a, float b) {
   return r;
 }
 
-// 8 bf16 of a group -> float32, penalties applied to history ids.
-template <bool PEN>
-__device__ __forceinline__ void unpack8(u32x4 d, int64_t g0, int n, const PenCtx& pc, float (&z)[8]) {
+// 8 bf16 of a group -> float32.
+__device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
   z[0] = bf16_lo(d.x); z[1] = bf16_hi(d.x);
   z[2] = bf16_lo(d.y); z[3] = bf16_hi(d.y);
   z[4] = bf16_lo(d.z); z[5] = bf16_hi(d.z);
   z[6] = bf16_lo(d.w); z[7] = bf16_hi(d.w);
-  if (PEN && pc.on && n > 0) apply_penalties<8>(z, g0, n, pc);
+}
+
+// Element e (0..7) of a group as float32.
+__device__ __forceinline__ float bf16_at(u32x4 d, int e) {
+  const uint32_t w = e < 2 ? d.x : e < 4 ? d.y : e < 6 ? d.z : d.w;
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// Maximum of a group.  v_max ignores quiet NaNs (the same as treating them
+// as -inf); a signalling NaN makes the result NaN, which the caller checks.
+__device__ __forceinline__ float group_max(const float (&z)[8]) {
+  return max2f(max3f(max3f(z[0], z[1], z[2]), z[3], z[4]), max3f(z[5], z[6], z[7]));
 }
 
 // Weight of z relative to the integer reference K in log2 units:
@@ -95,24 +105,37 @@ __device__ __forceinline__ float wexp(float z, float chi, float clo, float negK)
   return __builtin_amdgcn_exp2f(t);
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
+// Weight of a group: its 8 weights summed in id order.  The draw repeats
+// exactly these operations inside the group it lands in.
+__device__ __forceinline__ float group_weight(const float (&z)[8], float chi, float clo, float negK) {
+  float s = wexp(z[0], chi, clo, negK);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  for (int e = 1; e < 8; ++e) s += wexp(z[e], chi, clo, negK);
+  return s;
 }
 
-// Block-wide inclusive fp64 scan; also returns the block total.
-__device__ __forceinline__ double block_incl_scan_f64(double v, Shared& sh, double& total) {
+// A value the same in every lane, moved to scalar registers.
+__device__ __forceinline__ float uniform_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ double uniform_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Orders one wave's LDS stores before its later LDS loads from other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Block-wide inclusive fp64 scan with DPP inside waves; also returns the total.
+__device__ __forceinline__ double block_scan_f64(double v, Shared& sh, double& total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  v = wave_incl_scan_f64(v, lane);
+  v = dpp_wave_incl_scan_f64(v);
   __syncthreads();
   if (lane == kWave - 1) sh.f64[wid] = v;
   __syncthreads();
@@ -125,22 +148,6 @@ __device__ __forceinline__ double block_incl_scan_f64(double v, Shared& sh, doub
   }
   total = t;
   return v + off;
-}
-
-// Bitonic sort (ascending) of one (key, payload) per lane across a wave.
-__device__ __forceinline__ void wave_bitonic_sort(uint64_t& key, float& pay, int lane) {
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t ok = __shfl_xor(key, j, kWave);
-      const float op = __shfl_xor(pay, j, kWave);
-      const bool up = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool take = lower ? (up ? ok < key : ok > key) : (up ? ok > key : ok < key);
-      if (take) { key = ok; pay = op; }
-    }
-  }
 }
 
 // Bitonic sort (ascending) of n = 2^p (key, payload) pairs in LDS, whole block.
@@ -171,283 +178,355 @@ __device__ __forceinline__ uint64_t cand_key(float z, int64_t idx) {
 // ---------------------------------------------------------------------------
 // summary kernel
 // ---------------------------------------------------------------------------
-constexpr int kU = 16;                   // groups per thread in flight (16 x 16 B loads)
-constexpr int kQ = kMaxGroups / kNT;     // groups per thread over the row (16)
+constexpr int kQ = kMaxGroups / kNT;  // groups per thread (16)
 
-// Sequential group weight: the sum, in id order, of the 8 weights of a group.
-__device__ __forceinline__ float group_weight(const float (&z)[8], float chi, float clo, float negK) {
-  float s = wexp(z[0], chi, clo, negK);
-#pragma unroll
-  for (int e = 1; e < 8; ++e) s += wexp(z[e], chi, clo, negK);
-  return s;
-}
-
-// Orders one wave's LDS stores before its later LDS loads from other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Block-wide inclusive fp64 scan with DPP inside waves; also returns the total.
-__device__ __forceinline__ double block_scan_f64(double v, Shared& sh, double& total) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  v = dpp_wave_incl_scan_f64(v);
-  __syncthreads();
-  if (lane == kWave - 1) sh.f64[wid] = v;
-  __syncthreads();
-  double off = 0.0, t = 0.0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    const double x = sh.f64[w];
-    off += (w < wid) ? x : 0.0;
-    t += x;
-  }
-  total = t;
-  return v + off;
-}
-
-// Inverse-CDF draw in id order over per-thread group sums.  summ[q] is the
-// weight of group q * kNT + tid (in the thread's frame 2^-K_t, elements
-// below zmask excluded); dk = K_t - K* moves it to the common frame.  The
-// target u * S_K is located in three steps: the group round (kNT
-// consecutive groups), the thread inside the round (block scan), the element
-// inside the thread's group (sequential fp32 partial sums, the same
-// operations that produced summ).  Returns false when S_K is zero or not
-// finite (uniform across the block); else id and S_K.
-__device__ __forceinline__ bool round_draw(const float (&summ)[kQ], const u32x4* rv, float zmask, float chi,
-                                           float clo, float negK, int dk, double u, Shared& sh, int64_t& id,
-                                           double& S_K) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+// The row's groups owned by this thread: group j = q * kNT + tid holds ids
+// [8j, 8j + 8), so one load instruction of a wave reads 1 KB of contiguous
+// logits.  Each round q goes through a buffer resource that covers only the
+// rest of the row, so lanes past the row's end read zeros without touching
+// memory (their results are discarded), and the only per-lane address is
+// tid * 16.  All kQ loads are issued before any of them is used.
+__device__ __forceinline__ void issue_row_loads(const u32x4* rv, int ngroups, u32x4 (&d)[kQ]) {
+  const int voff = threadIdx.x * 16;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    const double r = dpp_wave_sum_f64(__builtin_ldexp((double)summ[q], dk));
-    if (lane == 0) sh.qt[q * kNW + wid] = r;
+    const int left = (ngroups - q * kNT) * 16;  // bytes of the row from round q on
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(rv + (left > 0 ? q * kNT : 0)), (short)0, left > 0 ? left : 0, 0x00020000);
+    d[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2 /* nt */));
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A lower bound of the min-p threshold m + T ln(min_p) in float arithmetic
+// (tlf = T ln(min_p) as a float), low by a relative margin that covers the
+// rounding of this computation.
+__device__ __forceinline__ float minp_bound(float m, float tlf) {
+  const float x = m + tlf;
+  return x - (1e-5f * (__builtin_fabsf(m) + __builtin_fabsf(tlf)) + 1e-30f);
+}
+
+// The min-p threshold: the smallest float z with (z - m) >= T ln(min_p) in
+// double arithmetic (tdl = T ln(min_p)).  The 64 lanes of the wave test 64
+// consecutive floats around m + tdl at once; the same value is returned in
+// every lane.  ok = false if the boundary was not found (never expected).
+__device__ __forceinline__ float minp_threshold(float m, double tdl, bool& ok) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double md = (double)m;
+  const double e = md + tdl;
+  const float z0 = e < -(double)FLT_MAX ? -FLT_MAX : (float)e;
+  // keys below that of -FLT_MAX are NaNs, for which the test is false
+  const uint32_t k0 = ord_key(z0) - 32u;
+  const float zl = key_value(k0 + (uint32_t)lane);
+  const uint64_t b = __ballot(((double)zl - md) >= tdl);
+  ok = b != 0 && (b & 1ull) == 0;
+  const float zt = key_value(k0 + (uint32_t)(ok ? __builtin_ctzll(b) : 32));
+  return zt < m ? zt : m;
+}
+
+// What a row does after the pass (decided by wave 0, broadcast through LDS).
+enum RowMode : int32_t {
+  kModeFallback = 0,  // the general pipeline
+  kModeGreedy = 1,    // argmax
+  kModeNoFilter = 2,  // id-order draw over all weights
+  kModeMinpStream = 3,  // id-order draw over the weights at or above the min-p threshold
+  kModeCand = 4,      // candidates above a known bound
+  kModeHist = 5       // candidates above a bound from a histogram of thread maxima
+};
+
+// Inverse-CDF draw in id order over sm.tsum (group j's weight at j).  With
+// `thread_frames`, group j's value is in the frame 2^-K_t of the thread t
+// that owns it (kref[t] = -K_t); otherwise in the row frame K*.
+// Wave w takes the groups w*kNT .. w*kNT + kNT - 1, its lane l the 16
+// consecutive groups from w*kNT + 16l (all owned by wave l/4): the round
+// totals locate the wave, a wave scan the lane, the lane's 16 sums the group,
+// and one re-read of that group the element (elements below zmask weigh 0).
+// The drawing lane writes the output row.  Returns false (uniformly) when
+// the total weight is zero or not finite; else S (the total).  With `sync`
+// the id is left in sh.u64[10] for the whole block; otherwise waves other
+// than the drawing one return at once.
+__device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, const u32x4* rv, const Smem& sm,
+                                          Shared& sh, bool thread_frames, float zmask, float chi, float clo,
+                                          float negks, double u, bool sync, double& S) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  // lane l: groups wid*kNT + 16l + i, owned by threads 16l + i
+  double v[16];
+  const float4* src = (const float4*)(sm.tsum + wid * kNT + lane * 16);
+  const float4* kr = (const float4*)(sm.kref + lane * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = src[i];
+    float4 k = {negks, negks, negks, negks};
+    if (thread_frames) k = kr[i];
+    v[4 * i] = __builtin_ldexp((double)f.x, (int)(negks - k.x));
+    v[4 * i + 1] = __builtin_ldexp((double)f.y, (int)(negks - k.y));
+    v[4 * i + 2] = __builtin_ldexp((double)f.z, (int)(negks - k.z));
+    v[4 * i + 3] = __builtin_ldexp((double)f.w, (int)(negks - k.w));
+  }
+  double part = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part += v[i];
+  const double incl = dpp_wave_incl_scan_f64(part);
+  if (lane == kWave - 1) sh.rtot[wid] = incl;
   __syncthreads();
-  if (wid == 0) {
-    // lane q < kQ: the total of group round q (ids [q*kNT*8, (q+1)*kNT*8))
-    double rt = 0.0;
-    if (lane < kQ)
-      for (int w = 0; w < kNW; ++w) rt += sh.qt[lane * kNW + w];
-    const double incl = dpp_wave_incl_scan_f64(rt);
-    const double tot = readlane63_f64(incl);
-    const double t = u * tot;
-    const uint64_t hit = __ballot(lane < kQ && rt > 0.0 && incl > t);
-    const uint64_t nz = __ballot(lane < kQ && rt > 0.0);
-    const int qs = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
-    const double before = __shfl(incl - rt, qs, kWave);
-    if (lane == 0) {
-      sh.i32[1] = qs;
-      sh.f64[kNW] = before;
-      sh.f64[kNW + 1] = tot;
-      sh.i32[4] = INT_MAX;
-      sh.i32[5] = -1;
+  // every thread: the total, in wave order, and the wave the target lies in
+  double cum = 0.0, before = 0.0, before_last = 0.0;
+  int qs = -1, qlast = 0;
+  S = 0.0;
+  for (int w = 0; w < kNW; ++w) S += sh.rtot[w];
+  if (!(S > 0.0) || !(S < 1e300)) return false;
+  const double t = u * S;
+  for (int w = 0; w < kNW; ++w) {
+    const double r = sh.rtot[w];
+    if (r > 0.0) {
+      if (qs < 0 && cum + r > t) { qs = w; before = cum; }
+      qlast = w;
+      before_last = cum;
+    }
+    cum += r;
+  }
+  if (qs < 0) { qs = qlast; before = before_last; }  // rounding: the last wave with weight
+  if (wid == qs) {
+    const uint64_t hit = __ballot(part > 0.0 && before + incl > t);
+    const uint64_t nz = __ballot(part > 0.0);
+    const int ls = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nz);
+    if (lane == ls) {
+      double bl = before + (incl - part), bsel = 0.0, blast = 0.0;
+      int is = -1, ilast = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const double w = v[i];
+        if (v[i] > 0.0) {
+          if (is < 0 && bl + w > t) { is = i; bsel = bl; }
+          ilast = i;
+          blast = bl;
+        }
+        bl += w;
+      }
+      if (is < 0) { is = ilast; bsel = blast; }
+      const int owner = lane * 16 + is;  // the thread that owns the group
+      const int j = wid * kNT + owner;
+      // the group's weights as the owner computed them: the running sum
+      // ends at exactly the group's value
+      const float nk = thread_frames ? sm.kref[owner] : negks;
+      const int dsh = (int)(negks - nk);
+      float z[8];
+      unpack8(rv[j], z);
+      float acc = 0.0f, prev = 0.0f;
+      int pe = -1, last_e = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = z[e] >= zmask ? wexp(z[e], chi, clo, nk) : 0.0f;
+        acc = (e == 0) ? w : acc + w;
+        const bool pos = acc > prev;
+        if (pos) last_e = e;
+        if (pe < 0 && pos && bsel + __builtin_ldexp((double)acc, dsh) > t) pe = e;
+        prev = acc;
+      }
+      if (pe < 0) pe = last_e;
+      const int32_t id = j * 8 + pe;
+      a.out_ids[row] = id;
+      if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+      sh.u64[10] = (uint64_t)id;
     }
   }
-  __syncthreads();
-  const int qs = __builtin_amdgcn_readfirstlane(sh.i32[1]);
-  const double before_round = sh.f64[kNW];
-  S_K = sh.f64[kNW + 1];
-  if (!(S_K > 0.0) || !(S_K < 1e300)) return false;
-  const double t = u * S_K;
-  float mine_f = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kQ; ++q)
-    if (q == qs) mine_f = summ[q];
-  const double mine = __builtin_ldexp((double)mine_f, dk);
-  double tot;
-  const double incl = before_round + block_scan_f64(mine, sh, tot);
-  if (mine > 0.0 && incl > t) atomicMin(&sh.i32[4], tid);
-  if (mine > 0.0) atomicMax(&sh.i32[5], tid);
-  __syncthreads();
-  int owner = sh.i32[4];
-  if (owner == INT_MAX) owner = sh.i32[5] < 0 ? 0 : sh.i32[5];  // rounding: the last thread with mass
-  if (tid == owner) {
-    const int jg = qs * kNT + tid;
-    const double bl = incl - mine;
-    float z[8];
-    unpack8<false>(rv[jg], 0, 8, PenCtx{}, z);
-    float acc = 0.0f, prev = 0.0f;
-    int pe = -1, last_e = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float w = z[e] >= zmask ? wexp(z[e], chi, clo, negK) : 0.0f;
-      acc = (e == 0) ? w : acc + w;
-      const bool pos = acc > prev;
-      if (pos) last_e = e;
-      if (pe < 0 && pos && bl + __builtin_ldexp((double)acc, dk) > t) pe = e;
-      prev = acc;
-    }
-    if (pe < 0) pe = last_e;
-    sh.u64[10] = (uint64_t)(jg * 8 + pe);
-  }
-  __syncthreads();
-  id = (int64_t)sh.u64[10];
+  if (sync) __syncthreads();
   return true;
 }
 
-// Re-reads the row (from cache) and replaces summ[q] by the weight of
-// group q * kNT + tid restricted to elements z >= zmask, summed in id order.
-__device__ __forceinline__ void masked_group_sums(const u32x4* rv, int ngroups, float zmask, float chi, float clo,
-                                                  float negK, float (&summ)[kQ]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < kQ / kU; ++it) {
-    if (it * kNT * kU >= ngroups) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) summ[it * kU + u] = 0.0f;
-      continue;
-    }
-    u32x4 d[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int j = (it * kU + u) * kNT + tid;
-      d[u] = rv[j < ngroups ? j : 0];
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = it * kU + u;
-      float z[8];
-      unpack8<false>(d[u], 0, 8, PenCtx{}, z);
-      float acc = z[0] >= zmask ? wexp(z[0], chi, clo, negK) : 0.0f;
-#pragma unroll
-      for (int e = 1; e < 8; ++e) acc += z[e] >= zmask ? wexp(z[e], chi, clo, negK) : 0.0f;
-      summ[q] = q * kNT + tid < ngroups ? acc : 0.0f;
-    }
-  }
-}
-
-// One row on the summary path.  Returns false (uniformly across the block)
-// when the row must be redone by the general pipeline.
+// One row on the summary path.  d holds the loads of the row's groups,
+// issued by the caller.  Returns false (uniformly across the block) when the
+// row must be redone by the general pipeline.
 //
-// Group j holds ids [8j, 8j+8); thread t owns the groups j = q*kNT + t
-// (q < kQ), so each 16-byte load instruction of a wave reads 1 KB of
-// contiguous logits and groups are in id order along (q, t).  The pass keeps,
-// per owned group, one float in registers: the group weight sum for
-// no-filter rows, the group maximum otherwise.  Each thread's weights use its
-// own integer reference exponent K_t (from its first group, kept in LDS for
-// the others), so sums from different threads rescale exactly by powers of
-// two into the frame K* = floor(max * log2(e) / T).
+// The pass keeps per owned group one float: its weight sum for no-filter
+// rows, its maximum otherwise, and keeps the group data in registers for the
+// candidate gathering.  Weights are computed in a per-thread frame 2^-K_t
+// (K_t an integer from the thread's first finite group, raised when a later
+// group lies far above it), moved after the pass to the frame of the wave
+// and then of the row, K* = floor(max * log2(e) / T), by exact powers of
+// two.  One barrier collects per-wave records; wave 0 turns them into the
+// row's maximum, argmax, total weight and bounds and picks what follows:
+//   no filter    -> the group sums go through LDS to the id-order draw;
+//   min-p bound small, or a top-k / top-p bound from a histogram of the
+//                   threads' largest group maxima -> the elements above the
+//                   bound are gathered into LDS from the registers, cut by
+//                   one wave (or the block for large sets) and drawn from in
+//                   id order;
+//   min-p alone over many groups -> masked group sums and the id-order draw.
 __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
-                                           uint32_t path, const Smem& sm, Shared& sh) {
+                                           uint32_t path, const Smem& sm, Shared& sh, const u32x4 (&d)[kQ]) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t V = a.V;
   const int ngroups = (int)(V / 8);
-  const char* rowp = (const char*)a.logits + row * a.stride * 2;
-  const u32x4* rv = (const u32x4*)rowp;
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
+  const bool debug = a.stats != nullptr || a.out_probs != nullptr;
   path |= ARCS_PATH_RESIDENT;
 
   const bool greedy = P.temperature == 0.0f || P.top_k == 1;
-  const bool kon = P.top_k >= 1 && (int64_t)P.top_k < V;
-  const bool pon = P.top_p < 1.0f;
-  const bool mon = P.min_p > 0.0f;
-  const bool nofilter = !greedy && !kon && !pon && !mon;
+  const bool nofilter = !greedy && !(P.top_k >= 1 && (int64_t)P.top_k < V) && !(P.top_p < 1.0f) && !(P.min_p > 0.0f);
+  const bool kon = !greedy && P.top_k >= 1 && (int64_t)P.top_k < V;
+  const bool pon = !greedy && P.top_p < 1.0f;
+  const bool mon = !greedy && P.min_p > 0.0f;
+  const bool weights = nofilter || pon;  // weights needed during the pass
 
   // temperature coefficient c = log2(e) / T = chi + clo, chi rounded down, clo > 0
-  float chi = 0.0f, clo = 0.0f;
+  float chi = 0.0f, clo = 0.0f, tlf = 0.0f;
+  double tdl = 0.0;  // T ln(min_p)
   if (!greedy) {
     const double c = 1.4426950408889634 / (double)P.temperature;
+    // temperatures so extreme that z * c leaves the float range: general path
+    if (!(c >= 1e-30 && c <= 1e30)) return false;
     chi = (float)c;
     if ((double)chi >= c) chi = key_value(ord_key(chi) - 1u);
     clo = (float)(c - (double)chi);
     if (!(clo > 0.0f)) clo = 1e-30f;
-    // temperatures so extreme that z * c leaves the float range: general path
-    if (!(c >= 1e-30 && c <= 1e30)) return false;
+    chi = uniform_f32(chi);
+    clo = uniform_f32(clo);
+    if (mon) {
+      tdl = uniform_f64((double)P.temperature * log((double)P.min_p));
+      tlf = uniform_f32((float)tdl);
+    }
   }
 
-  // ---- the HBM pass -------------------------------------------------------------
+  // ---- the pass over the row (loads already in flight) ----------------------------
   float best = -__builtin_inff();
-  int bq = -1;
-  u32x4 bdat = {0u, 0u, 0u, 0u};  // the first group holding this thread's maximum
-  float summ[kQ];                 // per owned group: weight sum (no filter) or maximum
-  double lsum = 0.0;              // top-p rows: this thread's weight total (frame K_t)
-  float negK = 0.0f;              // -K_t
-  bool kset = false, bad = false;
+  int bq = -1;                   // the thread's largest group (its data goes to sm.bdat; not for no-filter rows)
+  double lsum = 0.0;             // top-p rows: this thread's weight total (frame K_t)
+  float kfr = -__builtin_inff();  // K_t; -inf until the thread's first finite group
+  float negk = 0.0f;             // -K_t (0 before the first finite group: weights are 0 there)
+  bool bad = false, special = false;
 #pragma unroll
-  for (int it = 0; it < kQ / kU; ++it) {
-    if (it * kNT * kU >= ngroups) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) summ[it * kU + u] = nofilter ? 0.0f : -__builtin_inff();
-      continue;
+  for (int q = 0; q < kQ; ++q) {
+    const bool valid = tid < ngroups - q * kNT;
+    float z[8];
+    unpack8(d[q], z);
+    float g = group_max(z);
+    special = special || !(g == g);
+    g = valid && g == g ? g : -__builtin_inff();
+    if (!nofilter && g > best) {
+      bq = q;
+      sm.bdat[tid] = d[q];
     }
-    // all kU loads are issued before any use (the scheduling barrier keeps
-    // the compiler from waiting on one load before issuing the next); groups
-    // past the row read group 0 and their results are discarded
-    u32x4 d[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int j = (it * kU + u) * kNT + tid;
-      d[u] = __builtin_nontemporal_load(rv + (j < ngroups ? j : 0));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = it * kU + u;
-      const bool valid = q * kNT + tid < ngroups;
-      const u32x4 dv = d[u];
-      float z[8];
-      unpack8<false>(dv, 0, 8, PenCtx{}, z);
-      float g = max2f(max3f(max3f(z[0], z[1], z[2]), z[3], z[4]), max3f(z[5], z[6], z[7]));
-      g = valid ? g : -__builtin_inff();
-      const bool up = g > best;
-      best = up ? g : best;
-      bq = up ? q : bq;
-      bdat.x = up ? dv.x : bdat.x; bdat.y = up ? dv.y : bdat.y;
-      bdat.z = up ? dv.z : bdat.z; bdat.w = up ? dv.w : bdat.w;
-      if (greedy) continue;
-      if (!kset && g > -__builtin_inff()) {
-        kset = true;
-        const float x = g * chi;
-        if (x > -1048576.0f && x < 1048576.0f) negK = -__builtin_floorf(x);
-        else if (!(g == -__builtin_inff())) bad = true;
-      }
-      if (nofilter) {
-        const float s = group_weight(z, chi, clo, negK);
-        summ[q] = valid ? s : 0.0f;
-      } else {
-        summ[q] = g;
-        if (pon) {
-          const float s = group_weight(z, chi, clo, negK);
-          lsum += valid ? (double)s : 0.0;
+    best = max2f(best, g);
+    // filter rows: the group maximum; no-filter rows: the group weight (below)
+    if ((!greedy && !nofilter)) sm.tsum[q * kNT + tid] = g;
+    if (!weights) continue;
+    const float x = g * chi;
+    if (x > kfr + 64.0f) {
+      // the first finite group, or one far above the frame: (re)set it
+      if (!(x > -1048576.0f && x < 1048576.0f)) bad = true;
+      const float nk = __builtin_floorf(x);
+      if (kfr > -__builtin_inff()) {
+        const int sh_ = (int)(kfr - nk);
+        lsum = __builtin_ldexp(lsum, sh_);
+        if (nofilter) {
+          for (int p = 0; p < q; ++p) sm.tsum[p * kNT + tid] = __builtin_ldexpf(sm.tsum[p * kNT + tid], sh_);
         }
       }
+      kfr = nk;
+      negk = -nk;
     }
+    const float s = group_weight(z, chi, clo, negk);
+    if (nofilter) sm.tsum[q * kNT + tid] = valid ? s : 0.0f;
+    else lsum += valid ? (double)s : 0.0;
   }
-  sm.kref[tid] = negK;
 
-  // ---- block maximum and lowest argmax ---------------------------------------
+  // ---- wave records, one barrier ----------------------------------------------------
   {
     const float wm = dpp_wave_max_f32(best);
-    if (lane == 0) sh.bs.f32[wid] = wm;
-    if (tid == 0) sh.u64[0] = (uint64_t)INT64_MAX;
-    __syncthreads();
-    float m = sh.bs.f32[0];
+    const float kw = wm > -__builtin_inff() && weights ? __builtin_floorf(wm * chi) : 0.0f;  // K_w >= K_t
+    if (nofilter) sm.kref[tid] = negk;
+    if (weights && !nofilter) lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
+    const double ws = (pon && !greedy) ? dpp_wave_sum_f64(lsum) : 0.0;
+    uint32_t wcnt = 0;
+    if (mon && !greedy) {
+      const float wlo = minp_bound(wm, tlf);
 #pragma unroll
-    for (int w = 1; w < kNW; ++w) m = m > sh.bs.f32[w] ? m : sh.bs.f32[w];
-    if (m == m && best == m && bq >= 0) {
-      float z[8];
-      unpack8<false>(bdat, 0, 8, PenCtx{}, z);
-      int idx = INT_MAX;
+      for (int q = 0; q < kQ; ++q) {
+        const float g = sm.tsum[q * kNT + tid];
+        wcnt += (uint32_t)__builtin_popcountll(__ballot(g > -__builtin_inff() && g >= wlo));
+      }
+    }
+    uint32_t warg = 0xFFFFFFFFu;
+    if (greedy) {
+      uint32_t idx = 0xFFFFFFFFu;
+      if (best == wm && wm > -__builtin_inff()) {
+        // bq is the first of the thread's groups holding its maximum
+        float z[8];
+        unpack8(sm.bdat[tid], z);
 #pragma unroll
-      for (int e = 7; e >= 0; --e)
-        if (z[e] == m) idx = (bq * kNT + tid) * 8 + e;
-      atomicMin((unsigned long long*)&sh.u64[0], (unsigned long long)idx);
+        for (int e = 7; e >= 0; --e)
+          if (z[e] == wm) idx = (uint32_t)(bq * kNT + tid) * 8u + (uint32_t)e;
+      }
+      warg = dpp_wave_min_u32(idx);
     }
-    __syncthreads();
-    if (tid == 0) {
-      sh.f32[0] = m;
-      sh.u64[1] = (m == -__builtin_inff()) ? 0ull : sh.u64[0];
+    const uint32_t wflags = __ballot(bad || special) != 0 ? 1u : 0u;
+    if (lane == 0) {
+      sh.w_max[wid] = wm; sh.w_negk[wid] = -kw; sh.w_sum[wid] = ws;
+      sh.w_cnt[wid] = wcnt; sh.w_arg[wid] = warg; sh.w_flags[wid] = wflags;
     }
-    __syncthreads();
+    if (!greedy && !nofilter && tid < kBins) {
+      sm.bcnt[tid] = 0u;
+      sm.bmass[tid] = 0.0f;
+    }
+    if (tid == 0) { sh.i32[3] = 0; sh.i32[6] = 0; }
   }
-  const float m = sh.f32[0];
-  const int64_t argmax = (int64_t)sh.u64[1];
+  __syncthreads();
 
-  // NaN or +inf present: the general pipeline handles them exactly.
-  if (!(m == m) || m == __builtin_inff()) return false;
+  // ---- wave 0: the row's values and what follows ---------------------------------------
+  if (wid == 0) {
+    const bool in = lane < kNW;
+    const float rm = in ? sh.w_max[lane] : -__builtin_inff();
+    const float m = dpp_wave_max_f32(rm);
+    const bool flagged = __ballot(in && sh.w_flags[lane] != 0u) != 0;
+    int32_t mode = kModeFallback;
+    float negks = 0.0f, zt = -__builtin_inff(), zc = -FLT_MAX;
+    double S = 0.0, Pm = 0.0;
+    uint32_t arg = 0;
+    if (flagged) {
+      mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
+    } else if (greedy) {
+      mode = kModeGreedy;
+      const uint32_t cand = in && rm == m ? sh.w_arg[lane] : 0xFFFFFFFFu;
+      arg = m > -__builtin_inff() ? dpp_wave_min_u32(cand) : 0u;
+    } else if (m > -__builtin_inff() && m < __builtin_inff() && m * chi > -1048576.0f && m * chi < 1048576.0f) {
+      // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
+      negks = -__builtin_floorf(m * chi);
+      if (nofilter) {
+        mode = kModeNoFilter;
+      } else {
+        bool ok = true;
+        if (pon) {
+          const double x = in ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
+          S = dpp_wave_sum_f64(x);
+          ok = S > 0.0 && S < 1e300;
+          Pm = (double)P.top_p * S;
+        }
+        if (mon) {
+          bool found;
+          zt = minp_threshold(m, tdl, found);
+          ok = ok && found;
+          zc = zt > -FLT_MAX ? zt : -FLT_MAX;
+        }
+        const uint32_t ub = mon ? dpp_wave_sum_u32(in ? sh.w_cnt[lane] : 0u) : 0xFFFFFFFFu;
+        if (!ok) mode = kModeFallback;
+        else if (mon && !kon && !pon && ub > (uint32_t)(kCandCap / 8)) mode = kModeMinpStream;
+        else if ((mon && ub <= (uint32_t)(kCandCap / 8)) || ngroups <= kCandCap / 8) mode = kModeCand;
+        else mode = kModeHist;
+      }
+    }
+    if (lane == 0) {
+      sh.r_m = m; sh.r_negks = negks; sh.r_zt = zt; sh.r_zc = zc;
+      sh.r_S = S; sh.r_Pm = Pm; sh.r_mode = mode; sh.r_arg = arg;
+    }
+  }
+  __syncthreads();
+  const int32_t mode = sh.r_mode;
+  const float m = sh.r_m;
+  if (mode == kModeFallback) return false;
 
-  if (greedy) {
+  if (mode == kModeGreedy) {
+    const uint32_t argmax = sh.r_arg;
     path |= ARCS_PATH_GREEDY;
     if (tid == 0) {
       a.out_ids[row] = (int32_t)argmax;
@@ -461,17 +540,11 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       }
     }
     if (a.out_probs)
-      for (int64_t i = tid; i < V; i += kNT) a.out_probs[row * V + i] = (i == argmax) ? 1.0f : 0.0f;
+      for (int64_t i = tid; i < V; i += kNT) a.out_probs[row * V + i] = (i == (int64_t)argmax) ? 1.0f : 0.0f;
     return true;
   }
 
-  // all -inf (every id equally likely) or a maximum too large for the
-  // exponent frame: general path
-  if (m == -__builtin_inff() || !(m * chi > -1048576.0f && m * chi < 1048576.0f)) return false;
-  const float negKs = -__builtin_floorf(m * chi);
-  const int dk = (int)(negKs - negK);  // K_t - K*, exact
-
-  // ---- uniform --------------------------------------------------------------------
+  const float negks = sh.r_negks;
   double u;
   if (a.uniforms) {
     u = a.uniforms[row];
@@ -482,254 +555,228 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
 
   int64_t id = -1;
   int64_t L = V;
-  double S = 0.0, S_K = 0.0;
+  double S = sh.r_S, S_K = 0.0;
   uint32_t cut_key = 0u;
   int64_t cut_idx = -1;
 
-  if (nofilter) {
-    // ---- no filter: per-round totals, then one round's threads, then one group ------
+  if (mode == kModeNoFilter) {
     path |= ARCS_PATH_SORT_SKIP;
-    bool bad_any = __syncthreads_or(bad ? 1 : 0) != 0;
-    if (bad_any) return false;
-    if (!round_draw(summ, rv, -__builtin_inff(), chi, clo, negK, dk, u, sh, id, S)) return false;
+    if (!tsum_draw(a, row, rv, sm, sh, true, -__builtin_inff(), chi, clo, negks, u, debug, S)) return false;
+    if (!debug) return true;
     S_K = S;
-  } else {
-    // ---- filters --------------------------------------------------------------------
-    path |= ARCS_PATH_CUTOFF;
-    // total mass (top-p only; the other filters need none)
+    id = (int64_t)sh.u64[10];
+  } else if (mode == kModeMinpStream) {
+    // ---- min-p alone over many groups: masked sums (registers) and the id-order draw --
+    path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
+    const float zt = sh.r_zt;
     {
-      const double wsum = dpp_wave_sum_f64(__builtin_ldexp(lsum, dk));
-      if (lane == 0) sh.f64[wid] = wsum;
-      const int bad_any = __syncthreads_or(bad ? 1 : 0);
-      double tt = 0.0;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) tt += sh.f64[w];
-      S = tt;
-      if (bad_any || (pon && (!(S > 0.0) || !(S < 1e300)))) {
-        __syncthreads();
-        return false;
-      }
-    }
-    const double Pm = pon ? (double)P.top_p * S : 0.0;
-    // A lower bound on every value the kept set can hold.  min-p: its
-    // closed-form threshold m + T ln(min_p), taken a little low here in
-    // float arithmetic (the exact threshold is applied to the candidates).
-    float zlo = -__builtin_inff();
-    if (mon) {
-      const float lnmp = __logf(P.min_p);
-      const float x = __builtin_fmaf(P.temperature, lnmp, m);
-      zlo = x - (1e-5f * (__builtin_fabsf(m) + __builtin_fabsf(P.temperature * lnmp)) + 1e-30f);
-    }
-    // groups whose maximum reaches zlo
-    uint32_t myg = 0;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) myg += summ[q] >= zlo ? 1u : 0u;
-    if (tid == 0) {
-      sh.cnt2[0] = 0u; sh.cnt2[1] = 0u; sh.mass2[0] = 0.0f; sh.mass2[1] = 0.0f;
-      sh.i32[7] = 0;
-    }
-    __syncthreads();
-    {
-      const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)dpp_wave_incl_scan_u32(myg), 63);
-      if (lane == 0) atomicAdd(&sh.i32[7], (int)wc);
-    }
-    __syncthreads();
-    const uint32_t groups_m = (uint32_t)sh.i32[7];
-    // top-k / top-p bounds by bisection over the group maxima (bf16 values,
-    // 16-bit order keys): the largest key K with >= k groups whose maximum
-    // reaches K (each such maximum is an element), resp. whose maxima weigh
-    // at least P (a lower bound of the mass at or above K).  Only needed when
-    // the min-p bound leaves too many groups.
-    float zkp = -__builtin_inff();
-    if ((kon || pon) && (!mon || groups_m > (uint32_t)(kCandCap / 8))) {
-      float wq[kQ];
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) wq[q] = pon ? wexp(summ[q], chi, clo, negKs) : 0.0f;
-      const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
-      const float p_need = pon ? (float)(Pm * (1.0 + 1e-4)) : __builtin_inff();
-      // 16-bit order keys of bf16 values: 0x007F is -inf (a bound that always
-      // holds), 0xFF80 is +inf, keys outside [0x007F, 0xFF80] are NaNs (for
-      // which no maximum compares >=).  Invariant: the predicate holds at lo.
-      uint32_t lo_k = 0x7Fu, hi_k = 0x10000u, lo_p = 0x7Fu, hi_p = 0x10000u;
-      for (int step = 0; step < 17; ++step) {
-        const uint32_t mid_k = (lo_k + hi_k) >> 1, mid_p = (lo_p + hi_p) >> 1;
-        const float tk = key_value(mid_k << 16 | ((mid_k & 0x8000u) ? 0u : 0xFFFFu));
-        const float tp = key_value(mid_p << 16 | ((mid_p & 0x8000u) ? 0u : 0xFFFFu));
-        uint32_t c = 0;
-        float ms = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-          c += summ[q] >= tk ? 1u : 0u;
-          ms += summ[q] >= tp ? wq[q] : 0.0f;
-        }
-        const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)dpp_wave_incl_scan_u32(c), 63);
-        const float wmass = dpp_wave_sum_f32(ms);
-        const int slot = step & 1;
-        if (lane == 0) { atomicAdd(&sh.cnt2[slot], wc); atomicAdd(&sh.mass2[slot], wmass); }
-        __syncthreads();
-        const uint32_t tc = sh.cnt2[slot];
-        const float tm = sh.mass2[slot];
-        __syncthreads();
-        if (tid == 0) { sh.cnt2[slot] = 0u; sh.mass2[slot] = 0.0f; }
-        if (tc >= k_need) lo_k = mid_k; else hi_k = mid_k;
-        if (tm >= p_need) lo_p = mid_p; else hi_p = mid_p;
-        if (hi_k - lo_k <= 1 && hi_p - lo_p <= 1) break;
-      }
-      const float bk = kon ? key_value(lo_k << 16 | ((lo_k & 0x8000u) ? 0u : 0xFFFFu)) : -__builtin_inff();
-      const float bp = pon ? key_value(lo_p << 16 | ((lo_p & 0x8000u) ? 0u : 0xFFFFu)) : -__builtin_inff();
-      zkp = bk > bp ? bk : bp;
-    }
-    const float zc = zlo > zkp ? zlo : zkp;  // candidates: z >= zc
-    // min-p alone with many groups above its bound: the kept set is
-    // {z >= zt}, drawn from in id order without any ordering by value
-    const bool minp_stream = mon && !kon && !pon && groups_m > (uint32_t)(kCandCap / 8);
-    // list the groups to re-read
-    if (tid == 0) sh.i32[0] = 0;
-    __syncthreads();
-    if (!minp_stream) {
+      u32x4 dd[kQ];
+      issue_row_loads(rv, ngroups, dd);  // the row again, from cache
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
-        if (summ[q] >= zc && summ[q] > -__builtin_inff()) {
-          const int slot = atomicAdd(&sh.i32[0], 1);
-          if (slot < kGroupCap) sm.glist[slot] = q * kNT + tid;
-        }
+        float z[8];
+        unpack8(dd[q], z);
+        float s = z[0] >= zt ? wexp(z[0], chi, clo, negks) : 0.0f;
+#pragma unroll
+        for (int e = 1; e < 8; ++e) s += z[e] >= zt ? wexp(z[e], chi, clo, negks) : 0.0f;
+        sm.tsum[q * kNT + tid] = tid < ngroups - q * kNT ? s : 0.0f;
       }
-    }
-    // the exact min-p threshold: the smallest float z with
-    // ((double)z - m) / T >= ln(min_p), computed by one thread meanwhile
-    if (tid == 0) {
-      float zt = -__builtin_inff();
-      if (mon) {
-        const double lnmp = log((double)P.min_p), T = (double)P.temperature, md = (double)m;
-        auto keep = [&](float z) { return ((double)z - md) / T >= lnmp; };
-        zt = (float)(md + T * lnmp);
-        if (zt < -FLT_MAX) zt = -FLT_MAX;
-        if (keep(zt)) {
-          for (int i = 0; i < 64; ++i) {
-            const float dn = key_value(ord_key(zt) - 1u);
-            if (!keep(dn)) break;
-            zt = dn;
-          }
-        } else {
-          for (int i = 0; i < 64 && !keep(zt); ++i) zt = key_value(ord_key(zt) + 1u);
-        }
-        if (zt > m) zt = m;
-      }
-      sh.f32[1] = zt;
-      sh.i32[3] = 0;
-      sh.i32[6] = 0;
     }
     __syncthreads();
-    const int ng = sh.i32[0];
-    const float zt = sh.f32[1];
-    if (minp_stream) {
-      path |= ARCS_PATH_MINP_FLOOR;
-      masked_group_sums(rv, ngroups, zt, chi, clo, negK, summ);
-      if (!round_draw(summ, rv, zt, chi, clo, negK, dk, u, sh, id, S_K)) return false;
-      L = -1;  // counted by the debug outputs
-      cut_key = ord_key(zt);
-      cut_idx = INT64_MAX;
-    } else {
-    if (ng > kGroupCap) return false;
-    // re-read the listed groups, one per thread, and gather the candidates
-    const float zcut = zt > zc ? zt : zc;
-    for (int i = tid; i < ng; i += kNT) {
-      const int j = sm.glist[i];
-      const float nk = sm.kref[j % kNT];
-      const int dkj = (int)(negKs - nk);
-      float z[8];
-      unpack8<false>(rv[j], 0, 8, PenCtx{}, z);
+    if (!tsum_draw(a, row, rv, sm, sh, false, zt, chi, clo, negks, u, debug, S_K)) return false;
+    if (!debug) return true;
+    id = (int64_t)sh.u64[10];
+    L = -1;  // counted with the debug outputs
+    cut_key = ord_key(zt);
+    cut_idx = INT64_MAX;
+    S = 0.0;
+  } else {
+    path |= ARCS_PATH_CUTOFF;
+    const double Pm = sh.r_Pm;
+    const float zt = sh.r_zt;
+    float zc = sh.r_zc;
+    if (mode == kModeHist) {
+      // a histogram of the threads' two largest group maxima by weight, 8
+      // bins per unit of log2 weight below the row maximum: counts (top-k)
+      // and weights (top-p, a lower bound of the mass above each bin's edge)
+      float b1 = -__builtin_inff(), b2 = -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (z[e] >= zcut && z[e] > -__builtin_inff()) {
-          const int slot = atomicAdd(&sh.i32[3], 1);
-          if (slot < kCandCap) {
-            sm.ckey[slot] = cand_key(z[e], (int64_t)j * 8 + e);
-            sm.cw[slot] = __builtin_ldexpf(wexp(z[e], chi, clo, nk), dkj);
+      for (int q = 0; q < kQ; ++q) {
+        const float g = sm.tsum[q * kNT + tid];  // the group maxima
+        b2 = g > b1 ? b1 : (g > b2 ? g : b2);
+        b1 = g > b1 ? g : b1;
+      }
+      const float c8 = (chi + clo) * 8.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float v = h == 0 ? b1 : b2;
+        if (v > -__builtin_inff()) {
+          const float x = (m - v) * c8;
+          const int bin = x < (float)(kBins - 1) ? (int)x : kBins - 1;
+          atomicAdd(&sm.bcnt[bin], 1u);
+          if (pon) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
+        }
+      }
+      __syncthreads();
+      if (wid == 0) {
+        // the first bin (from the top) that meets a bound
+        const uint4 c4 = ((const uint4*)sm.bcnt)[lane];
+        const float4 m4 = ((const float4*)sm.bmass)[lane];
+        const uint32_t cl[4] = {c4.x, c4.y, c4.z, c4.w};
+        const double ml[4] = {(double)m4.x, (double)m4.y, (double)m4.z, (double)m4.w};
+        const uint32_t ctot = cl[0] + cl[1] + cl[2] + cl[3];
+        const double mtot = ml[0] + ml[1] + ml[2] + ml[3];
+        const uint32_t cex = dpp_wave_incl_scan_u32(ctot) - ctot;
+        const double mex = dpp_wave_incl_scan_f64(mtot) - mtot;
+        const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
+        const double p_need = pon ? Pm * (1.0 + 1e-4) : __builtin_inf();
+        int fb = 4;
+        uint32_t cc = cex;
+        double mc = mex;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cc += cl[i];
+          mc += ml[i];
+          if (fb == 4 && (cc >= k_need || mc >= p_need)) fb = i;
+        }
+        const uint64_t hb = __ballot(fb < 4);
+        const int lb = hb ? __builtin_ctzll(hb) : 0;
+        const int b = hb ? __builtin_amdgcn_readlane(lane * 4 + fb, lb) : kBins - 1;
+        float zn = -__builtin_inff();  // -inf: no useful bound
+        if (b < kBins - 1) {
+          const float edge = (float)(b + 1) / c8;
+          const float theta = (m - edge) - (1e-5f * (__builtin_fabsf(m) + edge) + 1e-30f);
+          zn = theta > zc ? theta : zc;
+        }
+        if (lane == 0) sh.r_zc = zn;
+      }
+      __syncthreads();
+      zc = sh.r_zc;
+      if (!(zc > -__builtin_inff())) return false;
+    }
+    const bool minp_complete = mon && !(zc > zt);
+    if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
+
+    // ---- gather the candidates z >= zc ---------------------------------------------
+    {
+      // the thread's largest group from registers: counts, one wave scan,
+      // one LDS atomic per wave
+      const bool pa = bq >= 0 && best >= zc;
+      const u32x4 bdat = pa ? sm.bdat[tid] : u32x4{0u, 0u, 0u, 0u};
+      uint32_t n = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n += pa && bf16_at(bdat, e) >= zc ? 1u : 0u;
+      if (__ballot(n != 0)) {
+        const uint32_t incl = dpp_wave_incl_scan_u32(n);
+        uint32_t base = 0;
+        if (lane == kWave - 1) base = (uint32_t)atomicAdd(&sh.i32[3], (int)incl);
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
+        uint32_t pos = base + incl - n;
+        if (pa) {
+          const int64_t i0 = (int64_t)(bq * kNT + tid) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float z = bf16_at(bdat, e);
+            if (z >= zc) {
+              if (pos < (uint32_t)kCandCap) {
+                sm.ckey[pos] = cand_key(z, i0 + e);
+                sm.cw[pos] = wexp(z, chi, clo, negks);
+              }
+              ++pos;
+            }
+          }
+        }
+      }
+      // the thread's other groups above the bound: re-read
+      uint32_t xmask = 0;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) xmask |= (q != bq && sm.tsum[q * kNT + tid] >= zc) ? (1u << q) : 0u;
+      while (xmask) {
+        const int q = __builtin_ctz(xmask);
+        xmask &= xmask - 1u;
+        const int j = q * kNT + tid;
+        const u32x4 dv = rv[j];
+        for (int e = 0; e < 8; ++e) {
+          const float z = bf16_at(dv, e);
+          if (z >= zc) {
+            const int slot = atomicAdd(&sh.i32[3], 1);
+            if (slot < kCandCap) {
+              sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
+              sm.cw[slot] = wexp(z, chi, clo, negks);
+            }
           }
         }
       }
     }
     __syncthreads();
     const int nc = sh.i32[3];
-    if (nc > kCandCap || nc == 0) {
-      __syncthreads();
-      return false;
-    }
-    // the candidate set is {z >= zcut}, a prefix of the order
-    // (value desc, id asc); the min-p set lies inside it when zcut == zt
-    const bool minp_complete = mon && !(zkp > zt);
-    if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
+    if (nc > kCandCap || nc == 0) return false;
 
     constexpr int64_t INF = INT64_MAX;
     if (nc <= kSmallSort) {
-      // ---- small candidate set: wave 0 ranks every candidate against all others ----
+      // ---- small candidate set: one wave ----------------------------------------------
       if (wid == 0) {
+        const bool in = lane < nc;
+        const uint64_t key = in ? sm.ckey[lane] : ~0ull;
+        const float w = in ? sm.cw[lane] : 0.0f;
         // rank by (value desc, id asc) = ascending key
-        if (lane < nc) {
-          const uint64_t myk = sm.ckey[lane];
-          int r = 0;
-          for (int i = 0; i < nc; ++i) r += sm.ckey[i] < myk ? 1 : 0;
-          sm.skey[r] = myk;
-          sm.sw[r] = sm.cw[lane];
+        const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+        uint32_t r = 0;
+        for (int j = 0; j < nc; ++j) {
+          const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)khi, j);
+          const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+          r += (oh < khi || (oh == khi && ol < klo)) ? 1u : 0u;
         }
+        if (in) { sm.skey[r] = key; sm.sw[r] = w; }
         wave_lds_sync();
-        // in-order fp64 prefix of the sorted weights (lane i sums entries 0..i)
-        double cum = 0.0;
-        uint64_t key = ~0ull;
-        float w = 0.0f;
-        if (lane < nc) {
-          key = sm.skey[lane];
-          w = sm.sw[lane];
-          for (int i = 0; i <= lane; ++i) cum += (double)sm.sw[i];
-        }
+        const uint64_t skey = in ? sm.skey[lane] : ~0ull;
+        const float sw = in ? sm.sw[lane] : 0.0f;
+        const double cum = dpp_wave_incl_scan_f64((double)sw);
         const int64_t Lk = (kon && (int64_t)P.top_k <= nc) ? (int64_t)P.top_k : INF;
         int64_t Lp = INF;
         if (pon) {
-          const uint64_t hit = __ballot(lane < nc && cum >= Pm);
+          const uint64_t hit = __ballot(in && cum >= Pm);
           if (hit) Lp = __builtin_ctzll(hit) + 1;
         }
-        const int64_t Lm = minp_complete ? (int64_t)nc : INF;
+        int64_t Lm = INF;
+        if (minp_complete) Lm = __builtin_popcountll(__ballot(in && key_value(~(uint32_t)(skey >> 32)) >= zt));
         int64_t Lw = Lk < Lp ? Lk : Lp;
         Lw = Lw < Lm ? Lw : Lm;
-        if (Lw == INF) {
+        if (Lw == INF || Lw < 1) {
           if (lane == 0) sh.i32[6] = -1;
         } else {
-          const double sk = __shfl(cum, (int)Lw - 1, kWave);
-          const uint64_t ck = __shfl(key, (int)Lw - 1, kWave);
+          const int lc = (int)Lw - 1;
+          const uint64_t cb = (uint64_t)__builtin_bit_cast(uint64_t, cum);
+          const double sk = __builtin_bit_cast(
+              double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(cb >> 32), lc) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cb, lc));
+          const uint64_t ck = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(skey >> 32), lc) << 32) |
+                              (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)skey, lc);
           const double t = u * sk;
-          // the kept entries in id order: rank by id among the first Lw
-          const uint32_t myid = (uint32_t)(key & 0xFFFFFFFFull);
-          double c2 = 0.0;
-          bool mine = false;
-          if (lane < Lw) {
-            for (int i = 0; i < Lw; ++i) {
-              const uint32_t oid = (uint32_t)(sm.skey[i] & 0xFFFFFFFFull);
-              if (oid <= myid) c2 += (double)sm.sw[i];
-            }
-            mine = w > 0.0f && c2 > t && c2 - (double)w <= t;
-          }
-          const uint64_t hit = __ballot(mine);
-          const uint64_t nz = __ballot(lane < Lw && w > 0.0f);
-          // rounding can leave t past the last boundary: take the largest kept id with weight
-          int ls;
-          if (hit) {
-            ls = __builtin_ctzll(hit);
-          } else {
-            uint32_t bestid = 0u;
-            int bl = 0;
-            for (int i = 0; i < (int)Lw; ++i) {
-              const uint32_t oid = (uint32_t)(sm.skey[i] & 0xFFFFFFFFull);
-              if (sm.sw[i] > 0.0f && oid >= bestid) { bestid = oid; bl = i; }
-            }
-            ls = nz ? bl : 0;
-          }
-          const uint64_t pid = __shfl(key, ls, kWave);
+          // the kept entries in id order: rank by id, then an in-order scan
+          const bool kept = lane < Lw;
+          const uint32_t myid = (uint32_t)skey;
+          uint32_t r2 = 0;
+          for (int j = 0; j < (int)Lw; ++j)
+            r2 += (uint32_t)__builtin_amdgcn_readlane((int)myid, j) < myid ? 1u : 0u;
+          wave_lds_sync();
+          if (kept) { sm.skey[r2] = myid; sm.sw[r2] = sw; }
+          wave_lds_sync();
+          const uint32_t id2 = kept ? (uint32_t)sm.skey[lane] : 0u;
+          const float w2 = kept ? sm.sw[lane] : 0.0f;
+          const double c2 = dpp_wave_incl_scan_f64((double)w2);
+          const uint64_t hit = __ballot(kept && w2 > 0.0f && c2 > t);
+          const uint64_t nz = __ballot(kept && w2 > 0.0f);
+          // rounding can leave t past the last boundary: the last kept id with weight
+          const int ls = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
+          const uint32_t pid = (uint32_t)__builtin_amdgcn_readlane((int)id2, ls);
           if (lane == 0) {
-            sh.u64[10] = pid & 0xFFFFFFFFull;
+            sh.u64[10] = pid;
             sh.u64[11] = (uint64_t)Lw;
             sh.f64[kNW + 1] = sk;
             sh.u64[12] = ck;
+            a.out_ids[row] = (int32_t)pid;
+            if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
           }
         }
       }
@@ -739,18 +786,24 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       int n2 = 128;
       while (n2 < nc) n2 <<= 1;
       for (int i = nc + tid; i < n2; i += kNT) { sm.ckey[i] = ~0ull; sm.cw[i] = 0.0f; }
-      if (tid == 0) { sh.u64[13] = (uint64_t)INF; sh.u64[14] = (uint64_t)INF; }
+      if (tid == 0) { sh.u64[13] = (uint64_t)INF; sh.u64[14] = (uint64_t)INF; sh.u64[15] = 0ull; }
       __syncthreads();
       block_bitonic_sort(sm.ckey, sm.cw, n2);
       // prefix mass over the sorted order (ENT consecutive entries per thread)
       constexpr int ENT = kCandCap / kNT;
       double loc[ENT];
       double lsum_c = 0.0;
+      uint32_t nm = 0;
 #pragma unroll
       for (int j = 0; j < ENT; ++j) {
         const int i = tid * ENT + j;
         lsum_c += (i < nc) ? (double)sm.cw[i] : 0.0;
         loc[j] = lsum_c;
+        if (minp_complete && i < nc && key_value(~(uint32_t)(sm.ckey[i] >> 32)) >= zt) ++nm;
+      }
+      if (minp_complete) {
+        const uint32_t wn = dpp_wave_sum_u32(nm);
+        if (lane == 0 && wn) atomicAdd((unsigned long long*)&sh.u64[15], (unsigned long long)wn);
       }
       double tot;
       const double incl = block_scan_f64(lsum_c, sh, tot);
@@ -768,10 +821,10 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       __syncthreads();
       const int64_t Lk = (kon && (int64_t)P.top_k <= nc) ? (int64_t)P.top_k : INF;
       const int64_t Lp = (int64_t)sh.u64[13];
-      const int64_t Lm = minp_complete ? (int64_t)nc : INF;
+      const int64_t Lm = minp_complete ? (int64_t)sh.u64[15] : INF;
       int64_t Lw = Lk < Lp ? Lk : Lp;
       Lw = Lw < Lm ? Lw : Lm;
-      if (Lw == INF) {
+      if (Lw == INF || Lw < 1) {
         if (tid == 0) sh.i32[6] = -1;
         __syncthreads();
       } else {
@@ -817,79 +870,76 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
             pos = Lw - 1;
             while (pos > 0 && !(sm.cw[pos] > 0.0f)) --pos;
           }
-          sh.u64[10] = sm.ckey[pos] & 0xFFFFFFFFull;
+          const uint32_t pid = (uint32_t)(sm.ckey[pos] & 0xFFFFFFFFull);
+          sh.u64[10] = pid;
           sh.u64[11] = (uint64_t)Lw;
+          a.out_ids[row] = (int32_t)pid;
+          if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
         }
         __syncthreads();
       }
     }
-    if (sh.i32[6] < 0) {
-      __syncthreads();
-      return false;
-    }
+    if (sh.i32[6] < 0) return false;
+    if (!debug) return true;
     id = (int64_t)sh.u64[10];
     L = (int64_t)sh.u64[11];
     S_K = sh.f64[kNW + 1];
     const uint64_t ck = sh.u64[12];
     cut_key = ~(uint32_t)(ck >> 32);
     cut_idx = (int64_t)(ck & 0xFFFFFFFFull);
-    }
-  }
-
-  if (tid == 0) {
-    a.out_ids[row] = (int32_t)id;
-    if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
   }
 
   // ---- debug outputs (the row is read again) ---------------------------------------
-  if (a.stats || a.out_probs) {
+  {
     const bool all_kept = (path & ARCS_PATH_SORT_SKIP) != 0;
     uint32_t kmin = 0xFFFFFFFFu;
     int64_t kmin_idx = -1;
+    uint64_t amax = 0;  // (key of the maximum, complement of the lowest index holding it)
     uint32_t nkept = 0;
     double wtot = 0.0;
     for (int j = tid; j < ngroups; j += kNT) {
-      const float nk = sm.kref[j % kNT];
-      const int dkj = (int)(negKs - nk);
       float z[8];
-      unpack8<false>(rv[j], 0, 8, PenCtx{}, z);
+      unpack8(rv[j], z);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int64_t idx = (int64_t)j * 8 + e;
-        const uint32_t k = ord_key(z[e]);
+        const uint32_t k = ord_key(z[e] == z[e] ? z[e] : -__builtin_inff());
         const bool kept = all_kept || k > cut_key || (k == cut_key && idx <= cut_idx);
-        if (a.out_probs) {
-          const double w = (double)__builtin_ldexpf(wexp(z[e], chi, clo, nk), dkj);
-          a.out_probs[row * V + idx] = kept ? (float)(w / S_K) : 0.0f;
-        }
+        const double w = (double)wexp(z[e], chi, clo, negks);
+        if (a.out_probs) a.out_probs[row * V + idx] = kept ? (float)(w / S_K) : 0.0f;
         if (kept && (k < kmin || (k == kmin && idx > kmin_idx))) { kmin = k; kmin_idx = idx; }
+        const uint64_t ak = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+        amax = ak > amax ? ak : amax;
         nkept += kept ? 1u : 0u;
-        wtot += (double)__builtin_ldexpf(wexp(z[e], chi, clo, nk), dkj);
+        wtot += w;
       }
     }
     if (a.stats) {
-      if (tid == 0) sh.u64[9] = ~0ull;
+      if (tid == 0) { sh.u64[9] = ~0ull; sh.u64[8] = 0ull; }
       __syncthreads();
       const uint64_t packed =
           ((uint64_t)kmin << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(kmin_idx < 0 ? 0 : kmin_idx));
       if (kmin_idx >= 0) atomicMin((unsigned long long*)&sh.u64[9], (unsigned long long)packed);
-      const uint32_t wk = (uint32_t)__builtin_amdgcn_readlane((int)dpp_wave_incl_scan_u32(nkept), 63);
+      atomicMax((unsigned long long*)&sh.u64[8], (unsigned long long)amax);
+      const uint32_t wk = dpp_wave_sum_u32(nkept);
       const double wt = dpp_wave_sum_f64(wtot);
       if (lane == 0) {
-        sh.qt[wid] = wt;
-        sh.qt[kNW + wid] = (double)wk;
+        sh.rtot[wid] = wt;
+        sh.w_cnt[wid] = wk;
       }
       __syncthreads();
       if (L < 0 || S == 0.0) {
-        double a0 = 0.0, a1 = 0.0;
-        for (int w = 0; w < kNW; ++w) { a0 += sh.qt[w]; a1 += sh.qt[kNW + w]; }
+        double a0 = 0.0;
+        uint64_t a1 = 0;
+        for (int w = 0; w < kNW; ++w) { a0 += sh.rtot[w]; a1 += sh.w_cnt[w]; }
         if (L < 0) L = (int64_t)a1;
         if (S == 0.0) S = a0;
       }
       if (tid == 0) {
         const uint64_t pk = sh.u64[9];
+        const uint32_t argmax = 0xFFFFFFFFu - (uint32_t)(sh.u64[8] & 0xFFFFFFFFu);
         // masses reported relative to the row max, as sums of exp((z - m) / T)
-        const double to_m = exp2((double)(-negKs) - (double)m * ((double)chi + (double)clo));
+        const double to_m = exp2((double)(-negks) - (double)m * ((double)chi + (double)clo));
         arcs_row_stats st = {};
         st.id = (int32_t)id; st.argmax = (int32_t)argmax; st.kept = (int32_t)L;
         st.cut_index = (int32_t)(0xFFFFFFFFu - (uint32_t)(pk & 0xFFFFFFFFu));
@@ -911,13 +961,21 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
   const Smem sm = carve_smem(smem_raw, kUnionSummary, a.bitmap_words);
-  arcs_row_params P;
+  const int ngroups = (int)(a.V / 8);
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
+  u32x4 d[kQ];
+  // Without penalty tables the row's loads go out right after the parameter
+  // record's, so that validating it overlaps their latency.
+  arcs_row_params P = a.params[row];
+  __builtin_amdgcn_sched_barrier(0);
+  if (!PEN) issue_row_loads(rv, ngroups, d);
   PenCtx pc;
   uint32_t path;
   if (!row_prologue<true, PEN>(a, row, sm, sh, P, pc, path)) return;
   // Rows with active penalties take the general pipeline; the summary path
   // handles the rest.
-  if (pc.on || !stream_row(a, row, P, path, sm, sh)) {
+  if (PEN && !pc.on) issue_row_loads(rv, ngroups, d);
+  if (pc.on || !stream_row(a, row, P, path, sm, sh, d)) {
     __syncthreads();
     generic_row<true, true>(a, row, P, pc, path, sm, sh);
   }
