@@ -64,6 +64,15 @@ def algorithmic_bytes(w) -> int:
     return int(b)
 
 
+def kernel_name(w) -> str:
+    """The kernel one step launches for this workload (as the launcher picks it)."""
+    if w.greedy_only:
+        return "argmax_kernel"
+    if w.dtype == "bf16" and w.V % 8 == 0 and w.V <= 131072:
+        return "sample_summary_kernel"
+    return "sample_kernel"
+
+
 def read_traffic(workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None when absent or taken on different kernel sources."""
@@ -252,7 +261,7 @@ def main():
             "algorithmic_bytes_per_launch": alg,
             "avg_launch_us": ms_per_step * 1e3,
             "isolated_launch_us": avg_launch_ms * 1e3,
-            "kernel": "argmax_kernel" if w.greedy_only else "sample_kernel",
+            "kernel": kernel_name(w),
         },
         "cpu_baseline": cpu,
     }
