@@ -1,10 +1,12 @@
 """Benchmark of the batched on-device sampler on one MI355X.
 
-One step = one call of the whole hot path (arcs_sample: penalties,
-max/normaliser, top-k/top-p/min-p cutoff, SplitMix64 draw, output) over one
-batch of synthetic logits that are already resident in HBM.  The default
-workload is the B=256, V=129,280 bf16 batch with T=0.7, top_k=50,
-top_p=0.9, min_p=0.05 on every row.  Launches rotate over enough copies of
+One step = one call of the hot path over one batch of synthetic logits that
+are already resident in HBM: arcs_argmax for greedy-only workloads, else
+arcs_sample (penalties, max/normaliser, top-k/top-p/min-p cutoff, SplitMix64
+draw, output).  The default workload is the B=256, V=129,280 bf16 batch of
+Zipf-shaped logits with greedy argmax on every row (66.2 MB read per step);
+--workload picks another (e.g. the same logits with T=0.7, top_k=50,
+top_p=0.9, min_p=0.05 on every row).  Launches rotate over enough copies of
 the logits (>= 512 MiB, twice the 256 MiB Infinity Cache) that every step
 reads its logits from HBM.
 
@@ -35,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sampled rows/s and achieved HBM GB/s (% of peak) at B=256, V=129,280"
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_WORKLOAD = "zipf_b256_bf16_t0.7_k50_p0.9_minp0.05"
+DEFAULT_WORKLOAD = "zipf_b256_bf16_greedy"
 ROTATE_BYTES = 512 * 2**20
 KERNEL_SOURCES = ["device_common.hpp", "sample_common.hpp", "sample_kernel.hip", "argmax_kernel.hip", "launch.hpp"]
 

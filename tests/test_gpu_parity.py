@@ -87,8 +87,10 @@ def _oracle(w, uniforms=None, want_probs=False):
 # --------------------------------------------------------------------------
 # argmax
 # --------------------------------------------------------------------------
+# bf16 rows with V % 8 == 0, V <= 131072 and 16-byte aligned rows take the
+# single-pass register kernel, the others the general loop.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("V", [1, 7, 8, 9, 1000, 20_005, 129_280])
+@pytest.mark.parametrize("V", [1, 7, 8, 9, 1000, 20_005, 129_280, 131_072, 131_080])
 def test_argmax_random_rows_with_ties(arcs, dtype, V):
     rng = np.random.default_rng(V)
     B = 37
@@ -103,8 +105,8 @@ def test_argmax_random_rows_with_ties(arcs, dtype, V):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_argmax_special_values(arcs, dtype):
-    V = 4099
+@pytest.mark.parametrize("V", [4099, 4096])
+def test_argmax_special_values(arcs, dtype, V):
     nan, inf = np.float32(np.nan), np.float32(np.inf)
     rows = []
     r = np.full(V, -3.0, np.float32); r[V - 1] = 2.0; rows.append(r)          # max at last index
