@@ -28,17 +28,15 @@ constexpr int kBins = 256;                     // summary path: bound histogram 
 //     j): its weight sum (rows without filters) or its maximum (filter
 //     rows); each thread's reference exponent [kNT] f32; candidates (keys
 //     u64, weights f32) [kCandCap]; a bound histogram (counts u32, masses
-//     f32) [kBins]; a sorted copy of small candidate sets; each thread's
-//     largest group (16 B) [kNT].
+//     f32) [kBins]; a sorted copy of small candidate sets.
 constexpr size_t kUnionGeneric = (size_t)kMaxBins * 12;
 constexpr size_t kOffTsum = 0;
 constexpr size_t kOffKref = kOffTsum + (size_t)kMaxGroups * 4;
 constexpr size_t kOffCand = kOffKref + (size_t)kNT * 4;
 constexpr size_t kOffHist = kOffCand + (size_t)kCandCap * 12;
 constexpr size_t kOffSort = kOffHist + (size_t)kBins * 8;
-constexpr size_t kOffBdat = kOffSort + (size_t)kSmallSort * 12;
-constexpr size_t kUnionSummary = kOffBdat + (size_t)kNT * 16;
-static_assert(kOffCand % 16 == 0 && kOffHist % 16 == 0 && kOffSort % 16 == 0 && kOffBdat % 16 == 0,
+constexpr size_t kUnionSummary = kOffSort + (size_t)kSmallSort * 12;
+static_assert(kOffCand % 16 == 0 && kOffHist % 16 == 0 && kOffSort % 16 == 0,
               "summary LDS layout");
 constexpr int64_t kMaxPenVocab = ARCS_MAX_PENALTY_VOCAB;
 
@@ -54,7 +52,6 @@ struct Smem {
   float* bmass;        // [kBins] bound histogram masses   (summary path)
   uint64_t* skey;      // [kSmallSort] rank-sorted keys    (summary path)
   float* sw;           // [kSmallSort] rank-sorted weights (summary path)
-  u32x4* bdat;         // [kNT] each thread's largest group (summary path)
   // penalty tables: history ids as a bitmap over V, the number of set bits
   // before each bitmap word, and per distinct id (in id order) its
   // occurrence count and its penalised logit
@@ -320,7 +317,6 @@ __device__ __forceinline__ Smem carve_smem(unsigned char* raw, size_t union_byte
   sm.bmass = (float*)(raw + kOffHist + (size_t)kBins * 4);
   sm.skey = (uint64_t*)(raw + kOffSort);
   sm.sw = (float*)(raw + kOffSort + (size_t)kSmallSort * 8);
-  sm.bdat = (u32x4*)(raw + kOffBdat);
   (void)union_bytes;
   unsigned char* pen_base = raw + kUnionGeneric;
   sm.bitmap = (uint32_t*)pen_base;
@@ -337,7 +333,7 @@ struct Shared {
   float f32[8];
   double f64[kNW + 4];
   // summary path, one record per wave: maximum, reference exponent (negated),
-  // weight total, group count bound, argmax candidate, flags
+  // weight total, kept count (debug outputs), argmax candidate, flags
   float w_max[kNW];
   float w_negk[kNW];
   double w_sum[kNW];

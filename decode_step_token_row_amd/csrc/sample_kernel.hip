@@ -334,6 +334,261 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
   return true;
 }
 
+
+// Gathers this thread's elements z >= bound (bound finite) into the candidate
+// list sm.ckey / sm.cw with their weights in the row frame (-negks): the two
+// largest groups from registers (counted first, one wave scan, one LDS atomic
+// per wave on the block count sh.i32[3]), any other group at or above the
+// bound re-read from memory (rare).  A count above kCandCap means the list is
+// incomplete.  Threads whose largest group lies below the bound hold nothing,
+// and a wave where that holds for every lane does nothing.
+__device__ __forceinline__ void gather_candidates(const u32x4* rv, const Smem& sm, Shared& sh, float bound, float best,
+                                                  int bq, float best2, int sq, u32x4 da, u32x4 db, float chi,
+                                                  float clo, float negks) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const bool pa = bq >= 0 && best >= bound;
+  const bool pb = sq >= 0 && best2 >= bound;
+  if (!__ballot(pa)) return;
+  uint32_t n = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    n += pa && bf16_at(da, e) >= bound ? 1u : 0u;
+    n += pb && bf16_at(db, e) >= bound ? 1u : 0u;
+  }
+  if (__ballot(n != 0)) {
+    const uint32_t incl = dpp_wave_incl_scan_u32(n);
+    uint32_t base = 0;
+    if (lane == kWave - 1) base = (uint32_t)atomicAdd(&sh.i32[3], (int)incl);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
+    uint32_t pos = base + incl - n;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 0 ? pa : pb) {
+        const u32x4 dv = h == 0 ? da : db;
+        const int64_t i0 = (int64_t)((h == 0 ? bq : sq) * kNT + tid) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float z = bf16_at(dv, e);
+          if (z >= bound) {
+            if (pos < (uint32_t)kCandCap) {
+              sm.ckey[pos] = cand_key(z, i0 + e);
+              sm.cw[pos] = wexp(z, chi, clo, negks);
+            }
+            ++pos;
+          }
+        }
+      }
+    }
+  }
+  // other groups at or above the bound (only where the second largest is): re-read
+  if (!__ballot(pb)) return;
+  uint32_t xmask = 0;
+  if (pb) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) xmask |= (q != bq && q != sq && sm.tsum[q * kNT + tid] >= bound) ? (1u << q) : 0u;
+  }
+  while (xmask) {
+    const int q = __builtin_ctz(xmask);
+    xmask &= xmask - 1u;
+    const int j = q * kNT + tid;
+    const u32x4 dv = rv[j];
+    for (int e = 0; e < 8; ++e) {
+      const float z = bf16_at(dv, e);
+      if (z >= bound) {
+        const uint32_t slot = (uint32_t)atomicAdd(&sh.i32[3], 1);
+        if (slot < (uint32_t)kCandCap) {
+          sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
+          sm.cw[slot] = wexp(z, chi, clo, negks);
+        }
+      }
+    }
+  }
+}
+
+// Cut and draw over nc <= kSmallSort candidates, by one wave (lane i holds
+// candidate i: its key and its weight in the row frame): rank by key with lane reads, an fp64 scan of
+// the weights in (value desc, id asc) order for L = min(L_k, L_p, L_m), then a
+// rank by id among the kept prefix and a second scan for the id-order draw.
+// Writes the output row and sh.u64[10..12] / sh.f64[kNW+1] (id, L, cut key,
+// S_K); returns false if no prefix length is known from the candidates.
+__device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh, int nc,
+                                               uint64_t key, float w, bool kon, int top_k, bool pon, double Pm,
+                                               bool minp_complete, float zt, double u) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int64_t INF = INT64_MAX;
+  const bool in = lane < nc;
+  key = in ? key : ~0ull;
+  w = in ? w : 0.0f;
+  // rank by (value desc, id asc) = ascending key
+  const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+  uint32_t r = 0;
+  for (int j = 0; j < nc; ++j) {
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)khi, j);
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+    r += (oh < khi || (oh == khi && ol < klo)) ? 1u : 0u;
+  }
+  wave_lds_sync();
+  if (in) { sm.skey[r] = key; sm.sw[r] = w; }
+  wave_lds_sync();
+  const uint64_t skey = in ? sm.skey[lane] : ~0ull;
+  const float sw = in ? sm.sw[lane] : 0.0f;
+  const double cum = dpp_wave_incl_scan_f64((double)sw);
+  const int64_t Lk = (kon && (int64_t)top_k <= nc) ? (int64_t)top_k : INF;
+  int64_t Lp = INF;
+  if (pon) {
+    const uint64_t hit = __ballot(in && cum >= Pm);
+    if (hit) Lp = __builtin_ctzll(hit) + 1;
+  }
+  int64_t Lm = INF;
+  if (minp_complete) Lm = __builtin_popcountll(__ballot(in && key_value(~(uint32_t)(skey >> 32)) >= zt));
+  int64_t Lw = Lk < Lp ? Lk : Lp;
+  Lw = Lw < Lm ? Lw : Lm;
+  if (Lw == INF || Lw < 1) return false;
+  const int lc = (int)Lw - 1;
+  const uint64_t cb = __builtin_bit_cast(uint64_t, cum);
+  const double sk = __builtin_bit_cast(
+      double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(cb >> 32), lc) << 32) |
+                  (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cb, lc));
+  const uint64_t ck = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(skey >> 32), lc) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)skey, lc);
+  const double t = u * sk;
+  // the kept entries in id order: rank by id, then an in-order scan
+  const bool kept = lane < Lw;
+  const uint32_t myid = (uint32_t)skey;
+  uint32_t r2 = 0;
+  for (int j = 0; j < (int)Lw; ++j) r2 += (uint32_t)__builtin_amdgcn_readlane((int)myid, j) < myid ? 1u : 0u;
+  wave_lds_sync();
+  if (kept) { sm.skey[r2] = myid; sm.sw[r2] = sw; }
+  wave_lds_sync();
+  const uint32_t id2 = kept ? (uint32_t)sm.skey[lane] : 0u;
+  const float w2 = kept ? sm.sw[lane] : 0.0f;
+  const double c2 = dpp_wave_incl_scan_f64((double)w2);
+  const uint64_t hit = __ballot(kept && w2 > 0.0f && c2 > t);
+  const uint64_t nz = __ballot(kept && w2 > 0.0f);
+  // rounding can leave t past the last boundary: the last kept id with weight
+  const int ls = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
+  const uint32_t pid = (uint32_t)__builtin_amdgcn_readlane((int)id2, ls);
+  if (lane == 0) {
+    sh.u64[10] = pid;
+    sh.u64[11] = (uint64_t)Lw;
+    sh.f64[kNW + 1] = sk;
+    sh.u64[12] = ck;
+    a.out_ids[row] = (int32_t)pid;
+    if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+  }
+  return true;
+}
+
+// Cut and draw over nc > kSmallSort candidates in ckey / cw (room for the next
+// power of two, at least 128; keys in
+// (value desc, id asc) order, weights in the row frame): a block bitonic sort,
+// block scans for the top-p crossing and the min-p count, a second sort of the
+// kept prefix by id, and the id-order draw.  All threads take part.  On
+// success the output row is written and sh.u64[10..12] / sh.f64[kNW+1] hold
+// id, L, the cut key and S_K; on failure (no prefix length known from the
+// candidates) sh.i32[6] = -1.
+__device__ __forceinline__ void large_cut_draw(const SampleArgs& a, int64_t row, uint64_t* ckey, float* cw, Shared& sh,
+                                               int nc, bool kon, int top_k, bool pon, double Pm, bool minp_complete,
+                                               float zt, double u) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  constexpr int64_t INF = INT64_MAX;
+  int n2 = 128;
+  while (n2 < nc) n2 <<= 1;
+  for (int i = nc + tid; i < n2; i += kNT) { ckey[i] = ~0ull; cw[i] = 0.0f; }
+  if (tid == 0) { sh.u64[13] = (uint64_t)INF; sh.u64[14] = (uint64_t)INF; sh.u64[15] = 0ull; }
+  __syncthreads();
+  block_bitonic_sort(ckey, cw, n2);
+  // prefix mass over the sorted order (ENT consecutive entries per thread)
+  constexpr int ENT = kCandCap / kNT;
+  double loc[ENT];
+  double lsum_c = 0.0;
+  uint32_t nm = 0;
+#pragma unroll
+  for (int j = 0; j < ENT; ++j) {
+    const int i = tid * ENT + j;
+    lsum_c += (i < nc) ? (double)cw[i] : 0.0;
+    loc[j] = lsum_c;
+    if (minp_complete && i < nc && key_value(~(uint32_t)(ckey[i] >> 32)) >= zt) ++nm;
+  }
+  if (minp_complete) {
+    const uint32_t wn = dpp_wave_sum_u32(nm);
+    if (lane == 0 && wn) atomicAdd((unsigned long long*)&sh.u64[15], (unsigned long long)wn);
+  }
+  double tot;
+  const double incl = block_scan_f64(lsum_c, sh, tot);
+  const double excl = incl - lsum_c;
+  if (pon) {
+#pragma unroll
+    for (int j = 0; j < ENT; ++j) {
+      const int i = tid * ENT + j;
+      if (i < nc && excl + loc[j] >= Pm) {
+        atomicMin((unsigned long long*)&sh.u64[13], (unsigned long long)(i + 1));
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t Lk = (kon && (int64_t)top_k <= nc) ? (int64_t)top_k : INF;
+  const int64_t Lp = (int64_t)sh.u64[13];
+  const int64_t Lm = minp_complete ? (int64_t)sh.u64[15] : INF;
+  int64_t Lw = Lk < Lp ? Lk : Lp;
+  Lw = Lw < Lm ? Lw : Lm;
+  if (Lw == INF || Lw < 1) {
+    if (tid == 0) sh.i32[6] = -1;
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int j = 0; j < ENT; ++j) {
+      const int i = tid * ENT + j;
+      if (i == Lw - 1) { sh.f64[kNW + 1] = excl + loc[j]; sh.u64[12] = ckey[i]; }
+    }
+    __syncthreads();
+    const double sk = sh.f64[kNW + 1];
+    const double t = u * sk;
+    // keep the first Lw entries, re-sorted by id
+    int m2 = 2;
+    while (m2 < Lw) m2 <<= 1;
+    for (int i = tid; i < n2; i += kNT) {
+      if (i < Lw) ckey[i] &= 0xFFFFFFFFull;
+      else { ckey[i] = ~0ull; cw[i] = 0.0f; }
+    }
+    __syncthreads();
+    block_bitonic_sort(ckey, cw, m2);
+    double ls2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < ENT; ++j) {
+      const int i = tid * ENT + j;
+      ls2 += (i < Lw) ? (double)cw[i] : 0.0;
+      loc[j] = ls2;
+    }
+    double tot2;
+    const double incl2 = block_scan_f64(ls2, sh, tot2);
+    const double excl2 = incl2 - ls2;
+#pragma unroll
+    for (int j = 0; j < ENT; ++j) {
+      const int i = tid * ENT + j;
+      if (i < Lw && cw[i] > 0.0f && excl2 + loc[j] > t) {
+        atomicMin((unsigned long long*)&sh.u64[14], (unsigned long long)i);
+        break;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t pos = (int64_t)sh.u64[14];
+      if (pos == INF) {  // rounding left t at the very end: the last kept id with weight
+        pos = Lw - 1;
+        while (pos > 0 && !(cw[pos] > 0.0f)) --pos;
+      }
+      const uint32_t pid = (uint32_t)(ckey[pos] & 0xFFFFFFFFull);
+      sh.u64[10] = pid;
+      sh.u64[11] = (uint64_t)Lw;
+      a.out_ids[row] = (int32_t)pid;
+      if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+    }
+    __syncthreads();
+  }
+}
+
 // One row on the summary path.  d holds the loads of the row's groups,
 // issued by the caller.  Returns false (uniformly across the block) when the
 // row must be redone by the general pipeline.
@@ -388,9 +643,25 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     }
   }
 
+  // the row's uniform, while the loads are in flight
+  double u = 0.0;
+  if (!greedy) {
+    if (a.uniforms) {
+      u = a.uniforms[row];
+    } else {
+      const uint64_t x = splitmix64_counter_output(a.seed, (uint64_t)row, a.step);
+      u = (double)(x >> 11) * 0x1p-53;
+    }
+    u = uniform_f64(u);
+  }
+
   // ---- the pass over the row (loads already in flight) ----------------------------
   float best = -__builtin_inff();
-  int bq = -1;                   // the thread's largest group (its data goes to sm.bdat; not for no-filter rows)
+  // the thread's two largest groups (not for no-filter rows): maxima, rounds
+  // and data, kept branch-free in registers and stored to LDS after the pass
+  float best2 = -__builtin_inff();
+  int bq = -1, sq = -1;
+  const bool track = !nofilter;
   double lsum = 0.0;             // top-p rows: this thread's weight total (frame K_t)
   float kfr = -__builtin_inff();  // K_t; -inf until the thread's first finite group
   float negk = 0.0f;             // -K_t (0 before the first finite group: weights are 0 there)
@@ -403,9 +674,12 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     float g = group_max(z);
     special = special || !(g == g);
     g = valid && g == g ? g : -__builtin_inff();
-    if (!nofilter && g > best) {
-      bq = q;
-      sm.bdat[tid] = d[q];
+    if (track) {
+      const bool up1 = g > best;
+      const bool up2 = !up1 && g > best2;
+      best2 = up1 ? best : (up2 ? g : best2);
+      sq = up1 ? bq : (up2 ? q : sq);
+      bq = up1 ? q : bq;
     }
     best = max2f(best, g);
     // filter rows: the group maximum; no-filter rows: the group weight (below)
@@ -431,29 +705,32 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     else lsum += valid ? (double)s : 0.0;
   }
 
-  // ---- wave records, one barrier ----------------------------------------------------
+  u32x4 bdat = d[0], sdat = d[0];
+  if (track) {
+    // the data of the two largest groups, by a static scan of the registers
+#pragma unroll
+    for (int q = 1; q < kQ; ++q) {
+      bdat.x = q == bq ? d[q].x : bdat.x; bdat.y = q == bq ? d[q].y : bdat.y;
+      bdat.z = q == bq ? d[q].z : bdat.z; bdat.w = q == bq ? d[q].w : bdat.w;
+      sdat.x = q == sq ? d[q].x : sdat.x; sdat.y = q == sq ? d[q].y : sdat.y;
+      sdat.z = q == sq ? d[q].z : sdat.z; sdat.w = q == sq ? d[q].w : sdat.w;
+    }
+  }
+
+  // ---- wave records ----------------------------------------------------------------
   {
     const float wm = dpp_wave_max_f32(best);
     const float kw = wm > -__builtin_inff() && weights ? __builtin_floorf(wm * chi) : 0.0f;  // K_w >= K_t
     if (nofilter) sm.kref[tid] = negk;
     if (weights && !nofilter) lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
     const double ws = (pon && !greedy) ? dpp_wave_sum_f64(lsum) : 0.0;
-    uint32_t wcnt = 0;
-    if (mon && !greedy) {
-      const float wlo = minp_bound(wm, tlf);
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const float g = sm.tsum[q * kNT + tid];
-        wcnt += (uint32_t)__builtin_popcountll(__ballot(g > -__builtin_inff() && g >= wlo));
-      }
-    }
     uint32_t warg = 0xFFFFFFFFu;
     if (greedy) {
       uint32_t idx = 0xFFFFFFFFu;
       if (best == wm && wm > -__builtin_inff()) {
         // bq is the first of the thread's groups holding its maximum
         float z[8];
-        unpack8(sm.bdat[tid], z);
+        unpack8(bdat, z);
 #pragma unroll
         for (int e = 7; e >= 0; --e)
           if (z[e] == wm) idx = (uint32_t)(bq * kNT + tid) * 8u + (uint32_t)e;
@@ -463,32 +740,32 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     const uint32_t wflags = __ballot(bad || special) != 0 ? 1u : 0u;
     if (lane == 0) {
       sh.w_max[wid] = wm; sh.w_negk[wid] = -kw; sh.w_sum[wid] = ws;
-      sh.w_cnt[wid] = wcnt; sh.w_arg[wid] = warg; sh.w_flags[wid] = wflags;
+      sh.w_arg[wid] = warg; sh.w_flags[wid] = wflags;
     }
-    if (!greedy && !nofilter && tid < kBins) {
-      sm.bcnt[tid] = 0u;
-      sm.bmass[tid] = 0.0f;
+    if (!greedy && !nofilter) {
+      if (tid < kBins) {
+        sm.bcnt[tid] = 0u;
+        sm.bmass[tid] = 0.0f;
+      }
+      if (tid == kNT - 1) { sh.i32[3] = 0; sh.i32[6] = 0; }
     }
-    if (tid == 0) { sh.i32[3] = 0; sh.i32[6] = 0; }
   }
   __syncthreads();
 
-  // ---- wave 0: the row's values and what follows ---------------------------------------
+  // ---- wave 0: the row's values and the mode (lane w reads record w) ----------------
   if (wid == 0) {
-    const bool in = lane < kNW;
-    const float rm = in ? sh.w_max[lane] : -__builtin_inff();
+    const bool rin = lane < kNW;
+    const float rm = rin ? sh.w_max[lane] : -__builtin_inff();
     const float m = dpp_wave_max_f32(rm);
-    const bool flagged = __ballot(in && sh.w_flags[lane] != 0u) != 0;
     int32_t mode = kModeFallback;
-    float negks = 0.0f, zt = -__builtin_inff(), zc = -FLT_MAX;
+    float negks = 0.0f, zt = -__builtin_inff(), zc0 = -FLT_MAX;
     double S = 0.0, Pm = 0.0;
-    uint32_t arg = 0;
-    if (flagged) {
+    uint32_t argmax = 0u;
+    if (__ballot(rin && sh.w_flags[lane] != 0u)) {
       mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
     } else if (greedy) {
       mode = kModeGreedy;
-      const uint32_t cand = in && rm == m ? sh.w_arg[lane] : 0xFFFFFFFFu;
-      arg = m > -__builtin_inff() ? dpp_wave_min_u32(cand) : 0u;
+      argmax = m > -__builtin_inff() ? dpp_wave_min_u32(rin && rm == m ? sh.w_arg[lane] : 0xFFFFFFFFu) : 0u;
     } else if (m > -__builtin_inff() && m < __builtin_inff() && m * chi > -1048576.0f && m * chi < 1048576.0f) {
       // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
       negks = -__builtin_floorf(m * chi);
@@ -497,7 +774,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       } else {
         bool ok = true;
         if (pon) {
-          const double x = in ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
+          const double x = rin ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
           S = dpp_wave_sum_f64(x);
           ok = S > 0.0 && S < 1e300;
           Pm = (double)P.top_p * S;
@@ -506,28 +783,29 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           bool found;
           zt = minp_threshold(m, tdl, found);
           ok = ok && found;
-          zc = zt > -FLT_MAX ? zt : -FLT_MAX;
+          zc0 = zt > -FLT_MAX ? zt : -FLT_MAX;
         }
-        const uint32_t ub = mon ? dpp_wave_sum_u32(in ? sh.w_cnt[lane] : 0u) : 0xFFFFFFFFu;
+        // min-p rows gather at the exact threshold; small rows take every
+        // element; the others first bound the cut with a histogram
         if (!ok) mode = kModeFallback;
-        else if (mon && !kon && !pon && ub > (uint32_t)(kCandCap / 8)) mode = kModeMinpStream;
-        else if ((mon && ub <= (uint32_t)(kCandCap / 8)) || ngroups <= kCandCap / 8) mode = kModeCand;
-        else mode = kModeHist;
+        else mode = (mon || ngroups <= kCandCap / 8) ? kModeCand : kModeHist;
       }
     }
     if (lane == 0) {
-      sh.r_m = m; sh.r_negks = negks; sh.r_zt = zt; sh.r_zc = zc;
-      sh.r_S = S; sh.r_Pm = Pm; sh.r_mode = mode; sh.r_arg = arg;
+      sh.r_m = m; sh.r_negks = negks; sh.r_zt = zt; sh.r_zc = zc0;
+      sh.r_S = S; sh.r_Pm = Pm; sh.r_mode = mode; sh.r_arg = argmax;
     }
   }
   __syncthreads();
-  const int32_t mode = sh.r_mode;
-  const float m = sh.r_m;
+  const float m = sh.r_m, negks = sh.r_negks, zt = sh.r_zt, zc0 = sh.r_zc;
+  double S = sh.r_S;
+  const double Pm = sh.r_Pm;
+  int32_t mode = sh.r_mode;
   if (mode == kModeFallback) return false;
 
   if (mode == kModeGreedy) {
-    const uint32_t argmax = sh.r_arg;
     path |= ARCS_PATH_GREEDY;
+    const uint32_t argmax = sh.r_arg;
     if (tid == 0) {
       a.out_ids[row] = (int32_t)argmax;
       if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
@@ -544,18 +822,20 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     return true;
   }
 
-  const float negks = sh.r_negks;
-  double u;
-  if (a.uniforms) {
-    u = a.uniforms[row];
-  } else {
-    const uint64_t x = splitmix64_counter_output(a.seed, (uint64_t)row, a.step);
-    u = (double)(x >> 11) * 0x1p-53;
+  // ---- the candidates z >= zc0 from the registers (min-p rows, small rows) ----------
+  int nc = -1;
+  if (mode == kModeCand) {
+    gather_candidates(rv, sm, sh, zc0, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
+    __syncthreads();
+    nc = sh.i32[3];
+    // more than the list holds (min-p rows only): masked sums for min-p alone,
+    // else a histogram bound above the threshold
+    if (nc > kCandCap) mode = (!kon && !pon) ? kModeMinpStream : kModeHist;
   }
 
   int64_t id = -1;
   int64_t L = V;
-  double S = sh.r_S, S_K = 0.0;
+  double S_K = 0.0;
   uint32_t cut_key = 0u;
   int64_t cut_idx = -1;
 
@@ -566,9 +846,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     S_K = S;
     id = (int64_t)sh.u64[10];
   } else if (mode == kModeMinpStream) {
-    // ---- min-p alone over many groups: masked sums (registers) and the id-order draw --
+    // ---- min-p alone over many groups: masked sums and the id-order draw ------------
     path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
-    const float zt = sh.r_zt;
     {
       u32x4 dd[kQ];
       issue_row_loads(rv, ngroups, dd);  // the row again, from cache
@@ -592,9 +871,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     S = 0.0;
   } else {
     path |= ARCS_PATH_CUTOFF;
-    const double Pm = sh.r_Pm;
-    const float zt = sh.r_zt;
-    float zc = sh.r_zc;
+    float zc = zc0;
     if (mode == kModeHist) {
       // a histogram of the threads' two largest group maxima by weight, 8
       // bins per unit of log2 weight below the row maximum: counts (top-k)
@@ -648,236 +925,29 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           const float theta = (m - edge) - (1e-5f * (__builtin_fabsf(m) + edge) + 1e-30f);
           zn = theta > zc ? theta : zc;
         }
-        if (lane == 0) sh.r_zc = zn;
+        if (lane == 0) { sh.r_zc = zn; sh.i32[3] = 0; }
       }
       __syncthreads();
       zc = sh.r_zc;
       if (!(zc > -__builtin_inff())) return false;
+      // ---- gather the candidates z >= zc -------------------------------------------
+      gather_candidates(rv, sm, sh, zc, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
+      __syncthreads();
+      nc = sh.i32[3];
     }
     const bool minp_complete = mon && !(zc > zt);
     if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
-
-    // ---- gather the candidates z >= zc ---------------------------------------------
-    {
-      // the thread's largest group from registers: counts, one wave scan,
-      // one LDS atomic per wave
-      const bool pa = bq >= 0 && best >= zc;
-      const u32x4 bdat = pa ? sm.bdat[tid] : u32x4{0u, 0u, 0u, 0u};
-      uint32_t n = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) n += pa && bf16_at(bdat, e) >= zc ? 1u : 0u;
-      if (__ballot(n != 0)) {
-        const uint32_t incl = dpp_wave_incl_scan_u32(n);
-        uint32_t base = 0;
-        if (lane == kWave - 1) base = (uint32_t)atomicAdd(&sh.i32[3], (int)incl);
-        base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
-        uint32_t pos = base + incl - n;
-        if (pa) {
-          const int64_t i0 = (int64_t)(bq * kNT + tid) * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float z = bf16_at(bdat, e);
-            if (z >= zc) {
-              if (pos < (uint32_t)kCandCap) {
-                sm.ckey[pos] = cand_key(z, i0 + e);
-                sm.cw[pos] = wexp(z, chi, clo, negks);
-              }
-              ++pos;
-            }
-          }
-        }
-      }
-      // the thread's other groups above the bound: re-read
-      uint32_t xmask = 0;
-#pragma unroll
-      for (int q = 0; q < kQ; ++q) xmask |= (q != bq && sm.tsum[q * kNT + tid] >= zc) ? (1u << q) : 0u;
-      while (xmask) {
-        const int q = __builtin_ctz(xmask);
-        xmask &= xmask - 1u;
-        const int j = q * kNT + tid;
-        const u32x4 dv = rv[j];
-        for (int e = 0; e < 8; ++e) {
-          const float z = bf16_at(dv, e);
-          if (z >= zc) {
-            const int slot = atomicAdd(&sh.i32[3], 1);
-            if (slot < kCandCap) {
-              sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
-              sm.cw[slot] = wexp(z, chi, clo, negks);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int nc = sh.i32[3];
-    if (nc > kCandCap || nc == 0) return false;
-
-    constexpr int64_t INF = INT64_MAX;
+    if (nc > kCandCap || nc <= 0) return false;
     if (nc <= kSmallSort) {
-      // ---- small candidate set: one wave ----------------------------------------------
       if (wid == 0) {
-        const bool in = lane < nc;
-        const uint64_t key = in ? sm.ckey[lane] : ~0ull;
-        const float w = in ? sm.cw[lane] : 0.0f;
-        // rank by (value desc, id asc) = ascending key
-        const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
-        uint32_t r = 0;
-        for (int j = 0; j < nc; ++j) {
-          const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)khi, j);
-          const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
-          r += (oh < khi || (oh == khi && ol < klo)) ? 1u : 0u;
-        }
-        if (in) { sm.skey[r] = key; sm.sw[r] = w; }
-        wave_lds_sync();
-        const uint64_t skey = in ? sm.skey[lane] : ~0ull;
-        const float sw = in ? sm.sw[lane] : 0.0f;
-        const double cum = dpp_wave_incl_scan_f64((double)sw);
-        const int64_t Lk = (kon && (int64_t)P.top_k <= nc) ? (int64_t)P.top_k : INF;
-        int64_t Lp = INF;
-        if (pon) {
-          const uint64_t hit = __ballot(in && cum >= Pm);
-          if (hit) Lp = __builtin_ctzll(hit) + 1;
-        }
-        int64_t Lm = INF;
-        if (minp_complete) Lm = __builtin_popcountll(__ballot(in && key_value(~(uint32_t)(skey >> 32)) >= zt));
-        int64_t Lw = Lk < Lp ? Lk : Lp;
-        Lw = Lw < Lm ? Lw : Lm;
-        if (Lw == INF || Lw < 1) {
-          if (lane == 0) sh.i32[6] = -1;
-        } else {
-          const int lc = (int)Lw - 1;
-          const uint64_t cb = (uint64_t)__builtin_bit_cast(uint64_t, cum);
-          const double sk = __builtin_bit_cast(
-              double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(cb >> 32), lc) << 32) |
-                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cb, lc));
-          const uint64_t ck = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(skey >> 32), lc) << 32) |
-                              (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)skey, lc);
-          const double t = u * sk;
-          // the kept entries in id order: rank by id, then an in-order scan
-          const bool kept = lane < Lw;
-          const uint32_t myid = (uint32_t)skey;
-          uint32_t r2 = 0;
-          for (int j = 0; j < (int)Lw; ++j)
-            r2 += (uint32_t)__builtin_amdgcn_readlane((int)myid, j) < myid ? 1u : 0u;
-          wave_lds_sync();
-          if (kept) { sm.skey[r2] = myid; sm.sw[r2] = sw; }
-          wave_lds_sync();
-          const uint32_t id2 = kept ? (uint32_t)sm.skey[lane] : 0u;
-          const float w2 = kept ? sm.sw[lane] : 0.0f;
-          const double c2 = dpp_wave_incl_scan_f64((double)w2);
-          const uint64_t hit = __ballot(kept && w2 > 0.0f && c2 > t);
-          const uint64_t nz = __ballot(kept && w2 > 0.0f);
-          // rounding can leave t past the last boundary: the last kept id with weight
-          const int ls = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
-          const uint32_t pid = (uint32_t)__builtin_amdgcn_readlane((int)id2, ls);
-          if (lane == 0) {
-            sh.u64[10] = pid;
-            sh.u64[11] = (uint64_t)Lw;
-            sh.f64[kNW + 1] = sk;
-            sh.u64[12] = ck;
-            a.out_ids[row] = (int32_t)pid;
-            if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
-          }
-        }
+        const uint64_t key = lane < nc ? sm.ckey[lane] : ~0ull;
+        const float w = lane < nc ? sm.cw[lane] : 0.0f;
+        if (!small_cut_draw(a, row, sm, sh, nc, key, w, kon, P.top_k, pon, Pm, minp_complete, zt, u) && lane == 0)
+          sh.i32[6] = -1;
       }
       __syncthreads();
     } else {
-      // ---- larger candidate set: block bitonic sort in LDS ------------------------
-      int n2 = 128;
-      while (n2 < nc) n2 <<= 1;
-      for (int i = nc + tid; i < n2; i += kNT) { sm.ckey[i] = ~0ull; sm.cw[i] = 0.0f; }
-      if (tid == 0) { sh.u64[13] = (uint64_t)INF; sh.u64[14] = (uint64_t)INF; sh.u64[15] = 0ull; }
-      __syncthreads();
-      block_bitonic_sort(sm.ckey, sm.cw, n2);
-      // prefix mass over the sorted order (ENT consecutive entries per thread)
-      constexpr int ENT = kCandCap / kNT;
-      double loc[ENT];
-      double lsum_c = 0.0;
-      uint32_t nm = 0;
-#pragma unroll
-      for (int j = 0; j < ENT; ++j) {
-        const int i = tid * ENT + j;
-        lsum_c += (i < nc) ? (double)sm.cw[i] : 0.0;
-        loc[j] = lsum_c;
-        if (minp_complete && i < nc && key_value(~(uint32_t)(sm.ckey[i] >> 32)) >= zt) ++nm;
-      }
-      if (minp_complete) {
-        const uint32_t wn = dpp_wave_sum_u32(nm);
-        if (lane == 0 && wn) atomicAdd((unsigned long long*)&sh.u64[15], (unsigned long long)wn);
-      }
-      double tot;
-      const double incl = block_scan_f64(lsum_c, sh, tot);
-      const double excl = incl - lsum_c;
-      if (pon) {
-#pragma unroll
-        for (int j = 0; j < ENT; ++j) {
-          const int i = tid * ENT + j;
-          if (i < nc && excl + loc[j] >= Pm) {
-            atomicMin((unsigned long long*)&sh.u64[13], (unsigned long long)(i + 1));
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      const int64_t Lk = (kon && (int64_t)P.top_k <= nc) ? (int64_t)P.top_k : INF;
-      const int64_t Lp = (int64_t)sh.u64[13];
-      const int64_t Lm = minp_complete ? (int64_t)sh.u64[15] : INF;
-      int64_t Lw = Lk < Lp ? Lk : Lp;
-      Lw = Lw < Lm ? Lw : Lm;
-      if (Lw == INF || Lw < 1) {
-        if (tid == 0) sh.i32[6] = -1;
-        __syncthreads();
-      } else {
-#pragma unroll
-        for (int j = 0; j < ENT; ++j) {
-          const int i = tid * ENT + j;
-          if (i == Lw - 1) { sh.f64[kNW + 1] = excl + loc[j]; sh.u64[12] = sm.ckey[i]; }
-        }
-        __syncthreads();
-        const double sk = sh.f64[kNW + 1];
-        const double t = u * sk;
-        // keep the first Lw entries, re-sorted by id
-        int m2 = 2;
-        while (m2 < Lw) m2 <<= 1;
-        for (int i = tid; i < n2; i += kNT) {
-          if (i < Lw) sm.ckey[i] &= 0xFFFFFFFFull;
-          else { sm.ckey[i] = ~0ull; sm.cw[i] = 0.0f; }
-        }
-        __syncthreads();
-        block_bitonic_sort(sm.ckey, sm.cw, m2);
-        double ls2 = 0.0;
-#pragma unroll
-        for (int j = 0; j < ENT; ++j) {
-          const int i = tid * ENT + j;
-          ls2 += (i < Lw) ? (double)sm.cw[i] : 0.0;
-          loc[j] = ls2;
-        }
-        double tot2;
-        const double incl2 = block_scan_f64(ls2, sh, tot2);
-        const double excl2 = incl2 - ls2;
-#pragma unroll
-        for (int j = 0; j < ENT; ++j) {
-          const int i = tid * ENT + j;
-          if (i < Lw && sm.cw[i] > 0.0f && excl2 + loc[j] > t) {
-            atomicMin((unsigned long long*)&sh.u64[14], (unsigned long long)i);
-            break;
-          }
-        }
-        __syncthreads();
-        if (tid == 0) {
-          int64_t pos = (int64_t)sh.u64[14];
-          if (pos == INF) {  // rounding left t at the very end: the last kept id with weight
-            pos = Lw - 1;
-            while (pos > 0 && !(sm.cw[pos] > 0.0f)) --pos;
-          }
-          const uint32_t pid = (uint32_t)(sm.ckey[pos] & 0xFFFFFFFFull);
-          sh.u64[10] = pid;
-          sh.u64[11] = (uint64_t)Lw;
-          a.out_ids[row] = (int32_t)pid;
-          if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
-        }
-        __syncthreads();
-      }
+      large_cut_draw(a, row, sm.ckey, sm.cw, sh, nc, kon, P.top_k, pon, Pm, minp_complete, zt, u);
     }
     if (sh.i32[6] < 0) return false;
     if (!debug) return true;

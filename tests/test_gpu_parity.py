@@ -21,7 +21,7 @@ import pytest
 
 from _util import ensure_built, hist_to_device, to_device_logits
 from oracle import sampler as oracle
-from workloads import f32_to_bf16_bits, make_params, make_workload
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits, make_params, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -343,6 +343,41 @@ def test_sort_skip_path_and_inert_filters(arcs):
     for b in range(8):
         if stats2[b]["kept"] == 30_000:
             assert ids2[b] == ids[b]
+
+
+def test_minp_rows_with_crowded_threads(arcs):
+    """min-p rows whose large values crowd a few 16-byte groups 8,192 tokens
+    apart (one thread's share of the row on the single-pass kernel): several
+    such groups per thread, a thread set past one wave's candidate capacity
+    after the exact threshold, and a dense run of 300 equal maxima."""
+    V = 129_280
+    base = make_workload("zipf_b256_bf16_t0.7_k50_p0.9_minp0.05", B=6)
+    z = np.stack([bf16_bits_to_f32(base.logits[b]) for b in range(6)])
+    hi = np.float32(4.0)
+    for b in (0, 1):
+        for q in range(6):
+            z[b, q * 8192 + 5 * 8 + 3] = hi - np.float32(0.125 * q)
+    for t in range(8):
+        for q in range(16):
+            g = q * 1024 + t
+            if g * 8 + 8 <= V:
+                z[2, g * 8:g * 8 + 8] = hi
+                z[3, g * 8:g * 8 + 8] = hi
+    z[4, :300] = hi
+    z[5, :300] = hi
+    w = base
+    w.logits = f32_to_bf16_bits(z)
+    p = make_params(6, temperature=0.7, min_p=0.05)
+    for b in (1, 3, 5):
+        p[b]["top_k"] = 50
+        p[b]["top_p"] = 0.9
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "crowded min-p")
+    logits = to_device_logits(w.logits, w.dtype)
+    got = arcs.sample(logits, arcs.params_to_device(w.params), seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
 
 
 def test_deterministic_replay(arcs):
