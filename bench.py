@@ -39,18 +39,25 @@ METRIC = "sampled rows/s and achieved HBM GB/s (% of peak) at B=256, V=129,280"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "zipf_b256_bf16_greedy"
 ROTATE_BYTES = 512 * 2**20
-KERNEL_SOURCES = ["device_common.hpp", "sample_common.hpp", "sample_kernel.hip", "argmax_kernel.hip", "launch.hpp"]
+# the sources each kernel is built from (with the launcher): a committed
+# counter summary holds only while these are unchanged
+KERNEL_SOURCES = {
+    "argmax": ["device_common.hpp", "launch.hpp", "api.hip", "argmax_kernel.hip"],
+    "sample": ["device_common.hpp", "launch.hpp", "api.hip", "sample_common.hpp", "sample_kernel.hip"],
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "decode_step_token_row_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "arcs.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -68,14 +75,15 @@ def algorithmic_bytes(w) -> int:
 
 def kernel_name(w) -> str:
     """The kernel one step launches for this workload (as the launcher picks it)."""
+    fits = w.dtype == "bf16" and w.V % 8 == 0 and w.V <= 131072
     if w.greedy_only:
-        return "argmax_kernel"
-    if w.dtype == "bf16" and w.V % 8 == 0 and w.V <= 131072:
+        return "argmax_fast_kernel" if fits else "argmax_kernel"
+    if fits:
         return "sample_summary_kernel"
     return "sample_kernel"
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, kind: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None when absent or taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
@@ -86,7 +94,7 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_hash") != kernel_source_hash():
+    if kv.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -195,6 +203,7 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i)
     e1.record()
+    issue = time.perf_counter() - t0  # host time to enqueue the launches
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = e0.elapsed_time(e1)
@@ -215,10 +224,11 @@ def main():
     alg = algorithmic_bytes(w)
     # one launch per step: the average launch duration over the timed region
     achieved = alg / (ms_per_step * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload, "argmax" if w.greedy_only else "sample")
     rows_per_s = w.B / (ms_per_step * 1e-3)
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step, launch avg {avg_launch_ms * 1e3:.2f} us "
-        f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.2f}), {achieved:.0f} GB/s, wall {wall:.3f}s")
+        f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.2f}), {achieved:.0f} GB/s, wall {wall:.4f}s, "
+        f"host enqueue {issue / args.steps * 1e6:.2f} us/step")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -156,13 +156,31 @@ __global__ __launch_bounds__(NT) void argmax_kernel(const void* __restrict__ log
 // all kFastQ loads of the row issued at once through buffer resources that
 // cover only the rest of the row (lanes past the end read zeros without
 // touching memory).  512 threads x 32 loads (two waves per SIMD, up to 256
-// VGPRs each) keep 256 KB per CU in flight.  Each thread keeps the data of
-// the first group reaching its maximum, so the lowest index is found from
-// registers once the block maximum is known.  Special maxima (NaN patterns, zeros, -inf) take the same
-// exact float32 path as the general kernel.
+// VGPRs each) keep 256 KB per CU in flight.
+//
+// The pass works on the raw 16-bit patterns as signed integers, with no
+// per-element order transform: non-negative floats order like their
+// patterns, negative ones in reverse, so a thread's largest value is its
+// largest pattern when that is >= 0 and otherwise its smallest pattern.
+// Each round reduces its group with packed 16-bit max and min, and the two
+// halves of each go into signed 32-bit keys (pattern << 16 | round code)
+// reduced with max / min: the round code (31 - q for the maximum, q for the
+// minimum) makes the first round holding a thread's extreme win ties.  After
+// the block maximum is known, each thread holding it finds the element in
+// that round's registers.  Special maxima (NaN patterns, zeros, -inf) take
+// the same exact float32 path as the general kernel.
 constexpr int kFastNT = 512;
 constexpr int kFastQ = 32;
 constexpr int64_t kFastGroups = (int64_t)kFastNT * kFastQ;
+static_assert(kFastQ <= 32, "round codes and the round switch cover 32 rounds");
+
+__device__ __forceinline__ s16x2 as_s16x2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
+__device__ __forceinline__ uint32_t pk_max_u(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2(a), as_s16x2(b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_s16x2(a), as_s16x2(b)));
+}
 
 __global__ __launch_bounds__(kFastNT) void argmax_fast_kernel(const void* __restrict__ logits, int64_t V,
                                                               int64_t stride, int32_t* __restrict__ out) {
@@ -187,21 +205,30 @@ __global__ __launch_bounds__(kFastNT) void argmax_fast_kernel(const void* __rest
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  int best = INT_MIN;
-  int bq = 0;  // the first of the thread's groups reaching its maximum, and its data
-  u32x4 bdat = d[0];
+  int pk = INT_MIN, nk = INT_MAX;  // (largest pattern, 31 - round), (smallest pattern, round)
 #pragma unroll
   for (int q = 0; q < kFastQ; ++q) {
-    int g = KT::group_key(d[q]);
-    g = tid < ngroups - q * kFastNT ? g : INT_MIN;
-    const bool up = g > best;
-    best = up ? g : best;
-    bq = up ? q : bq;
-    bdat.x = up ? d[q].x : bdat.x; bdat.y = up ? d[q].y : bdat.y;
-    bdat.z = up ? d[q].z : bdat.z; bdat.w = up ? d[q].w : bdat.w;
+    const uint32_t a = pk_max_u(pk_max_u(d[q].x, d[q].y), pk_max_u(d[q].z, d[q].w));
+    const uint32_t b = pk_min_u(pk_min_u(d[q].x, d[q].y), pk_min_u(d[q].z, d[q].w));
+    int ax = (int)((a << 16) | (uint32_t)(31 - q)), ay = (int)((a & 0xFFFF0000u) | (uint32_t)(31 - q));
+    int bx = (int)((b << 16) | (uint32_t)q), by = (int)((b & 0xFFFF0000u) | (uint32_t)q);
+    if ((q + 1) * kFastNT > ngroups) {  // a round the row does not fill (uniform)
+      const bool valid = tid < ngroups - q * kFastNT;
+      ax = valid ? ax : INT_MIN; ay = valid ? ay : INT_MIN;
+      bx = valid ? bx : INT_MAX; by = valid ? by : INT_MAX;
+    }
+    pk = max(max(pk, ax), ay);
+    nk = min(min(nk, bx), by);
+    // keep the reduction in round order (no deferred trees of per-round keys)
+    asm volatile("" : "+v"(pk), "+v"(nk));
   }
+  const int cp = pk >> 16, cn = nk >> 16;
+  const int raw = cp >= 0 ? cp : cn;
+  const int qsel = cp >= 0 ? 31 - (pk & 0xFFFF) : (nk & 0xFFFF);
+  int tk = (int)(short)(raw ^ ((raw >> 15) & 0x7FFF));  // the order key of the thread's largest value
+  tk = tid < ngroups ? tk : INT_MIN;
 
-  const int wmax = wave_max_i32(best);
+  const int wmax = dpp_wave_max_i32(tk);
   if (lane == 0) s_red[wid] = wmax;
   if (tid == 0) s_idx = 0xFFFFFFFFu;
   __syncthreads();
@@ -211,12 +238,39 @@ __global__ __launch_bounds__(kFastNT) void argmax_fast_kernel(const void* __rest
 
   const bool special = K > KT::kPosInf || K <= KT::kNegInf || K == 0 || K == -1;
   if (!special) {
+    // the pattern of the maximum (not +-0, so patterns compare exactly)
+    const uint32_t R = (uint32_t)(K ^ ((K >> 15) & 0x7FFF)) & 0xFFFFu;
     uint32_t idx = 0xFFFFFFFFu;
-    if (best == K) {
-      const uint32_t base = (uint32_t)(bq * kFastNT + tid) * 8u;
-#pragma unroll
-      for (int e = 7; e >= 0; --e)
-        if (KT::elem_key(bdat, e) == K) idx = base + (uint32_t)e;
+    uint64_t tied = __ballot(tk == K);
+    while (tied) {
+      const int t = __builtin_ctzll(tied);
+      tied &= tied - 1;
+      const int qu = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(qsel, t));
+      u32x4 v = d[0];
+      switch (qu) {
+#define ARCS_ROUND_(i) case i: v = d[i]; break;
+        ARCS_ROUND_(1) ARCS_ROUND_(2) ARCS_ROUND_(3) ARCS_ROUND_(4) ARCS_ROUND_(5) ARCS_ROUND_(6)
+        ARCS_ROUND_(7) ARCS_ROUND_(8) ARCS_ROUND_(9) ARCS_ROUND_(10) ARCS_ROUND_(11) ARCS_ROUND_(12)
+        ARCS_ROUND_(13) ARCS_ROUND_(14) ARCS_ROUND_(15) ARCS_ROUND_(16) ARCS_ROUND_(17) ARCS_ROUND_(18)
+        ARCS_ROUND_(19) ARCS_ROUND_(20) ARCS_ROUND_(21) ARCS_ROUND_(22) ARCS_ROUND_(23) ARCS_ROUND_(24)
+        ARCS_ROUND_(25) ARCS_ROUND_(26) ARCS_ROUND_(27) ARCS_ROUND_(28) ARCS_ROUND_(29) ARCS_ROUND_(30)
+        ARCS_ROUND_(31)
+#undef ARCS_ROUND_
+        default: break;
+      }
+      uint32_t e = 8;
+      e = (v.w >> 16) == R ? 7u : e;
+      e = (v.w & 0xFFFFu) == R ? 6u : e;
+      e = (v.z >> 16) == R ? 5u : e;
+      e = (v.z & 0xFFFFu) == R ? 4u : e;
+      e = (v.y >> 16) == R ? 3u : e;
+      e = (v.y & 0xFFFFu) == R ? 2u : e;
+      e = (v.x >> 16) == R ? 1u : e;
+      e = (v.x & 0xFFFFu) == R ? 0u : e;
+      if (lane == t && e < 8) {
+        const uint32_t i = (uint32_t)(qu * kFastNT + tid) * 8u + e;
+        idx = i < idx ? i : idx;
+      }
     }
     const uint32_t wmin = dpp_wave_min_u32(idx);
     if (lane == 0 && wmin != 0xFFFFFFFFu) atomicMin(&s_idx, wmin);

@@ -223,6 +223,18 @@ __device__ __forceinline__ uint32_t dpp_wave_min_u32(uint32_t v) {
   t = dpp_u32<0x143, 0xC>(id, v); v = v < t ? v : t;
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+// maximum across the wave, signed (same value in every lane)
+__device__ __forceinline__ int dpp_wave_max_i32(int v) {
+  const uint32_t id = 0x80000000u;
+  int t;
+  t = (int)dpp_u32<0xB1>(id, (uint32_t)v); v = v > t ? v : t;
+  t = (int)dpp_u32<0x4E>(id, (uint32_t)v); v = v > t ? v : t;
+  t = (int)dpp_u32<0x141>(id, (uint32_t)v); v = v > t ? v : t;
+  t = (int)dpp_u32<0x140>(id, (uint32_t)v); v = v > t ? v : t;
+  t = (int)dpp_u32<0x142, 0xA>(id, (uint32_t)v); v = v > t ? v : t;
+  t = (int)dpp_u32<0x143, 0xC>(id, (uint32_t)v); v = v > t ? v : t;
+  return __builtin_amdgcn_readlane(v, 63);
+}
 // sum across the wave (same value in every lane)
 __device__ __forceinline__ uint32_t dpp_wave_sum_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)dpp_wave_incl_scan_u32(v), 63);

@@ -132,6 +132,33 @@ def test_argmax_special_values(arcs, dtype, V):
     assert np.array_equal(got, want), (got, want)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [8, 1000, 4096, 129_280, 131_072])
+def test_argmax_negative_maxima_and_placed_ties(arcs, dtype, V):
+    """Rows whose maximum is negative (ties included), maxima repeated at
+    tokens 4,096 apart and within one run of 8, +inf, denormals."""
+    rng = np.random.default_rng(V + 7)
+    rows = list(rng.integers(-9, -1, (6, V)).astype(np.float32) * 0.25)  # maximum -0.5, many ties
+    r = np.full(V, -7.0, np.float32); r[V - 1] = -6.0; rows.append(r)        # last index
+    r = np.full(V, -7.0, np.float32); r[0] = -6.5; rows.append(r)            # first index
+    r = np.full(V, -1.0, np.float32)
+    for j in range(3, V, 4096):
+        r[j] = 4.0
+    rows.append(r)
+    r = np.full(V, -1.0, np.float32)
+    for j in (V - 2, V - 6, V - 8):
+        r[j] = 9.0
+    rows.append(r)
+    r = np.full(V, 1.0, np.float32); r[V // 2] = np.inf; r[V // 3] = np.inf; rows.append(r)
+    r = np.full(V, -1e30, np.float32); r[V // 5] = -1e-40; r[V - 3] = -2e-40; rows.append(r)
+    r = np.full(V, -1e30, np.float32); r[V // 7] = 1e-40; rows.append(r)
+    x = np.stack(rows)
+    raw = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    want = oracle.argmax(raw, dtype)
+    got = arcs.argmax(to_device_logits(raw, dtype)).cpu().numpy()
+    assert np.array_equal(got, want), (got, want)
+
+
 def test_argmax_full_size_zipf_b256(arcs):
     w = make_workload("zipf_b256_bf16_greedy")
     want = oracle.argmax(w.logits, "bf16")
