@@ -250,7 +250,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # argmax compares raw 16-bit patterns as integers; sampling weighs in fp32
+        "dtype": "i16" if (w.greedy_only and w.dtype == "bf16") else "f32",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
