@@ -26,18 +26,21 @@ constexpr int kBins = 256;                     // summary path: bound histogram 
 //   general path: radix histograms, counts [kMaxBins] u32 + masses [kMaxBins] u64;
 //   summary path: one f32 per group of the row, [kMaxGroups] (group j at
 //     j): its weight sum (rows without filters) or its maximum (filter
-//     rows); each thread's reference exponent [kNT] f32; candidates (keys
-//     u64, weights f32) [kCandCap]; a bound histogram (counts u32, masses
-//     f32) [kBins]; a sorted copy of small candidate sets.
+//     rows); candidates (keys u64, weights f32) [kCandCap], or, for rows
+//     without filters (which gather no candidates), each thread's reference
+//     exponent [kNT] f32 at the same place; a bound histogram (counts u32,
+//     masses f32) [kBins]; a sorted copy of small candidate sets.
 constexpr size_t kUnionGeneric = (size_t)kMaxBins * 12;
 constexpr size_t kOffTsum = 0;
-constexpr size_t kOffKref = kOffTsum + (size_t)kMaxGroups * 4;
-constexpr size_t kOffCand = kOffKref + (size_t)kNT * 4;
+constexpr size_t kOffCand = kOffTsum + (size_t)kMaxGroups * 4;
+constexpr size_t kOffKref = kOffCand;
 constexpr size_t kOffHist = kOffCand + (size_t)kCandCap * 12;
 constexpr size_t kOffSort = kOffHist + (size_t)kBins * 8;
 constexpr size_t kUnionSummary = kOffSort + (size_t)kSmallSort * 12;
 static_assert(kOffCand % 16 == 0 && kOffHist % 16 == 0 && kOffSort % 16 == 0,
               "summary LDS layout");
+static_assert((size_t)kCandCap * 12 >= (size_t)kMaxDistinct * 4 && (size_t)kCandCap * 12 >= (size_t)kNT * 4,
+              "the candidate area also holds the build-time counts and the reference exponents");
 constexpr int64_t kMaxPenVocab = ARCS_MAX_PENALTY_VOCAB;
 
 // Dynamic LDS layout.
@@ -63,16 +66,16 @@ struct Smem {
 
 __host__ __device__ inline size_t pen_prefix_bytes(uint32_t bitmap_words) { return ((size_t)bitmap_words * 2 + 15) / 16 * 16; }
 
-// The penalty tables follow the general path's union area; rows that use
-// them (active penalties) run the general path, the others may use the
-// summary path's larger union area, which overlaps the tables.
+// The penalty tables follow the union area of the kernel's path: the general
+// kernel keeps per distinct id its count and its penalised logit; the summary
+// kernel keeps only the penalised logits, its counts live in the candidate
+// area while the tables are built (it is free then).
 inline size_t sample_lds_bytes(bool summary, bool pen_tables, int64_t V) {
-  size_t b = kUnionGeneric;
+  size_t b = summary ? kUnionSummary : kUnionGeneric;
   if (pen_tables) {
     const uint32_t bw = (uint32_t)((V + 31) / 32);
-    b += (size_t)bw * 4 + pen_prefix_bytes(bw) + (size_t)kMaxDistinct * 8;
+    b += (size_t)bw * 4 + pen_prefix_bytes(bw) + (size_t)kMaxDistinct * (summary ? 4 : 8);
   }
-  if (summary && b < kUnionSummary) b = kUnionSummary;
   return b;
 }
 
@@ -304,8 +307,8 @@ __device__ __forceinline__ bool is_kept(float z, int64_t idx, const KeptCtx& kc)
 // 3-6 radix levels, 7 tie split, 8 draw, 9 debug stats, 10-15 resident path.
 // Carve the dynamic LDS block: the union area (the general path uses its
 // first kUnionGeneric bytes, the summary path up to kUnionSummary), and the
-// penalty tables after the general part of the union area.
-__device__ __forceinline__ Smem carve_smem(unsigned char* raw, size_t union_bytes, uint32_t bitmap_words) {
+// penalty tables after the union area of the kernel's path.
+__device__ __forceinline__ Smem carve_smem(unsigned char* raw, bool summary, uint32_t bitmap_words) {
   Smem sm;
   sm.hcnt = (uint32_t*)raw;
   sm.hmass = (uint64_t*)(raw + (size_t)kMaxBins * 4);
@@ -317,12 +320,17 @@ __device__ __forceinline__ Smem carve_smem(unsigned char* raw, size_t union_byte
   sm.bmass = (float*)(raw + kOffHist + (size_t)kBins * 4);
   sm.skey = (uint64_t*)(raw + kOffSort);
   sm.sw = (float*)(raw + kOffSort + (size_t)kSmallSort * 8);
-  (void)union_bytes;
-  unsigned char* pen_base = raw + kUnionGeneric;
+  unsigned char* pen_base = raw + (summary ? kUnionSummary : kUnionGeneric);
   sm.bitmap = (uint32_t*)pen_base;
   sm.wprefix = (uint16_t*)(pen_base + (size_t)bitmap_words * 4);
-  sm.pcount = (uint32_t*)(pen_base + (size_t)bitmap_words * 4 + pen_prefix_bytes(bitmap_words));
-  sm.zpen = (float*)((unsigned char*)sm.pcount + (size_t)kMaxDistinct * 4);
+  unsigned char* after = pen_base + (size_t)bitmap_words * 4 + pen_prefix_bytes(bitmap_words);
+  if (summary) {
+    sm.pcount = (uint32_t*)(raw + kOffCand);  // only while the tables are built
+    sm.zpen = (float*)after;
+  } else {
+    sm.pcount = (uint32_t*)after;
+    sm.zpen = (float*)(after + (size_t)kMaxDistinct * 4);
+  }
   return sm;
 }
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
-  const Smem sm = carve_smem(smem_raw, kUnionGeneric, a.bitmap_words);
+  const Smem sm = carve_smem(smem_raw, false, a.bitmap_words);
   arcs_row_params P = a.params[row];
   PenCtx pc;
   uint32_t path;
@@ -89,6 +89,15 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
 __device__ __forceinline__ float bf16_at(u32x4 d, int e) {
   const uint32_t w = e < 2 ? d.x : e < 4 ? d.y : e < 6 ? d.z : d.w;
   return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// The values z' of group j (elements 8j .. 8j + 7) from its 16 bytes: the
+// bf16 widened, then, on rows with active penalties, the history ids among
+// them replaced by their penalised logits from the LDS tables.
+template <bool PEN>
+__device__ __forceinline__ void load_z8(u32x4 d, int j, const PenCtx& pc, float (&z)[8]) {
+  unpack8(d, z);
+  if (PEN && pc.on) apply_penalties<8>(z, (int64_t)j * 8, 8, pc);
 }
 
 // Maximum of a group.  v_max ignores quiet NaNs (the same as treating them
@@ -245,9 +254,10 @@ enum RowMode : int32_t {
 // the total weight is zero or not finite; else S (the total).  With `sync`
 // the id is left in sh.u64[10] for the whole block; otherwise waves other
 // than the drawing one return at once.
-__device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, const u32x4* rv, const Smem& sm,
-                                          Shared& sh, bool thread_frames, float zmask, float chi, float clo,
-                                          float negks, double u, bool sync, double& S) {
+template <bool PEN>
+__device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, const u32x4* rv, const PenCtx& pc,
+                                          const Smem& sm, Shared& sh, bool thread_frames, float zmask, float chi,
+                                          float clo, float negks, double u, bool sync, double& S) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   // lane l: groups wid*kNT + 16l + i, owned by threads 16l + i
   double v[16];
@@ -311,7 +321,7 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
       const float nk = thread_frames ? sm.kref[owner] : negks;
       const int dsh = (int)(negks - nk);
       float z[8];
-      unpack8(rv[j], z);
+      load_z8<PEN>(rv[j], j, pc, z);
       float acc = 0.0f, prev = 0.0f;
       int pe = -1, last_e = 0;
 #pragma unroll
@@ -342,18 +352,26 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
 // bound re-read from memory (rare).  A count above kCandCap means the list is
 // incomplete.  Threads whose largest group lies below the bound hold nothing,
 // and a wave where that holds for every lane does nothing.
-__device__ __forceinline__ void gather_candidates(const u32x4* rv, const Smem& sm, Shared& sh, float bound, float best,
-                                                  int bq, float best2, int sq, u32x4 da, u32x4 db, float chi,
-                                                  float clo, float negks) {
+template <bool PEN>
+__device__ __forceinline__ void gather_candidates(const u32x4* rv, const PenCtx& pc, const Smem& sm, Shared& sh,
+                                                  float bound, float best, int bq, float best2, int sq, u32x4 da,
+                                                  u32x4 db, float chi, float clo, float negks) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const bool pa = bq >= 0 && best >= bound;
   const bool pb = sq >= 0 && best2 >= bound;
   if (!__ballot(pa)) return;
+  float za[8], zb[8];
+  unpack8(da, za);
+  unpack8(db, zb);
+  if (PEN && pc.on) {
+    if (pa) apply_penalties<8>(za, (int64_t)(bq * kNT + tid) * 8, 8, pc);
+    if (pb) apply_penalties<8>(zb, (int64_t)(sq * kNT + tid) * 8, 8, pc);
+  }
   uint32_t n = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    n += pa && bf16_at(da, e) >= bound ? 1u : 0u;
-    n += pb && bf16_at(db, e) >= bound ? 1u : 0u;
+    n += pa && za[e] >= bound ? 1u : 0u;
+    n += pb && zb[e] >= bound ? 1u : 0u;
   }
   if (__ballot(n != 0)) {
     const uint32_t incl = dpp_wave_incl_scan_u32(n);
@@ -364,11 +382,10 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const Smem& s
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (h == 0 ? pa : pb) {
-        const u32x4 dv = h == 0 ? da : db;
         const int64_t i0 = (int64_t)((h == 0 ? bq : sq) * kNT + tid) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float z = bf16_at(dv, e);
+          const float z = h == 0 ? za[e] : zb[e];
           if (z >= bound) {
             if (pos < (uint32_t)kCandCap) {
               sm.ckey[pos] = cand_key(z, i0 + e);
@@ -391,9 +408,10 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const Smem& s
     const int q = __builtin_ctz(xmask);
     xmask &= xmask - 1u;
     const int j = q * kNT + tid;
-    const u32x4 dv = rv[j];
+    float zx[8];
+    load_z8<PEN>(rv[j], j, pc, zx);
     for (int e = 0; e < 8; ++e) {
-      const float z = bf16_at(dv, e);
+      const float z = zx[e];
       if (z >= bound) {
         const uint32_t slot = (uint32_t)atomicAdd(&sh.i32[3], 1);
         if (slot < (uint32_t)kCandCap) {
@@ -608,8 +626,10 @@ __device__ __forceinline__ void large_cut_draw(const SampleArgs& a, int64_t row,
 //                   one wave (or the block for large sets) and drawn from in
 //                   id order;
 //   min-p alone over many groups -> masked group sums and the id-order draw.
+template <bool PEN>
 __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
-                                           uint32_t path, const Smem& sm, Shared& sh, const u32x4 (&d)[kQ]) {
+                                           const PenCtx& pc, uint32_t path, const Smem& sm, Shared& sh,
+                                           const u32x4 (&d)[kQ]) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t V = a.V;
   const int ngroups = (int)(V / 8);
@@ -671,6 +691,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     const bool valid = tid < ngroups - q * kNT;
     float z[8];
     unpack8(d[q], z);
+    if (PEN && pc.on && valid) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
     float g = group_max(z);
     special = special || !(g == g);
     g = valid && g == g ? g : -__builtin_inff();
@@ -730,7 +751,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       if (best == wm && wm > -__builtin_inff()) {
         // bq is the first of the thread's groups holding its maximum
         float z[8];
-        unpack8(bdat, z);
+        load_z8<PEN>(bdat, bq * kNT + tid, pc, z);
 #pragma unroll
         for (int e = 7; e >= 0; --e)
           if (z[e] == wm) idx = (uint32_t)(bq * kNT + tid) * 8u + (uint32_t)e;
@@ -825,7 +846,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // ---- the candidates z >= zc0 from the registers (min-p rows, small rows) ----------
   int nc = -1;
   if (mode == kModeCand) {
-    gather_candidates(rv, sm, sh, zc0, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
+    gather_candidates<PEN>(rv, pc, sm, sh, zc0, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
     __syncthreads();
     nc = sh.i32[3];
     // more than the list holds (min-p rows only): masked sums for min-p alone,
@@ -841,7 +862,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
 
   if (mode == kModeNoFilter) {
     path |= ARCS_PATH_SORT_SKIP;
-    if (!tsum_draw(a, row, rv, sm, sh, true, -__builtin_inff(), chi, clo, negks, u, debug, S)) return false;
+    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, true, -__builtin_inff(), chi, clo, negks, u, debug, S)) return false;
     if (!debug) return true;
     S_K = S;
     id = (int64_t)sh.u64[10];
@@ -855,6 +876,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       for (int q = 0; q < kQ; ++q) {
         float z[8];
         unpack8(dd[q], z);
+        if (PEN && pc.on && tid < ngroups - q * kNT) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
         float s = z[0] >= zt ? wexp(z[0], chi, clo, negks) : 0.0f;
 #pragma unroll
         for (int e = 1; e < 8; ++e) s += z[e] >= zt ? wexp(z[e], chi, clo, negks) : 0.0f;
@@ -862,7 +884,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       }
     }
     __syncthreads();
-    if (!tsum_draw(a, row, rv, sm, sh, false, zt, chi, clo, negks, u, debug, S_K)) return false;
+    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, false, zt, chi, clo, negks, u, debug, S_K)) return false;
     if (!debug) return true;
     id = (int64_t)sh.u64[10];
     L = -1;  // counted with the debug outputs
@@ -875,7 +897,9 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     if (mode == kModeHist) {
       // a histogram of the threads' two largest group maxima by weight, 8
       // bins per unit of log2 weight below the row maximum: counts (top-k)
-      // and weights (top-p, a lower bound of the mass above each bin's edge)
+      // and weights (top-p, a lower bound of the mass above each bin's edge).
+      // When the bound lies beyond the last bin (a large k at a low
+      // temperature), the histogram is built again with bins 16 times wider.
       float b1 = -__builtin_inff(), b2 = -__builtin_inff();
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
@@ -883,55 +907,65 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
         b2 = g > b1 ? b1 : (g > b2 ? g : b2);
         b1 = g > b1 ? g : b1;
       }
-      const float c8 = (chi + clo) * 8.0f;
+      float c8 = (chi + clo) * 8.0f;
+      for (int attempt = 0; attempt < 3; ++attempt, c8 *= 0.0625f) {
+        if (attempt > 0) {
+          if (tid < kBins) {
+            sm.bcnt[tid] = 0u;
+            sm.bmass[tid] = 0.0f;
+          }
+          __syncthreads();
+        }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float v = h == 0 ? b1 : b2;
-        if (v > -__builtin_inff()) {
-          const float x = (m - v) * c8;
-          const int bin = x < (float)(kBins - 1) ? (int)x : kBins - 1;
-          atomicAdd(&sm.bcnt[bin], 1u);
-          if (pon) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
+        for (int h = 0; h < 2; ++h) {
+          const float v = h == 0 ? b1 : b2;
+          if (v > -__builtin_inff()) {
+            const float x = (m - v) * c8;
+            const int bin = x < (float)(kBins - 1) ? (int)x : kBins - 1;
+            atomicAdd(&sm.bcnt[bin], 1u);
+            if (pon) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
+          }
         }
-      }
-      __syncthreads();
-      if (wid == 0) {
-        // the first bin (from the top) that meets a bound
-        const uint4 c4 = ((const uint4*)sm.bcnt)[lane];
-        const float4 m4 = ((const float4*)sm.bmass)[lane];
-        const uint32_t cl[4] = {c4.x, c4.y, c4.z, c4.w};
-        const double ml[4] = {(double)m4.x, (double)m4.y, (double)m4.z, (double)m4.w};
-        const uint32_t ctot = cl[0] + cl[1] + cl[2] + cl[3];
-        const double mtot = ml[0] + ml[1] + ml[2] + ml[3];
-        const uint32_t cex = dpp_wave_incl_scan_u32(ctot) - ctot;
-        const double mex = dpp_wave_incl_scan_f64(mtot) - mtot;
-        const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
-        const double p_need = pon ? Pm * (1.0 + 1e-4) : __builtin_inf();
-        int fb = 4;
-        uint32_t cc = cex;
-        double mc = mex;
+        __syncthreads();
+        if (wid == 0) {
+          // the first bin (from the top) that meets a bound
+          const uint4 c4 = ((const uint4*)sm.bcnt)[lane];
+          const float4 m4 = ((const float4*)sm.bmass)[lane];
+          const uint32_t cl[4] = {c4.x, c4.y, c4.z, c4.w};
+          const double ml[4] = {(double)m4.x, (double)m4.y, (double)m4.z, (double)m4.w};
+          const uint32_t ctot = cl[0] + cl[1] + cl[2] + cl[3];
+          const double mtot = ml[0] + ml[1] + ml[2] + ml[3];
+          const uint32_t cex = dpp_wave_incl_scan_u32(ctot) - ctot;
+          const double mex = dpp_wave_incl_scan_f64(mtot) - mtot;
+          const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
+          const double p_need = pon ? Pm * (1.0 + 1e-4) : __builtin_inf();
+          int fb = 4;
+          uint32_t cc = cex;
+          double mc = mex;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cc += cl[i];
-          mc += ml[i];
-          if (fb == 4 && (cc >= k_need || mc >= p_need)) fb = i;
+          for (int i = 0; i < 4; ++i) {
+            cc += cl[i];
+            mc += ml[i];
+            if (fb == 4 && (cc >= k_need || mc >= p_need)) fb = i;
+          }
+          const uint64_t hb = __ballot(fb < 4);
+          const int lb = hb ? __builtin_ctzll(hb) : 0;
+          const int b = hb ? __builtin_amdgcn_readlane(lane * 4 + fb, lb) : kBins - 1;
+          float zn = -__builtin_inff();  // -inf: no useful bound
+          if (b < kBins - 1) {
+            const float edge = (float)(b + 1) / c8;
+            const float theta = (m - edge) - (1e-5f * (__builtin_fabsf(m) + edge) + 1e-30f);
+            zn = theta > zc ? theta : zc;
+          }
+          if (lane == 0) { sh.r_zc = zn; sh.i32[3] = 0; }
         }
-        const uint64_t hb = __ballot(fb < 4);
-        const int lb = hb ? __builtin_ctzll(hb) : 0;
-        const int b = hb ? __builtin_amdgcn_readlane(lane * 4 + fb, lb) : kBins - 1;
-        float zn = -__builtin_inff();  // -inf: no useful bound
-        if (b < kBins - 1) {
-          const float edge = (float)(b + 1) / c8;
-          const float theta = (m - edge) - (1e-5f * (__builtin_fabsf(m) + edge) + 1e-30f);
-          zn = theta > zc ? theta : zc;
-        }
-        if (lane == 0) { sh.r_zc = zn; sh.i32[3] = 0; }
+        __syncthreads();
+        if (sh.r_zc > -__builtin_inff()) break;
       }
-      __syncthreads();
       zc = sh.r_zc;
       if (!(zc > -__builtin_inff())) return false;
       // ---- gather the candidates z >= zc -------------------------------------------
-      gather_candidates(rv, sm, sh, zc, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
+      gather_candidates<PEN>(rv, pc, sm, sh, zc, best, bq, best2, sq, bdat, sdat, chi, clo, negks);
       __syncthreads();
       nc = sh.i32[3];
     }
@@ -969,7 +1003,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     double wtot = 0.0;
     for (int j = tid; j < ngroups; j += kNT) {
       float z[8];
-      unpack8(rv[j], z);
+      load_z8<PEN>(rv[j], j, pc, z);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int64_t idx = (int64_t)j * 8 + e;
@@ -1030,7 +1064,7 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
-  const Smem sm = carve_smem(smem_raw, kUnionSummary, a.bitmap_words);
+  const Smem sm = carve_smem(smem_raw, true, a.bitmap_words);
   const int ngroups = (int)(a.V / 8);
   const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
   u32x4 d[kQ];
@@ -1042,10 +1076,10 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
   PenCtx pc;
   uint32_t path;
   if (!row_prologue<true, PEN>(a, row, sm, sh, P, pc, path)) return;
-  // Rows with active penalties take the general pipeline; the summary path
-  // handles the rest.
-  if (PEN && !pc.on) issue_row_loads(rv, ngroups, d);
-  if (pc.on || !stream_row(a, row, P, path, sm, sh, d)) {
+  // With penalty tables the loads go out once the tables are built (the
+  // build's barriers would otherwise wait for them).
+  if (PEN) issue_row_loads(rv, ngroups, d);
+  if (!stream_row<PEN>(a, row, P, pc, path, sm, sh, d)) {
     __syncthreads();
     generic_row<true, true>(a, row, P, pc, path, sm, sh);
   }

@@ -372,6 +372,26 @@ def test_sort_skip_path_and_inert_filters(arcs):
             assert ids2[b] == ids[b]
 
 
+def test_large_top_k_low_temperature_and_penalised_rows_stay_resident(arcs):
+    """top-k up to 1,000 at temperatures down to 0.3 (the bound lies many
+    units of log2 weight below the maximum), with and without penalties: the
+    rows finish on the single-pass path and match the oracle."""
+    B = 16
+    w = make_workload("zipf_b512_bf16_mixed_penalties", B=B, V=129_280, hist_len=1024)
+    p = make_params(B, temperature=0.3)
+    for b in range(B):
+        p[b]["temperature"] = [0.3, 0.32, 0.5, 1.2][b % 4]
+        p[b]["top_k"] = [600, 941, 1000, 809][(b // 4) % 4]
+        if b >= B // 2:
+            p[b]["presence"], p[b]["frequency"], p[b]["repetition"] = 0.5, 0.3, 1.1
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "large top-k")
+    assert np.all(stats["path"] & arcs.PATH_RESIDENT), stats["path"]
+    assert np.all((stats["path"][B // 2:] & 32) != 0)
+
+
 def test_minp_rows_with_crowded_threads(arcs):
     """min-p rows whose large values crowd a few 16-byte groups 8,192 tokens
     apart (one thread's share of the row on the single-pass kernel): several
