@@ -159,7 +159,12 @@ __device__ __forceinline__ double block_scan_f64(double v, Shared& sh, double& t
   return v + off;
 }
 
-// Bitonic sort (ascending) of n = 2^p (key, payload) pairs in LDS, whole block.
+// Bitonic sort (ascending) of n = 2^p (key, payload) pairs in LDS, whole
+// block.  Entry i is handled by thread i mod kNT, so the 64 entries of an
+// aligned run of 64 all belong to one wave: a stage of stride j < 64 stays
+// inside each wave and needs only a wave-level LDS fence after it, unless the
+// next stage crosses waves; strides >= 64 are followed by a block barrier.
+// The caller has synchronised the block before the call.
 __device__ __forceinline__ void block_bitonic_sort(uint64_t* keys, float* pay, int n) {
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -174,7 +179,10 @@ __device__ __forceinline__ void block_bitonic_sort(uint64_t* keys, float* pay, i
           }
         }
       }
-      __syncthreads();
+      // the next stage: stride j / 2, or the first stride of the next merge
+      const int jn = j > 1 ? j >> 1 : k;
+      if (j >= kWave || (jn >= kWave && (k << 1) <= n) || j == 1 && k == n) __syncthreads();
+      else wave_lds_sync();
     }
   }
 }
@@ -404,19 +412,26 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const PenCtx&
 #pragma unroll
     for (int q = 0; q < kQ; ++q) xmask |= (q != bq && q != sq && sm.tsum[q * kNT + tid] >= bound) ? (1u << q) : 0u;
   }
-  while (xmask) {
-    const int q = __builtin_ctz(xmask);
-    xmask &= xmask - 1u;
-    const int j = q * kNT + tid;
-    float zx[8];
-    load_z8<PEN>(rv[j], j, pc, zx);
-    for (int e = 0; e < 8; ++e) {
-      const float z = zx[e];
-      if (z >= bound) {
-        const uint32_t slot = (uint32_t)atomicAdd(&sh.i32[3], 1);
-        if (slot < (uint32_t)kCandCap) {
-          sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
-          sm.cw[slot] = wexp(z, chi, clo, negks);
+  if (!__ballot(xmask != 0)) return;
+  // all of them in flight at once, then appended
+  u32x4 xd[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q)
+    if ((xmask >> q) & 1u) xd[q] = rv[q * kNT + tid];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    if ((xmask >> q) & 1u) {
+      const int j = q * kNT + tid;
+      float zx[8];
+      load_z8<PEN>(xd[q], j, pc, zx);
+      for (int e = 0; e < 8; ++e) {
+        const float z = zx[e];
+        if (z >= bound) {
+          const uint32_t slot = (uint32_t)atomicAdd(&sh.i32[3], 1);
+          if (slot < (uint32_t)kCandCap) {
+            sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
+            sm.cw[slot] = wexp(z, chi, clo, negks);
+          }
         }
       }
     }
