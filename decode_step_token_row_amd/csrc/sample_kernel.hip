@@ -141,52 +141,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Block-wide inclusive fp64 scan with DPP inside waves; also returns the total.
-__device__ __forceinline__ double block_scan_f64(double v, Shared& sh, double& total) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  v = dpp_wave_incl_scan_f64(v);
-  __syncthreads();
-  if (lane == kWave - 1) sh.f64[wid] = v;
-  __syncthreads();
-  double off = 0.0, t = 0.0;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    const double x = sh.f64[w];
-    off += (w < wid) ? x : 0.0;
-    t += x;
-  }
-  total = t;
-  return v + off;
-}
-
-// Bitonic sort (ascending) of n = 2^p (key, payload) pairs in LDS, whole
-// block.  Entry i is handled by thread i mod kNT, so the 64 entries of an
-// aligned run of 64 all belong to one wave: a stage of stride j < 64 stays
-// inside each wave and needs only a wave-level LDS fence after it, unless the
-// next stage crosses waves; strides >= 64 are followed by a block barrier.
-// The caller has synchronised the block before the call.
-__device__ __forceinline__ void block_bitonic_sort(uint64_t* keys, float* pay, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += kNT) {
-        const int p = i ^ j;
-        if (p > i) {
-          const bool up = (i & k) == 0;
-          const uint64_t x = keys[i], y = keys[p];
-          if ((x > y) == up) {
-            keys[i] = y; keys[p] = x;
-            const float t = pay[i]; pay[i] = pay[p]; pay[p] = t;
-          }
-        }
-      }
-      // the next stage: stride j / 2, or the first stride of the next merge
-      const int jn = j > 1 ? j >> 1 : k;
-      if (j >= kWave || (jn >= kWave && (k << 1) <= n) || j == 1 && k == n) __syncthreads();
-      else wave_lds_sync();
-    }
-  }
-}
-
 // Sort key of a candidate: ascending order = value descending, id ascending.
 __device__ __forceinline__ uint64_t cand_key(float z, int64_t idx) {
   return ((uint64_t)(~ord_key(z)) << 32) | (uint64_t)(uint32_t)idx;
@@ -251,20 +205,31 @@ enum RowMode : int32_t {
   kModeHist = 5       // candidates above a bound from a histogram of thread maxima
 };
 
+// Which entries a draw keeps: order key above th, or equal to it with an id
+// at most istar.
+struct KeepCut {
+  uint32_t th;
+  int64_t istar;
+};
+__device__ __forceinline__ bool keep_cut(float z, int64_t idx, const KeepCut& c) {
+  const uint32_t k = ord_key(z);
+  return k > c.th || (k == c.th && idx <= c.istar);
+}
+
 // Inverse-CDF draw in id order over sm.tsum (group j's weight at j).  With
 // `thread_frames`, group j's value is in the frame 2^-K_t of the thread t
 // that owns it (kref[t] = -K_t); otherwise in the row frame K*.
 // Wave w takes the groups w*kNT .. w*kNT + kNT - 1, its lane l the 16
 // consecutive groups from w*kNT + 16l (all owned by wave l/4): the round
 // totals locate the wave, a wave scan the lane, the lane's 16 sums the group,
-// and one re-read of that group the element (elements below zmask weigh 0).
+// and one re-read of that group the element (entries `cut` drops weigh 0).
 // The drawing lane writes the output row.  Returns false (uniformly) when
 // the total weight is zero or not finite; else S (the total).  With `sync`
 // the id is left in sh.u64[10] for the whole block; otherwise waves other
 // than the drawing one return at once.
 template <bool PEN>
 __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, const u32x4* rv, const PenCtx& pc,
-                                          const Smem& sm, Shared& sh, bool thread_frames, float zmask, float chi,
+                                          const Smem& sm, Shared& sh, bool thread_frames, KeepCut cut, float chi,
                                           float clo, float negks, double u, bool sync, double& S) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   // lane l: groups wid*kNT + 16l + i, owned by threads 16l + i
@@ -334,7 +299,7 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
       int pe = -1, last_e = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float w = z[e] >= zmask ? wexp(z[e], chi, clo, nk) : 0.0f;
+        const float w = keep_cut(z[e], (int64_t)j * 8 + e, cut) ? wexp(z[e], chi, clo, nk) : 0.0f;
         acc = (e == 0) ? w : acc + w;
         const bool pos = acc > prev;
         if (pos) last_e = e;
@@ -413,27 +378,38 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const PenCtx&
     for (int q = 0; q < kQ; ++q) xmask |= (q != bq && q != sq && sm.tsum[q * kNT + tid] >= bound) ? (1u << q) : 0u;
   }
   if (!__ballot(xmask != 0)) return;
-  // all of them in flight at once, then appended
+  // all of them in flight at once; each round's entries placed with one LDS
+  // atomic per wave
   u32x4 xd[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q)
     if ((xmask >> q) & 1u) xd[q] = rv[q * kNT + tid];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    if ((xmask >> q) & 1u) {
-      const int j = q * kNT + tid;
-      float zx[8];
+    const bool mine = (xmask >> q) & 1u;
+    if (!__ballot(mine)) continue;
+    const int j = q * kNT + tid;
+    float zx[8];
+    uint32_t m8 = 0;
+    if (mine) {
       load_z8<PEN>(xd[q], j, pc, zx);
-      for (int e = 0; e < 8; ++e) {
-        const float z = zx[e];
-        if (z >= bound) {
-          const uint32_t slot = (uint32_t)atomicAdd(&sh.i32[3], 1);
-          if (slot < (uint32_t)kCandCap) {
-            sm.ckey[slot] = cand_key(z, (int64_t)j * 8 + e);
-            sm.cw[slot] = wexp(z, chi, clo, negks);
-          }
-        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m8 |= zx[e] >= bound ? (1u << e) : 0u;
+    }
+    const uint32_t nq = (uint32_t)__builtin_popcount(m8);
+    const uint32_t qincl = dpp_wave_incl_scan_u32(nq);
+    uint32_t qbase = 0;
+    if (lane == kWave - 1) qbase = (uint32_t)atomicAdd(&sh.i32[3], (int)qincl);
+    qbase = (uint32_t)__builtin_amdgcn_readlane((int)qbase, kWave - 1);
+    uint32_t slot = qbase + qincl - nq;
+    while (m8) {
+      const int e = __builtin_ctz(m8);
+      m8 &= m8 - 1u;
+      if (slot < (uint32_t)kCandCap) {
+        sm.ckey[slot] = cand_key(zx[e], (int64_t)j * 8 + e);
+        sm.cw[slot] = wexp(zx[e], chi, clo, negks);
       }
+      ++slot;
     }
   }
 }
@@ -512,114 +488,339 @@ __device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row,
   return true;
 }
 
-// Cut and draw over nc > kSmallSort candidates in ckey / cw (room for the next
-// power of two, at least 128; keys in
-// (value desc, id asc) order, weights in the row frame): a block bitonic sort,
-// block scans for the top-p crossing and the min-p count, a second sort of the
-// kept prefix by id, and the id-order draw.  All threads take part.  On
-// success the output row is written and sh.u64[10..12] / sh.f64[kNW+1] hold
-// id, L, the cut key and S_K; on failure (no prefix length known from the
-// candidates) sh.i32[6] = -1.
-__device__ __forceinline__ void large_cut_draw(const SampleArgs& a, int64_t row, uint64_t* ckey, float* cw, Shared& sh,
-                                               int nc, bool kon, int top_k, bool pon, double Pm, bool minp_complete,
-                                               float zt, double u) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  constexpr int64_t INF = INT64_MAX;
-  int n2 = 128;
-  while (n2 < nc) n2 <<= 1;
-  for (int i = nc + tid; i < n2; i += kNT) { ckey[i] = ~0ull; cw[i] = 0.0f; }
-  if (tid == 0) { sh.u64[13] = (uint64_t)INF; sh.u64[14] = (uint64_t)INF; sh.u64[15] = 0ull; }
-  __syncthreads();
-  block_bitonic_sort(ckey, cw, n2);
-  // prefix mass over the sorted order (ENT consecutive entries per thread)
+// Cut over nc > kSmallSort candidates (keys and row-frame weights in LDS, in
+// no particular order) without sorting them.  A radix descent over the value
+// order keys, 8 bits a level from the highest bit in which the candidates'
+// keys differ down to bit `lowbit` (16 when every value is a widened bf16,
+// whose low 16 key bits follow from its sign; 0 otherwise), with per-digit
+// counts and 2^-50 fixed-point masses, finds the value theta of the L-th
+// entry in (value desc, id asc) order, L = min(L_k, L_p, L_m), and the count
+// and mass above it.  How many ties at theta are kept follows in closed
+// form (they weigh the same); when not all are, a descent over their ids
+// (9 + 8 bits; ids < 2^17) finds the last kept one.  The bins live at
+// sm.hcnt / sm.hmass (inside the group area, free at this point).  Returns
+// false (uniformly) when the candidates reach no target.
+constexpr double kFixScale = 1125899906842624.0;  // 2^50: weights < 2, at most 4096 of them
+__device__ __forceinline__ uint64_t to_fix50(float w) { return (uint64_t)((double)w * kFixScale); }
+
+__device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int nc, int lowbit, bool kon, int top_k,
+                                                 bool pon, double Pm, bool minp_complete, float zt, KeepCut& cut,
+                                                 int64_t& L) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   constexpr int ENT = kCandCap / kNT;
-  double loc[ENT];
-  double lsum_c = 0.0;
-  uint32_t nm = 0;
+  uint32_t* hc = sm.hcnt;
+  uint64_t* hm = sm.hmass;
+  constexpr uint64_t NONE = ~0ull;
+  for (int i = tid; i < 512; i += kNT) { hc[i] = 0u; hm[i] = 0ull; }
+  if (tid == 0) { sh.u64[13] = 0ull; sh.u64[14] = 0ull; sh.i32[1] = INT_MIN; sh.i32[2] = INT_MAX; }
+  __syncthreads();
+  // the span of the value keys: min and max (as int atomics on flipped keys)
+  {
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < ENT; ++j) {
-    const int i = tid * ENT + j;
-    lsum_c += (i < nc) ? (double)cw[i] : 0.0;
-    loc[j] = lsum_c;
-    if (minp_complete && i < nc && key_value(~(uint32_t)(ckey[i] >> 32)) >= zt) ++nm;
+    for (int r = 0; r < ENT; ++r) {
+      const int i = tid + r * kNT;
+      if (i < nc) {
+        const uint32_t vk = ~(uint32_t)(sm.ckey[i] >> 32);
+        kmin = vk < kmin ? vk : kmin;
+        kmax = vk > kmax ? vk : kmax;
+      }
+    }
+    kmin = dpp_wave_min_u32(kmin);
+    kmax = ~dpp_wave_min_u32(~kmax);
+    if (lane == 0) {
+      atomicMax(&sh.i32[1], (int)(kmax ^ 0x80000000u));
+      atomicMin(&sh.i32[2], (int)(kmin ^ 0x80000000u));
+    }
   }
+  // the min-p count, with the first level
   if (minp_complete) {
-    const uint32_t wn = dpp_wave_sum_u32(nm);
-    if (lane == 0 && wn) atomicAdd((unsigned long long*)&sh.u64[15], (unsigned long long)wn);
-  }
-  double tot;
-  const double incl = block_scan_f64(lsum_c, sh, tot);
-  const double excl = incl - lsum_c;
-  if (pon) {
+    uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < ENT; ++j) {
-      const int i = tid * ENT + j;
-      if (i < nc && excl + loc[j] >= Pm) {
-        atomicMin((unsigned long long*)&sh.u64[13], (unsigned long long)(i + 1));
-        break;
+    for (int r = 0; r < ENT; ++r) {
+      const int i = tid + r * kNT;
+      if (i < nc && key_value(~(uint32_t)(sm.ckey[i] >> 32)) >= zt) ++c;
+    }
+    const uint32_t wc = dpp_wave_sum_u32(c);
+    if (lane == 0 && wc) atomicAdd((unsigned long long*)&sh.u64[13], (unsigned long long)wc);
+  }
+  uint64_t Pfix = NONE;
+  if (pon) {
+    const double x = Pm * kFixScale;
+    Pfix = x < 9.0e18 ? (uint64_t)__builtin_ceil(x) : NONE;
+  }
+  uint64_t cnt_above = 0, mass_above = 0, c_eq = nc, m_eq = 0;
+  __syncthreads();
+  const uint32_t vmax = (uint32_t)sh.i32[1] ^ 0x80000000u, vmin = (uint32_t)sh.i32[2] ^ 0x80000000u;
+  const uint32_t span = vmin ^ vmax;
+  const int hb = span ? 31 - __builtin_clz(span) : -1;  // the highest differing bit
+  uint32_t pref = hb >= 0 ? (hb == 31 ? 0u : vmin & ~((2u << hb) - 1u)) : vmin;  // the common bits
+  for (int top = hb; top >= lowbit; top -= 8) {
+    const int shf = top - 7 > lowbit ? top - 7 : lowbit;
+    const uint32_t dmask = (1u << (top - shf + 1)) - 1u;
+#pragma unroll
+    for (int r = 0; r < ENT; ++r) {
+      const int i = tid + r * kNT;
+      if (i < nc) {
+        const uint32_t vk = ~(uint32_t)(sm.ckey[i] >> 32);
+        if (top == 31 || (vk >> (top + 1)) == (pref >> (top + 1))) {
+          const uint32_t d = (vk >> shf) & dmask;
+          atomicAdd(&hc[d], 1u);
+          if (pon) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)to_fix50(sm.cw[i]));
+        }
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      uint64_t Lc = (kon && top_k <= nc) ? (uint64_t)top_k : NONE;
+      if (minp_complete) Lc = sh.u64[13] < Lc ? sh.u64[13] : Lc;
+      const uint64_t need_c = Lc == NONE ? NONE : Lc - cnt_above;
+      const uint64_t need_m = Pfix == NONE ? NONE : Pfix - mass_above;
+      // lane l: digits 255 - 4l .. 252 - 4l, from the top
+      uint32_t c[4];
+      uint64_t m[4];
+      uint64_t ctot = 0, mtot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 255 - 4 * lane - j;
+        c[j] = hc[d]; m[j] = hm[d];
+        hc[d] = 0u; hm[d] = 0ull;
+        ctot += c[j]; mtot += m[j];
+      }
+      uint64_t cc = wave_incl_scan_u64(ctot, lane) - ctot;
+      uint64_t mc = wave_incl_scan_u64(mtot, lane) - mtot;
+      int fj = 4;
+      uint64_t cb = 0, mb = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (fj == 4 && (cc + c[j] >= need_c || mc + m[j] >= need_m)) { fj = j; cb = cc; mb = mc; }
+        cc += c[j]; mc += m[j];
+      }
+      const uint64_t hit = __ballot(fj < 4);
+      if (hit == 0) {
+        if (lane == 0) sh.i32[0] = -1;
+      } else if (lane == __builtin_ctzll(hit)) {
+        sh.i32[0] = 255 - 4 * lane - fj;
+        sh.u64[3] = cb; sh.u64[4] = mb; sh.u64[5] = c[fj]; sh.u64[6] = m[fj];
+      }
+    }
+    __syncthreads();
+    const int dstar = sh.i32[0];
+    if (dstar < 0) return false;  // only at the first level: the candidates reach no target
+    cnt_above += sh.u64[3];
+    mass_above += sh.u64[4];
+    c_eq = sh.u64[5];
+    m_eq = sh.u64[6];
+    pref |= (uint32_t)dstar << shf;
+    __syncthreads();
+  }
+  if (hb < lowbit) {
+    // every candidate holds the same value: all of them are ties at it
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < ENT; ++r) {
+      const int i = tid + r * kNT;
+      if (i < nc) m += to_fix50(sm.cw[i]);
+    }
+    m = wave_sum_u64(m);
+    if (lane == 0) atomicAdd((unsigned long long*)&sh.u64[14], (unsigned long long)m);
+    __syncthreads();
+    m_eq = sh.u64[14];
+    uint64_t Lc0 = (kon && top_k <= nc) ? (uint64_t)top_k : NONE;
+    if (minp_complete) Lc0 = sh.u64[13] < Lc0 ? sh.u64[13] : Lc0;
+    if (Lc0 == NONE && (Pfix == NONE || m_eq < Pfix)) return false;
+  }
+  const uint32_t th = lowbit == 16 ? ((pref & 0xFFFF0000u) | ((pref & 0x80000000u) ? 0u : 0xFFFFu)) : pref;
+  // ties at theta kept: r of c_eq
+  uint64_t Lc = (kon && top_k <= nc) ? (uint64_t)top_k : NONE;
+  if (minp_complete) Lc = sh.u64[13] < Lc ? sh.u64[13] : Lc;
+  uint64_t r = c_eq;
+  if (Lc != NONE && Lc - cnt_above < r) r = Lc - cnt_above;
+  if (Pfix != NONE) {
+    const uint64_t w_eq = c_eq ? m_eq / c_eq : 0;
+    if (w_eq > 0) {
+      const uint64_t need = Pfix > mass_above ? Pfix - mass_above : 0;
+      uint64_t rp = (need + w_eq - 1) / w_eq;
+      rp = rp < 1 ? 1 : rp;
+      r = rp < r ? rp : r;
+    }
+  }
+  L = (int64_t)(cnt_above + r);
+  cut.th = th;
+  cut.istar = INT64_MAX;
+  if (r < c_eq && c_eq <= (uint64_t)kSmallSort) {
+    // few ties: their ids listed in LDS, ranked by one wave
+    if (tid == 0) sh.i32[4] = 0;
+    __syncthreads();
+    uint32_t* ids = (uint32_t*)sm.skey;
+#pragma unroll
+    for (int q = 0; q < ENT; ++q) {
+      const int i = tid + q * kNT;
+      if (i < nc) {
+        const uint64_t k = sm.ckey[i];
+        if (~(uint32_t)(k >> 32) == th) {
+          const int slot = atomicAdd(&sh.i32[4], 1);
+          if (slot < kSmallSort) ids[slot] = (uint32_t)k;
+        }
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      const int n = (int)c_eq;
+      const uint32_t my = lane < n ? ids[lane] : 0xFFFFFFFFu;
+      uint32_t rank = 0;
+      for (int j = 0; j < n; ++j) rank += (uint32_t)__builtin_amdgcn_readlane((int)my, j) < my ? 1u : 0u;
+      if (lane < n && rank == (uint32_t)(r - 1)) sh.u64[3] = my;
+    }
+    __syncthreads();
+    cut.istar = (int64_t)sh.u64[3];
+  } else if (r < c_eq) {
+    // the r-th smallest id among the ties: ids >> 8 (512 bins), then the low 8 bits
+    int64_t hi_d = 0;
+    uint64_t before = 0;
+    for (int lev = 0; lev < 2; ++lev) {
+#pragma unroll
+      for (int q = 0; q < ENT; ++q) {
+        const int i = tid + q * kNT;
+        if (i < nc) {
+          const uint64_t k = sm.ckey[i];
+          const uint32_t id = (uint32_t)k;
+          if (~(uint32_t)(k >> 32) == th && (lev == 0 || (int64_t)(id >> 8) == hi_d))
+            atomicAdd(&hc[lev == 0 ? (id >> 8) : (id & 255u)], 1u);
+        }
+      }
+      __syncthreads();
+      if (wid == 0) {
+        const int nb = lev == 0 ? 512 : 256, per = nb / kWave;
+        uint32_t tot = 0;
+        for (int j = 0; j < per; ++j) tot += hc[lane * per + j];
+        uint64_t cc = wave_incl_scan_u64(tot, lane) - tot;
+        const uint64_t need = r - before;
+        int dd = -1;
+        uint64_t cb = 0;
+        for (int j = 0; j < per; ++j) {
+          const uint32_t x = hc[lane * per + j];
+          if (dd < 0 && cc + x >= need) { dd = lane * per + j; cb = cc; }
+          cc += x;
+        }
+        for (int j = 0; j < per; ++j) hc[lane * per + j] = 0u;
+        const uint64_t hit = __ballot(dd >= 0);
+        if (hit != 0 && lane == __builtin_ctzll(hit)) { sh.i32[0] = dd; sh.u64[3] = cb; }
+      }
+      __syncthreads();
+      if (lev == 0) { hi_d = sh.i32[0]; before += sh.u64[3]; }
+      else cut.istar = (hi_d << 8) | (int64_t)sh.i32[0];
+      __syncthreads();
+    }
+  }
+  return true;
+}
+
+// Inverse-CDF draw in id order over the kept candidates (those `cut` keeps),
+// from the candidate list alone: weights in 2^-50 fixed point, summed per
+// bucket of 256 ids with LDS atomics (exact, so independent of their order),
+// one wave scan locates the bucket of t = floor(u * S_K), a second the group
+// of 8 ids inside it, and thread 0 walks that group's kept candidates in id
+// order.  Writes the output row, sh.u64[10] (id) and sh.f64[kNW + 1] (S_K in
+// the row frame).  Returns false (uniformly) when the kept mass is zero.
+__device__ __forceinline__ bool cand_draw(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh, int nc,
+                                          const KeepCut& cut, uint64_t uf) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  constexpr int ENT = kCandCap / kNT;
+  uint64_t* hm = sm.hmass;
+  for (int i = tid; i < 512; i += kNT) hm[i] = 0ull;
+  if (tid == 0) sh.i32[4] = 0;
+  __syncthreads();
+  uint32_t myid[ENT];
+  uint64_t myw[ENT];
+#pragma unroll
+  for (int q = 0; q < ENT; ++q) {
+    const int i = tid + q * kNT;
+    myw[q] = 0ull;
+    myid[q] = 0xFFFFFFFFu;
+    if (i < nc) {
+      const uint64_t k = sm.ckey[i];
+      const uint32_t id = (uint32_t)k;
+      if (keep_cut(key_value(~(uint32_t)(k >> 32)), (int64_t)id, cut)) {
+        myid[q] = id;
+        myw[q] = to_fix50(sm.cw[i]);
+        if (myw[q]) atomicAdd((unsigned long long*)&hm[id >> 8], (unsigned long long)myw[q]);
       }
     }
   }
   __syncthreads();
-  const int64_t Lk = (kon && (int64_t)top_k <= nc) ? (int64_t)top_k : INF;
-  const int64_t Lp = (int64_t)sh.u64[13];
-  const int64_t Lm = minp_complete ? (int64_t)sh.u64[15] : INF;
-  int64_t Lw = Lk < Lp ? Lk : Lp;
-  Lw = Lw < Lm ? Lw : Lm;
-  if (Lw == INF || Lw < 1) {
-    if (tid == 0) sh.i32[6] = -1;
-    __syncthreads();
-  } else {
+  // the bucket: lane l sums buckets 8l .. 8l + 7
+  if (wid == 0) {
+    uint64_t b[8], tot = 0;
 #pragma unroll
-    for (int j = 0; j < ENT; ++j) {
-      const int i = tid * ENT + j;
-      if (i == Lw - 1) { sh.f64[kNW + 1] = excl + loc[j]; sh.u64[12] = ckey[i]; }
-    }
-    __syncthreads();
-    const double sk = sh.f64[kNW + 1];
-    const double t = u * sk;
-    // keep the first Lw entries, re-sorted by id
-    int m2 = 2;
-    while (m2 < Lw) m2 <<= 1;
-    for (int i = tid; i < n2; i += kNT) {
-      if (i < Lw) ckey[i] &= 0xFFFFFFFFull;
-      else { ckey[i] = ~0ull; cw[i] = 0.0f; }
-    }
-    __syncthreads();
-    block_bitonic_sort(ckey, cw, m2);
-    double ls2 = 0.0;
+    for (int j = 0; j < 8; ++j) { b[j] = hm[8 * lane + j]; tot += b[j]; }
+    const uint64_t incl = wave_incl_scan_u64(tot, lane);
+    const uint64_t SK = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, kWave - 1) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), kWave - 1) << 32);
+    const uint64_t t = __umul64hi(uf, SK);  // floor(u * S_K) < S_K
+    uint64_t c = incl - tot;
+    int bj = -1;
+    uint64_t before = 0;
 #pragma unroll
-    for (int j = 0; j < ENT; ++j) {
-      const int i = tid * ENT + j;
-      ls2 += (i < Lw) ? (double)cw[i] : 0.0;
-      loc[j] = ls2;
+    for (int j = 0; j < 8; ++j) {
+      if (bj < 0 && c + b[j] > t) { bj = j; before = c; }
+      c += b[j];
     }
-    double tot2;
-    const double incl2 = block_scan_f64(ls2, sh, tot2);
-    const double excl2 = incl2 - ls2;
-#pragma unroll
-    for (int j = 0; j < ENT; ++j) {
-      const int i = tid * ENT + j;
-      if (i < Lw && cw[i] > 0.0f && excl2 + loc[j] > t) {
-        atomicMin((unsigned long long*)&sh.u64[14], (unsigned long long)i);
-        break;
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t pos = (int64_t)sh.u64[14];
-      if (pos == INF) {  // rounding left t at the very end: the last kept id with weight
-        pos = Lw - 1;
-        while (pos > 0 && !(cw[pos] > 0.0f)) --pos;
-      }
-      const uint32_t pid = (uint32_t)(ckey[pos] & 0xFFFFFFFFull);
-      sh.u64[10] = pid;
-      sh.u64[11] = (uint64_t)Lw;
-      a.out_ids[row] = (int32_t)pid;
-      if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
-    }
-    __syncthreads();
+    const uint64_t hit = __ballot(bj >= 0);
+    if (lane == 0) { sh.u64[7] = SK; sh.u64[8] = t; sh.i32[5] = -1; }
+    if (hit != 0 && lane == __builtin_ctzll(hit)) { sh.i32[5] = 8 * lane + bj; sh.u64[9] = before; }
+    // the groups of the next step use hm[0 .. 31]
+    if (lane < 32) hm[lane] = 0ull;
   }
+  __syncthreads();
+  const int bstar = sh.i32[5];
+  if (bstar < 0) return false;  // no kept mass
+  const uint64_t t = sh.u64[8];
+#pragma unroll
+  for (int q = 0; q < ENT; ++q)
+    if (myw[q] && (int)(myid[q] >> 8) == bstar) atomicAdd((unsigned long long*)&hm[(myid[q] >> 3) & 31u], (unsigned long long)myw[q]);
+  __syncthreads();
+  if (wid == 0) {
+    const uint64_t g = lane < 32 ? hm[lane] : 0ull;
+    const uint64_t incl = wave_incl_scan_u64(g, lane) + sh.u64[9];
+    const uint64_t hit = __ballot(lane < 32 && incl > t);
+    if (lane == 0) sh.i32[7] = hit ? __builtin_ctzll(hit) : 31;
+    if (hit != 0 && lane == __builtin_ctzll(hit)) sh.u64[9] = incl - g;
+  }
+  __syncthreads();
+  const uint32_t gstar = ((uint32_t)bstar << 5) | (uint32_t)sh.i32[7];
+  uint64_t* lst = sm.skey;  // ids in 0..7, weights in 8..15
+#pragma unroll
+  for (int q = 0; q < ENT; ++q) {
+    if (myw[q] && (myid[q] >> 3) == gstar) {
+      const int slot = atomicAdd(&sh.i32[4], 1);
+      if (slot < 8) { lst[slot] = myid[q]; lst[8 + slot] = myw[q]; }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int n = sh.i32[4] < 8 ? sh.i32[4] : 8;
+    uint64_t acc = sh.u64[9];
+    uint32_t pid = 0xFFFFFFFFu, last = 0xFFFFFFFFu;
+    // the group's kept entries in id order (at most 8)
+    for (int r = 0; r < n; ++r) {
+      uint32_t best = 0xFFFFFFFFu;
+      int bi = -1;
+      for (int i = 0; i < n; ++i) {
+        const uint32_t id = (uint32_t)lst[i];
+        if (id < best && (r == 0 || id > last)) { best = id; bi = i; }
+      }
+      last = best;
+      acc += lst[8 + bi];
+      if (pid == 0xFFFFFFFFu && acc > t) pid = best;
+    }
+    if (pid == 0xFFFFFFFFu) pid = last;  // not reached with exact sums
+    a.out_ids[row] = (int32_t)pid;
+    if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+    sh.u64[10] = pid;
+    sh.f64[kNW + 1] = (double)sh.u64[7] / kFixScale;
+  }
+  return true;
 }
 
 // One row on the summary path.  d holds the loads of the row's groups,
@@ -877,7 +1078,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
 
   if (mode == kModeNoFilter) {
     path |= ARCS_PATH_SORT_SKIP;
-    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, true, -__builtin_inff(), chi, clo, negks, u, debug, S)) return false;
+    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, true, KeepCut{0u, INT64_MAX}, chi, clo, negks, u, debug, S))
+      return false;
     if (!debug) return true;
     S_K = S;
     id = (int64_t)sh.u64[10];
@@ -892,14 +1094,18 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
         float z[8];
         unpack8(dd[q], z);
         if (PEN && pc.on && tid < ngroups - q * kNT) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
-        float s = z[0] >= zt ? wexp(z[0], chi, clo, negks) : 0.0f;
+        const KeepCut cut{ord_key(zt), INT64_MAX};
+        const int64_t i0 = (int64_t)(q * kNT + tid) * 8;
+        float s = keep_cut(z[0], i0, cut) ? wexp(z[0], chi, clo, negks) : 0.0f;
 #pragma unroll
-        for (int e = 1; e < 8; ++e) s += z[e] >= zt ? wexp(z[e], chi, clo, negks) : 0.0f;
+        for (int e = 1; e < 8; ++e) s += keep_cut(z[e], i0 + e, cut) ? wexp(z[e], chi, clo, negks) : 0.0f;
         sm.tsum[q * kNT + tid] = tid < ngroups - q * kNT ? s : 0.0f;
       }
     }
     __syncthreads();
-    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, false, zt, chi, clo, negks, u, debug, S_K)) return false;
+    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, false, KeepCut{ord_key(zt), INT64_MAX}, chi, clo, negks, u, debug,
+                        S_K))
+      return false;
     if (!debug) return true;
     id = (int64_t)sh.u64[10];
     L = -1;  // counted with the debug outputs
@@ -995,17 +1201,29 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           sh.i32[6] = -1;
       }
       __syncthreads();
+      if (sh.i32[6] < 0) return false;
+      if (!debug) return true;
+      id = (int64_t)sh.u64[10];
+      L = (int64_t)sh.u64[11];
+      S_K = sh.f64[kNW + 1];
+      const uint64_t ck = sh.u64[12];
+      cut_key = ~(uint32_t)(ck >> 32);
+      cut_idx = (int64_t)(ck & 0xFFFFFFFFull);
     } else {
-      large_cut_draw(a, row, sm.ckey, sm.cw, sh, nc, kon, P.top_k, pon, Pm, minp_complete, zt, u);
+      // a larger set: select the cut, then draw in id order over masked group sums
+      KeepCut cut;
+      const int lowbit = (PEN && pc.on) ? 0 : 16;
+      if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, pon, Pm, minp_complete, zt, cut, L)) return false;
+      const double ux = u * 0x1p64;  // the uniform as a 64-bit fraction
+      const uint64_t uf = ux >= 0x1p64 ? ~0ull : (ux <= 0.0 ? 0ull : (uint64_t)ux);
+      if (!cand_draw(a, row, sm, sh, nc, cut, uf)) return false;
+      if (!debug) return true;
+      __syncthreads();
+      id = (int64_t)sh.u64[10];
+      S_K = sh.f64[kNW + 1];
+      cut_key = cut.th;
+      cut_idx = cut.istar;
     }
-    if (sh.i32[6] < 0) return false;
-    if (!debug) return true;
-    id = (int64_t)sh.u64[10];
-    L = (int64_t)sh.u64[11];
-    S_K = sh.f64[kNW + 1];
-    const uint64_t ck = sh.u64[12];
-    cut_key = ~(uint32_t)(ck >> 32);
-    cut_idx = (int64_t)(ck & 0xFFFFFFFFull);
   }
 
   // ---- debug outputs (the row is read again) ---------------------------------------
