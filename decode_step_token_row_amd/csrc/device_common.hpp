@@ -66,22 +66,12 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   for (int o = 32; o > 0; o >>= 1) { int t = __shfl_xor(v, o, kWave); v = v > t ? v : t; }
   return v;
 }
-__device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { int t = __shfl_xor(v, o, kWave); v = v < t ? v : t; }
-  return v;
-}
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) { float t = __shfl_xor(v, o, kWave); v = v > t ? v : t; }
   return v;
 }
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
@@ -171,15 +161,6 @@ __device__ __forceinline__ double dpp_wave_sum_f64(double v) {
   v += dpp_f64<0x142, 0xA>(0.0, v);
   v += dpp_f64<0x143, 0xC>(0.0, v);
   return readlane63_f64(v);
-}
-__device__ __forceinline__ float dpp_wave_sum_f32(float v) {
-  v += dpp_f32<0xB1>(0.0f, v);
-  v += dpp_f32<0x4E>(0.0f, v);
-  v += dpp_f32<0x141>(0.0f, v);
-  v += dpp_f32<0x140>(0.0f, v);
-  v += dpp_f32<0x142, 0xA>(0.0f, v);
-  v += dpp_f32<0x143, 0xC>(0.0f, v);
-  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 __device__ __forceinline__ float dpp_wave_max_f32(float v) {
   const float ni = -__builtin_inff();

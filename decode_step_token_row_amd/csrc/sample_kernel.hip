@@ -13,27 +13,28 @@
 //
 // Two kernels:
 //
-// sample_summary_kernel (bf16 rows, 16-byte aligned, V <= 131072, V % 8 == 0,
-//   no active penalties): the row is read from HBM exactly once, 8 x 16-byte
-//   loads per lane in flight.  Each thread turns every group of 8 logits into
-//   weights e = exp2(z*log2(e)/T - K_t) (K_t an integer reference from the
-//   thread's first group, so rescaling between threads is an exact power of
-//   two) and leaves a per-group summary in LDS: the group weight sum (fp32,
-//   summed in id order) for no-filter rows, the group maximum (bf16) for
-//   filter rows, plus an fp64 per-thread weight total.  After the pass:
-//     greedy rows   -> block max, lowest index (one group re-read);
-//     no filter     -> the draw scans per-thread chunk totals, then the
-//                      chunk's group sums, then one group's 8 weights;
-//     any filter    -> a lower bound on the cutoff from the group maxima
-//                      (min-p's closed-form threshold, a group-count bound
-//                      for top-k, a group-mass bound for top-p), the groups
-//                      above it re-read and their candidates gathered into
-//                      LDS, sorted by (value desc, id asc), the kept prefix
-//                      cut, re-sorted by id, and the inverse-CDF draw done
-//                      on it.
-//   Rows the fast path cannot take exactly (NaN or +inf logits, extreme
-//   values, more than kCandCap candidates, penalties) run the general
-//   pipeline instead.
+// sample_summary_kernel (bf16 rows, 16-byte aligned, V <= 131072, V % 8 == 0):
+//   the row is read from HBM exactly once, all 16 loads of 16 bytes per lane
+//   issued before any is used.  Each thread turns every group of 8 logits
+//   (penalised through LDS tables when the row has active penalties) into
+//   its maximum and, for rows without filters or with top-p, its weight
+//   exp2(z*log2(e)/T - K_t) (K_t an integer reference exponent of the thread,
+//   so moving sums between frames is an exact power of two), and leaves one
+//   float per group in LDS: the weight sum for rows without filters, the
+//   maximum for the others.  After the pass, per-wave records and one wave
+//   give the row's maximum, mass and min-p threshold, and then:
+//     greedy rows   -> the lowest index of the maximum, from registers;
+//     no filter     -> an id-order draw over the group sums;
+//     any filter    -> a bound below which nothing is kept (the min-p
+//                      threshold, or a histogram of the threads' largest
+//                      group maxima for top-k / top-p), the elements above it
+//                      gathered into LDS as candidates (mostly from
+//                      registers), the cut L = min(L_k, L_p, L_m) found by one
+//                      wave for small sets or by a radix select for large
+//                      ones, and the inverse-CDF draw in id order.
+//   Rows the fast path cannot take exactly (signalling NaN, +inf, extreme
+//   values or temperatures, more than kCandCap candidates) run the general
+//   pipeline in the same workgroup.
 //
 // sample_kernel (everything else): the general streaming pipeline of
 //   sample_common.hpp -- pass A for max/argmax, fixed-point softmax mass,
@@ -85,11 +86,6 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
   z[6] = bf16_lo(d.w); z[7] = bf16_hi(d.w);
 }
 
-// Element e (0..7) of a group as float32.
-__device__ __forceinline__ float bf16_at(u32x4 d, int e) {
-  const uint32_t w = e < 2 ? d.x : e < 4 ? d.y : e < 6 ? d.z : d.w;
-  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-}
 
 // The values z' of group j (elements 8j .. 8j + 7) from its 16 bytes: the
 // bf16 widened, then, on rows with active penalties, the history ids among
@@ -169,13 +165,6 @@ __device__ __forceinline__ void issue_row_loads(const u32x4* rv, int ngroups, u3
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// A lower bound of the min-p threshold m + T ln(min_p) in float arithmetic
-// (tlf = T ln(min_p) as a float), low by a relative margin that covers the
-// rounding of this computation.
-__device__ __forceinline__ float minp_bound(float m, float tlf) {
-  const float x = m + tlf;
-  return x - (1e-5f * (__builtin_fabsf(m) + __builtin_fabsf(tlf)) + 1e-30f);
-}
 
 // The min-p threshold: the smallest float z with (z - m) >= T ln(min_p) in
 // double arithmetic (tdl = T ln(min_p)).  The 64 lanes of the wave test 64
@@ -828,20 +817,22 @@ __device__ __forceinline__ bool cand_draw(const SampleArgs& a, int64_t row, cons
 // row must be redone by the general pipeline.
 //
 // The pass keeps per owned group one float: its weight sum for no-filter
-// rows, its maximum otherwise, and keeps the group data in registers for the
-// candidate gathering.  Weights are computed in a per-thread frame 2^-K_t
-// (K_t an integer from the thread's first finite group, raised when a later
-// group lies far above it), moved after the pass to the frame of the wave
-// and then of the row, K* = floor(max * log2(e) / T), by exact powers of
-// two.  One barrier collects per-wave records; wave 0 turns them into the
-// row's maximum, argmax, total weight and bounds and picks what follows:
+// rows, its maximum otherwise, and notes each thread's two largest groups,
+// whose 16 bytes stay in registers for the candidate gathering.  Weights are
+// computed in a per-thread frame 2^-K_t (K_t an integer from the thread's
+// first finite group, raised when a later group lies far above it), moved
+// after the pass to the frame of the wave and then of the row,
+// K* = floor(max * log2(e) / T), by exact powers of two.  One barrier
+// collects per-wave records; wave 0 turns them into the row's maximum,
+// argmax, total weight and min-p threshold and picks what follows (a second
+// barrier):
 //   no filter    -> the group sums go through LDS to the id-order draw;
-//   min-p bound small, or a top-k / top-p bound from a histogram of the
+//   min-p rows, small rows, or a top-k / top-p bound from a histogram of the
 //                   threads' largest group maxima -> the elements above the
-//                   bound are gathered into LDS from the registers, cut by
-//                   one wave (or the block for large sets) and drawn from in
-//                   id order;
-//   min-p alone over many groups -> masked group sums and the id-order draw.
+//                   bound are gathered into LDS, cut by one wave (at most 64
+//                   of them) or by a radix select, and drawn from in id order;
+//   min-p alone over more than the list holds -> masked group sums and the
+//                   id-order draw.
 template <bool PEN>
 __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
                                            const PenCtx& pc, uint32_t path, const Smem& sm, Shared& sh,
@@ -861,7 +852,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   const bool weights = nofilter || pon;  // weights needed during the pass
 
   // temperature coefficient c = log2(e) / T = chi + clo, chi rounded down, clo > 0
-  float chi = 0.0f, clo = 0.0f, tlf = 0.0f;
+  float chi = 0.0f, clo = 0.0f;
   double tdl = 0.0;  // T ln(min_p)
   if (!greedy) {
     const double c = 1.4426950408889634 / (double)P.temperature;
@@ -873,10 +864,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     if (!(clo > 0.0f)) clo = 1e-30f;
     chi = uniform_f32(chi);
     clo = uniform_f32(clo);
-    if (mon) {
-      tdl = uniform_f64((double)P.temperature * log((double)P.min_p));
-      tlf = uniform_f32((float)tdl);
-    }
+    if (mon) tdl = uniform_f64((double)P.temperature * log((double)P.min_p));
   }
 
   // the row's uniform, while the loads are in flight

@@ -436,6 +436,43 @@ def test_deterministic_replay(arcs):
         assert np.array_equal(arcs.sample(logits, params, seed=3, step=9).cpu().numpy(), first)
 
 
+def test_graph_capture_replays_match_eager(arcs):
+    """Both entry points captured in a HIP graph (seed and step are baked in):
+    every replay, with eager launches and synchronisations between replays,
+    gives the eager result."""
+    import torch
+    B = 64
+    w = make_workload("zipf_b512_bf16_mixed_penalties", B=B, hist_len=256)
+    logits = to_device_logits(w.logits, "bf16")
+    params = arcs.params_to_device(w.params)
+    hi, ho = hist_to_device(w)
+    want_s = arcs.sample(logits, params, hi, ho, seed=7, step=3).cpu().numpy()
+    want_a = arcs.argmax(logits).cpu().numpy()
+    out_s = torch.empty(B, dtype=torch.int32, device="cuda")
+    out_a = torch.empty(B, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up launches outside the capture
+        arcs.sample(logits, params, hi, ho, seed=7, step=3, out=out_s)
+        arcs.argmax(logits, out=out_a)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arcs.sample(logits, params, hi, ho, seed=7, step=3, out=out_s)
+        arcs.argmax(logits, out=out_a)
+    for i in range(6):
+        out_s.fill_(-5)
+        out_a.fill_(-5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_s.cpu().numpy(), want_s), i
+        assert np.array_equal(out_a.cpu().numpy(), want_a), i
+        other = arcs.sample(logits, params, hi, ho, seed=11, step=i).cpu().numpy()  # eager work in between
+        assert other.shape == (B,)
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # the named workloads at full size
 # --------------------------------------------------------------------------
