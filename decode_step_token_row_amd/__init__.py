@@ -13,9 +13,11 @@ from ._binding import (  # noqa: F401
     ROW_STATS_DTYPE,
     argmax,
     library,
+    make_key,
     params_to_device,
     sample,
     sample_debug,
+    sample_keyed,
     status_string,
     version,
     workspace_bytes,

@@ -83,6 +83,9 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_debug.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p, c_p, c_p, c_p]
         lib.arcs_sample_debug.restype = c_i
+        lib.arcs_sample_keyed.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i,
+                                          c_p, c_p, c_p, ctypes.c_size_t, c_p]
+        lib.arcs_sample_keyed.restype = c_i
         lib.arcs_sample_workspace_bytes.argtypes = [c_i64, c_i64, c_i]
         lib.arcs_sample_workspace_bytes.restype = ctypes.c_size_t
         lib.arcs_status_string.argtypes = [c_i]
@@ -200,6 +203,41 @@ def sample(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step
                                ws_bytes, _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_sample")
+    return out
+
+
+def make_key(seed: int = 0, step: int = 0, device="cuda"):
+    """A device RNG key {seed, step} for sample_keyed (int64 storage of the
+    two uint64 words)."""
+    torch = _torch()
+    words = [int(seed) & (2**64 - 1), int(step) & (2**64 - 1)]
+    words = [w - 2**64 if w >= 2**63 else w for w in words]
+    return torch.tensor(words, dtype=torch.int64, device=device)
+
+
+def sample_keyed(logits, params, key, hist_ids=None, hist_offsets=None, advance: bool = True,
+                 out=None, out_status=None, workspace=None, stream=None):
+    """arcs_sample_keyed: seed and step read from the device key (see make_key);
+    with `advance` the key's step moves on by one after the draw."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    _check_params(params, B)
+    _check_hist(hist_ids, hist_offsets, B)
+    if not key.is_cuda or key.dtype != torch.int64 or key.numel() != 2 or not key.is_contiguous():
+        raise ValueError("key must be a contiguous device int64 tensor of 2 elements (seed, step)")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=logits.device)
+        ws_bytes = ws_need
+    st = library().arcs_sample_keyed(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),
+                                     _ptr(hist_ids), _ptr(hist_offsets), _ptr(key), 1 if advance else 0,
+                                     _ptr(out), _ptr(out_status), _ptr(workspace), ws_bytes,
+                                     _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample_keyed")
     return out
 
 

@@ -44,7 +44,7 @@ int fixed_bits(int64_t V) {
 
 int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                 const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
-                uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status,
+                uint64_t seed, uint64_t step, const uint64_t* key, int32_t* out_ids, int32_t* out_status,
                 void* workspace, size_t workspace_bytes, const double* uniforms, float* out_probs,
                 arcs_row_stats* out_stats, void* stream) {
   int st = check_common(logits, dtype, B, V, row_stride, out_ids);
@@ -62,6 +62,7 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   a.hist_offsets = hist_offsets;
   a.seed = seed;
   a.step = step;
+  a.key = key;
   a.out_ids = out_ids;
   a.out_status = out_status;
   a.uniforms = uniforms;
@@ -95,8 +96,20 @@ int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
                 uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step,
-                     out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                     nullptr, out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr,
                      stream);
+}
+
+int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const arcs_row_params* params, const int32_t* hist_ids,
+                      const int64_t* hist_offsets, uint64_t* key, int advance, int32_t* out_ids,
+                      int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (key == nullptr) return ARCS_ERR_NULL_POINTER;
+  if (((uintptr_t)key) % 8u != 0) return ARCS_ERR_MISALIGNED;
+  int st = sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, 0, 0, key,
+                       out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr, stream);
+  if (st != ARCS_OK || !advance) return st;
+  return arcs::launch_advance_step(key, (hipStream_t)stream) == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
 }
 
 int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
@@ -106,7 +119,7 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
                       size_t workspace_bytes, const double* uniforms, float* out_probs,
                       arcs_row_stats* out_stats, void* stream) {
   return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step,
-                     out_ids, out_status, workspace, workspace_bytes, uniforms, out_probs,
+                     nullptr, out_ids, out_status, workspace, workspace_bytes, uniforms, out_probs,
                      out_stats, stream);
 }
 

@@ -19,6 +19,7 @@ struct SampleArgs {
   const int64_t* hist_offsets;
   uint64_t seed;
   uint64_t step;
+  const uint64_t* key;  // device {seed, step} read at run time instead of seed / step, or NULL
   int32_t* out_ids;
   int32_t* out_status;
   const double* uniforms;
@@ -33,5 +34,6 @@ struct SampleArgs {
 hipError_t launch_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
                          bool vec, int32_t* out, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream);
+hipError_t launch_advance_step(uint64_t* key, hipStream_t stream);
 
 }  // namespace arcs

@@ -700,7 +700,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
     double x = u * 0x1p64;
     uf = (x >= 0x1p64) ? ~0ull : (x <= 0.0 ? 0ull : (uint64_t)x);
   } else {
-    uint64_t x = splitmix64_counter_output(a.seed, (uint64_t)row, a.step);
+    uint64_t x = splitmix64_counter_output(a.key ? a.key[0] : a.seed, (uint64_t)row, a.key ? a.key[1] : a.step);
     uf = (x >> 11) << 11;
     u = (double)(x >> 11) * 0x1p-53;
   }

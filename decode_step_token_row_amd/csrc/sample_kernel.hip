@@ -873,7 +873,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     if (a.uniforms) {
       u = a.uniforms[row];
     } else {
-      const uint64_t x = splitmix64_counter_output(a.seed, (uint64_t)row, a.step);
+      const uint64_t x = splitmix64_counter_output(a.key ? a.key[0] : a.seed, (uint64_t)row, a.key ? a.key[1] : a.step);
       u = (double)(x >> 11) * 0x1p-53;
     }
     u = uniform_f64(u);
@@ -1343,6 +1343,18 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hi
                : launch_one(sample_kernel<false, true, false>, false, a, B, lds, stream, done[7]);
   return pen ? launch_one(sample_kernel<false, false, true>, false, a, B, lds, stream, done[8])
              : launch_one(sample_kernel<false, false, false>, false, a, B, lds, stream, done[9]);
+}
+
+// The step of a device-held key moves on by one.  Enqueued after the
+// sampling kernel on the same stream, so every workgroup has read the old
+// value; inside a captured graph each replay advances it.
+__global__ void advance_step_kernel(uint64_t* key) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) key[1] += 1u;
+}
+
+hipError_t launch_advance_step(uint64_t* key, hipStream_t stream) {
+  hipLaunchKernelGGL(advance_step_kernel, dim3(1), dim3(64), 0, stream, key);
+  return hipGetLastError();
 }
 
 }  // namespace arcs

@@ -166,6 +166,28 @@ int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
                 const int64_t* hist_offsets, uint64_t seed, uint64_t step, int32_t* out_ids,
                 int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * arcs_sample_keyed: arcs_sample with the RNG key in device memory, for
+ * decode loops captured in a HIP graph.  Arc PR #217 ("device decode loop",
+ * "What this does", step 3) keeps the per-step state on the device and moves
+ * it on with a device kernel, so that a captured step needs no host work
+ * between launches; a key passed by value would instead be frozen into the
+ * graph at capture time.
+ *   key       device uint64[2] = {seed, step}, 8-byte aligned, read when the
+ *             kernels run (the uniform of row b uses counter step * 2^32 + b
+ *             under seed, exactly as arcs_sample)
+ *   advance   nonzero: a one-thread kernel enqueued after the sampling kernel
+ *             on the same stream adds 1 to key[1] (each graph replay then
+ *             samples the next step); 0: key is only read
+ * Other arguments, errors and outputs as arcs_sample; a NULL or misaligned
+ * key is rejected before any launch.  Calls that share one key must be
+ * ordered on one stream.
+ */
+int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const arcs_row_params* params, const int32_t* hist_ids,
+                      const int64_t* hist_offsets, uint64_t* key, int advance, int32_t* out_ids,
+                      int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace arcs_sample needs for this shape (may be 0). */
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype);
 

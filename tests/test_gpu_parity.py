@@ -473,6 +473,45 @@ def test_graph_capture_replays_match_eager(arcs):
         torch.cuda.synchronize()
 
 
+def test_keyed_sampling_matches_by_value_key_eager_and_in_a_graph(arcs):
+    """arcs_sample_keyed reads {seed, step} from device memory: eager calls
+    with advance walk through steps s0, s0+1, ...; a captured graph replays
+    the next step each time; both give arcs_sample's ids for those steps."""
+    import torch
+    B, s0, seed = 48, 5, 2**63 + 12345
+    w = make_workload("zipf_b512_bf16_mixed_penalties", B=B, V=20_005, hist_len=200)
+    logits = to_device_logits(w.logits, "bf16")
+    params = arcs.params_to_device(w.params)
+    hi, ho = hist_to_device(w)
+    want = [arcs.sample(logits, params, hi, ho, seed=seed, step=s0 + i).cpu().numpy() for i in range(8)]
+    key = arcs.make_key(seed, s0)
+    for i in range(3):
+        got = arcs.sample_keyed(logits, params, key, hi, ho).cpu().numpy()
+        assert np.array_equal(got, want[i]), i
+    assert int(key[1]) == s0 + 3
+    got = arcs.sample_keyed(logits, params, key, hi, ho, advance=False).cpu().numpy()
+    assert np.array_equal(got, want[3]) and int(key[1]) == s0 + 3
+    # captured: each replay samples the next step
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        arcs.sample_keyed(logits, params, key, hi, ho, advance=False, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arcs.sample_keyed(logits, params, key, hi, ho, out=out)
+    for i in range(3, 8):
+        out.fill_(-5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want[i]), i
+        assert int(key[1]) == s0 + i + 1
+        arcs.sample(logits, params, hi, ho, seed=1, step=i)  # eager work in between
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # the named workloads at full size
 # --------------------------------------------------------------------------

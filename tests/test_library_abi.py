@@ -17,8 +17,8 @@ def arcs():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    for name in ("arcs_argmax", "arcs_sample", "arcs_sample_workspace_bytes", "arcs_status_string",
-                 "arcs_sample_debug", "arcs_version"):
+    for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
+                 "arcs_status_string", "arcs_sample_debug", "arcs_version"):
         assert name in fns
 
 
@@ -68,3 +68,9 @@ def test_host_validation_rejects_before_launch(arcs):
     assert S(p, 0, 4, 10, 10, p, None, p, 0, 0, p, None, None, 0, None) == -9
     assert S(p, 0, 4, 10, 5, p, None, None, 0, 0, p, None, None, 0, None) == -4
     assert S(p, 3, 4, 10, 10, p, None, None, 0, 0, p, None, None, 0, None) == -5
+    # sample with a device key: the key is checked before anything else runs
+    K = lib.arcs_sample_keyed
+    assert K(p, 0, 4, 10, 10, p, None, None, None, 1, p, None, None, 0, None) == -1
+    assert K(p, 0, 4, 10, 10, p, None, None, ctypes.c_void_p(base + 4), 1, p, None, None, 0, None) == -8
+    assert K(p, 0, 4, 10, 10, None, None, None, p, 1, p, None, None, 0, None) == -1
+    assert K(p, 0, 4, 10, 9, p, None, None, p, 0, p, None, None, 0, None) == -4
