@@ -408,10 +408,13 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const PenCtx&
 // the weights in (value desc, id asc) order for L = min(L_k, L_p, L_m), then a
 // rank by id among the kept prefix and a second scan for the id-order draw.
 // Writes the output row and sh.u64[10..12] / sh.f64[kNW+1] (id, L, cut key,
-// S_K); returns false if no prefix length is known from the candidates.
-__device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh, int nc,
+// S_K).  Returns 1 when drawn, 0 when no prefix length is known from the
+// candidates, 2 (nothing written) when `lazy_cap` > 0 and the kept mass
+// reaches it.
+__device__ __forceinline__ int small_cut_draw(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh, int nc,
                                                uint64_t key, float w, bool kon, int top_k, bool pon, double Pm,
-                                               bool minp_complete, float zt, double u) {
+                                               bool minp_complete, float zt, double u,
+                                              double lazy_cap) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int64_t INF = INT64_MAX;
   const bool in = lane < nc;
@@ -441,12 +444,15 @@ __device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row,
   if (minp_complete) Lm = __builtin_popcountll(__ballot(in && key_value(~(uint32_t)(skey >> 32)) >= zt));
   int64_t Lw = Lk < Lp ? Lk : Lp;
   Lw = Lw < Lm ? Lw : Lm;
-  if (Lw == INF || Lw < 1) return false;
+  if (Lw == INF || Lw < 1) return 0;
   const int lc = (int)Lw - 1;
   const uint64_t cb = __builtin_bit_cast(uint64_t, cum);
   const double sk = __builtin_bit_cast(
       double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(cb >> 32), lc) << 32) |
                   (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cb, lc));
+  // top-p left out while the row's mass is only bounded below: the cut
+  // stands when the kept mass stays under top_p times that bound
+  if (lazy_cap > 0.0 && !(sk < lazy_cap)) return 2;
   const uint64_t ck = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(skey >> 32), lc) << 32) |
                       (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)skey, lc);
   const double t = u * sk;
@@ -474,7 +480,7 @@ __device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row,
     a.out_ids[row] = (int32_t)pid;
     if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
   }
-  return true;
+  return 1;
 }
 
 // Cut over nc > kSmallSort candidates (keys and row-frame weights in LDS, in
@@ -488,13 +494,16 @@ __device__ __forceinline__ bool small_cut_draw(const SampleArgs& a, int64_t row,
 // form (they weigh the same); when not all are, a descent over their ids
 // (9 + 8 bits; ids < 2^17) finds the last kept one.  The bins live at
 // sm.hcnt / sm.hmass (inside the group area, free at this point).  Returns
-// false (uniformly) when the candidates reach no target.
+// false (uniformly) when the candidates reach no target; kept_mass is the
+// kept entries' weight (from the 2^-50 fixed-point sums; masses are tracked
+// when `track_mass`, which top-p needs).
 constexpr double kFixScale = 1125899906842624.0;  // 2^50: weights < 2, at most 4096 of them
 __device__ __forceinline__ uint64_t to_fix50(float w) { return (uint64_t)((double)w * kFixScale); }
 
 __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int nc, int lowbit, bool kon, int top_k,
                                                  bool pon, double Pm, bool minp_complete, float zt, KeepCut& cut,
-                                                 int64_t& L) {
+                                                 int64_t& L, double& kept_mass,
+                                                 bool track_mass) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   constexpr int ENT = kCandCap / kNT;
   uint32_t* hc = sm.hcnt;
@@ -555,7 +564,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
         if (top == 31 || (vk >> (top + 1)) == (pref >> (top + 1))) {
           const uint32_t d = (vk >> shf) & dmask;
           atomicAdd(&hc[d], 1u);
-          if (pon) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)to_fix50(sm.cw[i]));
+          if (track_mass) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)to_fix50(sm.cw[i]));
         }
       }
     }
@@ -635,6 +644,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     }
   }
   L = (int64_t)(cnt_above + r);
+  kept_mass = (double)(mass_above + r * (c_eq ? m_eq / c_eq : 0)) / kFixScale;
   cut.th = th;
   cut.istar = INT64_MAX;
   if (r < c_eq && c_eq <= (uint64_t)kSmallSort) {
@@ -812,6 +822,33 @@ __device__ __forceinline__ bool cand_draw(const SampleArgs& a, int64_t row, cons
   return true;
 }
 
+// The row's exact total weight in the row frame (-negks): the row read
+// again (from cache), every element weighed; fp64 per thread, one wave sum
+// and one LDS sum.  All threads call it; uniform result.
+template <bool PEN>
+__device__ __forceinline__ double exact_row_mass(const u32x4* rv, const PenCtx& pc, int ngroups, float chi,
+                                                 float clo, float negks, Shared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  u32x4 dd[kQ];
+  issue_row_loads(rv, ngroups, dd);
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const bool valid = tid < ngroups - q * kNT;
+    float z[8];
+    unpack8(dd[q], z);
+    if (PEN && pc.on && valid) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
+    s += valid ? (double)group_weight(z, chi, clo, negks) : 0.0;
+  }
+  s = dpp_wave_sum_f64(s);
+  __syncthreads();
+  if (lane == 0) sh.rtot[wid] = s;
+  __syncthreads();
+  double S = 0.0;
+  for (int w = 0; w < kNW; ++w) S += sh.rtot[w];
+  return S;
+}
+
 // One row on the summary path.  d holds the loads of the row's groups,
 // issued by the caller.  Returns false (uniformly across the block) when the
 // row must be redone by the general pipeline.
@@ -850,6 +887,15 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   const bool pon = !greedy && P.top_p < 1.0f;
   const bool mon = !greedy && P.min_p > 0.0f;
   const bool weights = nofilter || pon;  // weights needed during the pass
+  // top-p with top-k: the pass weighs only each group's maximum, which bounds
+  // the row's mass from below; a top-k prefix whose mass stays under top_p
+  // times that bound is not cut by top-p, and only when it is not is the
+  // exact mass computed (a second read of the row).  A prefix of at most k
+  // tokens rarely reaches top_p of the mass; a min-p set without top-k holds
+  // most of it on exactly the peaked rows where top-p cuts, so those rows
+  // weigh every element in the pass.  The penalised kernel always weighs every
+  // element: there the second-read code measured slower than what it saves.
+  bool lazy = !PEN && pon && kon;
 
   // temperature coefficient c = log2(e) / T = chi + clo, chi rounded down, clo > 0
   float chi = 0.0f, clo = 0.0f;
@@ -925,7 +971,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       kfr = nk;
       negk = -nk;
     }
-    const float s = group_weight(z, chi, clo, negk);
+    const float s = lazy ? wexp(g, chi, clo, negk) : group_weight(z, chi, clo, negk);
     if (nofilter) sm.tsum[q * kNT + tid] = valid ? s : 0.0f;
     else lsum += valid ? (double)s : 0.0;
   }
@@ -1023,8 +1069,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   }
   __syncthreads();
   const float m = sh.r_m, negks = sh.r_negks, zt = sh.r_zt, zc0 = sh.r_zc;
-  double S = sh.r_S;
-  const double Pm = sh.r_Pm;
+  double S = sh.r_S;  // a lower bound of the row's mass while `lazy`
+  double Pm = sh.r_Pm;
   int32_t mode = sh.r_mode;
   if (mode == kModeFallback) return false;
 
@@ -1147,7 +1193,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           const uint32_t cex = dpp_wave_incl_scan_u32(ctot) - ctot;
           const double mex = dpp_wave_incl_scan_f64(mtot) - mtot;
           const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
-          const double p_need = pon ? Pm * (1.0 + 1e-4) : __builtin_inf();
+          const double p_need = (pon && !lazy) ? Pm * (1.0 + 1e-4) : __builtin_inf();
           int fb = 4;
           uint32_t cc = cex;
           double mc = mex;
@@ -1182,13 +1228,22 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
     if (nc > kCandCap || nc <= 0) return false;
     if (nc <= kSmallSort) {
-      if (wid == 0) {
-        const uint64_t key = lane < nc ? sm.ckey[lane] : ~0ull;
-        const float w = lane < nc ? sm.cw[lane] : 0.0f;
-        if (!small_cut_draw(a, row, sm, sh, nc, key, w, kon, P.top_k, pon, Pm, minp_complete, zt, u) && lane == 0)
-          sh.i32[6] = -1;
+      for (;;) {
+        if (wid == 0) {
+          const uint64_t key = lane < nc ? sm.ckey[lane] : ~0ull;
+          const float w = lane < nc ? sm.cw[lane] : 0.0f;
+          const double cap = lazy ? (double)P.top_p * S * (1.0 - 1e-5) : 0.0;
+          const int rc = small_cut_draw(a, row, sm, sh, nc, key, w, kon, P.top_k, pon && !lazy, Pm, minp_complete,
+                                        zt, u, cap);
+          if (lane == 0) sh.i32[6] = rc == 1 ? 0 : (rc == 2 ? 1 : -1);
+        }
+        __syncthreads();
+        if (!lazy || sh.i32[6] != 1) break;
+        // top-p may cut inside the prefix: the exact mass, then the cut again
+        S = exact_row_mass<PEN>(rv, pc, ngroups, chi, clo, negks, sh);
+        Pm = (double)P.top_p * S;
+        lazy = false;
       }
-      __syncthreads();
       if (sh.i32[6] < 0) return false;
       if (!debug) return true;
       id = (int64_t)sh.u64[10];
@@ -1201,7 +1256,18 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       // a larger set: select the cut, then draw in id order over masked group sums
       KeepCut cut;
       const int lowbit = (PEN && pc.on) ? 0 : 16;
-      if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, pon, Pm, minp_complete, zt, cut, L)) return false;
+      double kept_mass = 0.0;
+      if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, pon && !lazy, Pm, minp_complete, zt, cut, L, kept_mass,
+                            pon))
+        return false;
+      if (lazy && !(kept_mass < (double)P.top_p * S * (1.0 - 1e-5))) {
+        // top-p may cut inside the prefix: the exact mass, then the cut again
+        S = exact_row_mass<PEN>(rv, pc, ngroups, chi, clo, negks, sh);
+        Pm = (double)P.top_p * S;
+        lazy = false;
+        if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, true, Pm, minp_complete, zt, cut, L, kept_mass, true))
+          return false;
+      }
       const double ux = u * 0x1p64;  // the uniform as a 64-bit fraction
       const uint64_t uf = ux >= 0x1p64 ? ~0ull : (ux <= 0.0 ? 0ull : (uint64_t)ux);
       if (!cand_draw(a, row, sm, sh, nc, cut, uf)) return false;
@@ -1215,6 +1281,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   }
 
   // ---- debug outputs (the row is read again) ---------------------------------------
+  if (lazy) S = 0.0;  // only a bound: the re-read below gives the mass
   {
     const bool all_kept = (path & ARCS_PATH_SORT_SKIP) != 0;
     uint32_t kmin = 0xFFFFFFFFu;

@@ -392,6 +392,35 @@ def test_large_top_k_low_temperature_and_penalised_rows_stay_resident(arcs):
     assert np.all((stats["path"][B // 2:] & 32) != 0)
 
 
+def test_top_p_with_other_filters_binding_or_not(arcs):
+    """top-p together with top-k or min-p: rows where top-p does not cut
+    inside the other filters' prefix (settled from a lower bound of the mass)
+    and rows where it does (the exact mass is computed), on small and large
+    candidate sets, with and without penalties, plus min-p + top-p rows whose
+    min-p set overflows the candidate list."""
+    B = 16
+    w = make_workload("zipf_b512_bf16_mixed_penalties", B=B, V=129_280, hist_len=512)
+    p = make_params(B, temperature=0.7)
+    cfg = [(0.7, 50, 0.9, 0.05), (0.7, -1, 0.3, 0.01), (1.0, 500, 0.5, 0.0), (1.0, 500, 0.99, 0.0),
+           (1.5, -1, 0.95, 1e-4), (0.4, 2000, 0.8, 0.0), (1.2, 64, 0.2, 0.0), (0.9, -1, 0.999, 0.2)]
+    for b in range(B):
+        T, k, tp, mp = cfg[b % 8]
+        p[b]["temperature"], p[b]["top_k"], p[b]["top_p"], p[b]["min_p"] = T, k, tp, mp
+        if b >= 8:
+            p[b]["presence"], p[b]["frequency"], p[b]["repetition"] = 0.5, 0.3, 1.1
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "top-p with others")
+    for b, r in enumerate(refs):  # the reported mass is the exact one
+        if r.status == 0 and not r.greedy:
+            assert abs(stats[b]["mass_total"] - r.S) <= 1e-5 * r.S, (b, stats[b]["mass_total"], r.S)
+    logits = to_device_logits(w.logits, w.dtype)
+    hi, ho = hist_to_device(w)
+    got = arcs.sample(logits, arcs.params_to_device(w.params), hi, ho, seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
+
+
 def test_minp_rows_with_crowded_threads(arcs):
     """min-p rows whose large values crowd a few 16-byte groups 8,192 tokens
     apart (one thread's share of the row on the single-pass kernel): several
