@@ -243,12 +243,22 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, BlockScratch
   return v + off;
 }
 
+// A workgroup barrier that orders LDS only: it waits for the wave's LDS
+// operations, not for its outstanding global loads (which __syncthreads
+// would drain), so row loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_incl_scan_u32(uint32_t v, BlockScratch& bs, uint32_t& total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   v = wave_incl_scan_u32(v, lane);
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier(); else __syncthreads();
   if (lane == kWave - 1) bs.u32[wid] = v;
-  __syncthreads();
+  if (LDS_ONLY) lds_barrier(); else __syncthreads();
   uint32_t off = 0, t = 0;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) {
@@ -356,6 +366,34 @@ struct Shared {
   uint32_t r_arg;
 };
 
+// Per-row parameter validation: ARCS_ROW_OK or the row's error code.
+__device__ __forceinline__ int row_param_status(const arcs_row_params& P) {
+  if (!(P.temperature >= 0.0f)) return ARCS_ROW_BAD_TEMPERATURE;
+  if (!(P.top_p > 0.0f)) return ARCS_ROW_BAD_TOP_P;
+  if (!(P.min_p >= 0.0f && P.min_p <= 1.0f)) return ARCS_ROW_BAD_MIN_P;
+  if (!(__builtin_isfinite(P.presence) && __builtin_isfinite(P.frequency) && __builtin_isfinite(P.repetition)) ||
+      P.repetition < 0.0f)
+    return ARCS_ROW_BAD_PENALTY;
+  if (P.flags != 0) return ARCS_ROW_BAD_FLAGS;
+  return ARCS_ROW_OK;
+}
+
+// A row whose parameters or history failed: -1, its status, zeroed debug outputs.
+__device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t row, int status) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    a.out_ids[row] = -1;
+    if (a.out_status) a.out_status[row] = status;
+    if (a.stats) {
+      arcs_row_stats st = {};
+      st.id = -1; st.argmax = -1; st.status = status;
+      a.stats[row] = st;
+    }
+  }
+  if (a.out_probs)
+    for (int64_t i = tid; i < a.V; i += kNT) a.out_probs[row * a.V + i] = 0.0f;
+}
+
 // Parameter validation and penalty tables.  Returns false when the row is
 // finished (invalid parameters: out_ids = -1 and the status written).
 //
@@ -370,13 +408,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   const int tid = threadIdx.x;
   const int64_t V = a.V;
   // ---- 0. parameters (P holds the row's record, loaded by the caller) ------
-  int status = ARCS_ROW_OK;
-  if (!(P.temperature >= 0.0f)) status = ARCS_ROW_BAD_TEMPERATURE;
-  else if (!(P.top_p > 0.0f)) status = ARCS_ROW_BAD_TOP_P;
-  else if (!(P.min_p >= 0.0f && P.min_p <= 1.0f)) status = ARCS_ROW_BAD_MIN_P;
-  else if (!(__builtin_isfinite(P.presence) && __builtin_isfinite(P.frequency) &&
-             __builtin_isfinite(P.repetition)) || P.repetition < 0.0f) status = ARCS_ROW_BAD_PENALTY;
-  else if (P.flags != 0) status = ARCS_ROW_BAD_FLAGS;
+  int status = row_param_status(P);
 
   pc.on = false;
   pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
@@ -440,17 +472,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   }
 
   if (status != ARCS_ROW_OK) {
-    if (tid == 0) {
-      a.out_ids[row] = -1;
-      if (a.out_status) a.out_status[row] = status;
-      if (a.stats) {
-        arcs_row_stats st = {};
-        st.id = -1; st.argmax = -1; st.status = status;
-        a.stats[row] = st;
-      }
-    }
-    if (a.out_probs)
-      for (int64_t i = tid; i < V; i += kNT) a.out_probs[row * V + i] = 0.0f;
+    write_row_failure(a, row, status);
     return false;
   }
   path = pc.on ? ARCS_PATH_PENALTY : 0u;

@@ -87,13 +87,32 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
 }
 
 
+// The history ids among the 8 elements of the group at g0 (a multiple of 8)
+// take their penalised values from the LDS tables: one pass of the loop per
+// history id in the group (groups without one cost a bitmap read), rather
+// than a branch per element.
+__device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCtx& pc) {
+  const uint32_t w = (uint32_t)(g0 >> 5), s5 = (uint32_t)(g0 & 31);
+  const uint32_t word = pc.bitmap[w];
+  uint32_t bits = (word >> s5) & 0xFFu;
+  if (!bits) return;
+  uint32_t r = (uint32_t)pc.wprefix[w] + (uint32_t)__builtin_popcount(word & ((1u << s5) - 1u));
+  do {
+    const int e = __builtin_ctz(bits);
+    bits &= bits - 1u;
+    const float pz = pc.zpen[r++];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z[k] = e == k ? pz : z[k];
+  } while (bits);
+}
+
 // The values z' of group j (elements 8j .. 8j + 7) from its 16 bytes: the
 // bf16 widened, then, on rows with active penalties, the history ids among
 // them replaced by their penalised logits from the LDS tables.
 template <bool PEN>
 __device__ __forceinline__ void load_z8(u32x4 d, int j, const PenCtx& pc, float (&z)[8]) {
   unpack8(d, z);
-  if (PEN && pc.on) apply_penalties<8>(z, (int64_t)j * 8, 8, pc);
+  if (PEN && pc.on) penalize8(z, (int64_t)j * 8, pc);
 }
 
 // Maximum of a group.  v_max ignores quiet NaNs (the same as treating them
@@ -326,8 +345,8 @@ __device__ __forceinline__ void gather_candidates(const u32x4* rv, const PenCtx&
   unpack8(da, za);
   unpack8(db, zb);
   if (PEN && pc.on) {
-    if (pa) apply_penalties<8>(za, (int64_t)(bq * kNT + tid) * 8, 8, pc);
-    if (pb) apply_penalties<8>(zb, (int64_t)(sq * kNT + tid) * 8, 8, pc);
+    if (pa) penalize8(za, (int64_t)(bq * kNT + tid) * 8, pc);
+    if (pb) penalize8(zb, (int64_t)(sq * kNT + tid) * 8, pc);
   }
   uint32_t n = 0;
 #pragma unroll
@@ -834,10 +853,14 @@ __device__ __forceinline__ double exact_row_mass(const u32x4* rv, const PenCtx& 
   double s = 0.0;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    const bool valid = tid < ngroups - q * kNT;
+    // the round's bound is formed here, not hoisted out of the unrolled
+    // loop: sixteen live lane masks would crowd out the scalar registers
+    int lim = ngroups - q * kNT;
+    asm volatile("" : "+s"(lim));
+    const bool valid = tid < lim;
     float z[8];
     unpack8(dd[q], z);
-    if (PEN && pc.on && valid) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
+    if (PEN && pc.on && valid) penalize8(z, (int64_t)(q * kNT + tid) * 8, pc);
     s += valid ? (double)group_weight(z, chi, clo, negks) : 0.0;
   }
   s = dpp_wave_sum_f64(s);
@@ -870,10 +893,29 @@ __device__ __forceinline__ double exact_row_mass(const u32x4* rv, const PenCtx& 
 //                   of them) or by a radix select, and drawn from in id order;
 //   min-p alone over more than the list holds -> masked group sums and the
 //                   id-order draw.
+// What the row's uniform is made from, read at the start of the kernel with
+// the parameter record (before the row's loads, so that using it does not
+// wait for them): the override of the debug entry point, or the RNG key (by
+// value, or from device memory for the keyed entry point).
+struct RowRng {
+  uint64_t seed, step;
+  double u_override;
+  bool override_on;
+};
+
+__device__ __forceinline__ RowRng load_row_rng(const SampleArgs& a, int64_t row) {
+  RowRng r;
+  r.override_on = a.uniforms != nullptr;
+  r.u_override = r.override_on ? a.uniforms[row] : 0.0;
+  r.seed = a.key ? a.key[0] : a.seed;
+  r.step = a.key ? a.key[1] : a.step;
+  return r;
+}
+
 template <bool PEN>
 __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
-                                           const PenCtx& pc, uint32_t path, const Smem& sm, Shared& sh,
-                                           const u32x4 (&d)[kQ]) {
+                                           const RowRng& rng, const PenCtx& pc, uint32_t path, const Smem& sm,
+                                           Shared& sh, const u32x4 (&d)[kQ]) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t V = a.V;
   const int ngroups = (int)(V / 8);
@@ -916,10 +958,10 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // the row's uniform, while the loads are in flight
   double u = 0.0;
   if (!greedy) {
-    if (a.uniforms) {
-      u = a.uniforms[row];
+    if (rng.override_on) {
+      u = rng.u_override;
     } else {
-      const uint64_t x = splitmix64_counter_output(a.key ? a.key[0] : a.seed, (uint64_t)row, a.key ? a.key[1] : a.step);
+      const uint64_t x = splitmix64_counter_output(rng.seed, (uint64_t)row, rng.step);
       u = (double)(x >> 11) * 0x1p-53;
     }
     u = uniform_f64(u);
@@ -938,10 +980,14 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   bool bad = false, special = false;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    const bool valid = tid < ngroups - q * kNT;
+    // the round's bound is formed here, not hoisted out of the unrolled
+    // loop: sixteen live lane masks would crowd out the scalar registers
+    int lim = ngroups - q * kNT;
+    asm volatile("" : "+s"(lim));
+    const bool valid = tid < lim;
     float z[8];
     unpack8(d[q], z);
-    if (PEN && pc.on && valid) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
+    if (PEN && pc.on && valid) penalize8(z, (int64_t)(q * kNT + tid) * 8, pc);
     float g = group_max(z);
     special = special || !(g == g);
     g = valid && g == g ? g : -__builtin_inff();
@@ -1127,7 +1173,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       for (int q = 0; q < kQ; ++q) {
         float z[8];
         unpack8(dd[q], z);
-        if (PEN && pc.on && tid < ngroups - q * kNT) apply_penalties<8>(z, (int64_t)(q * kNT + tid) * 8, 8, pc);
+        if (PEN && pc.on && tid < ngroups - q * kNT) penalize8(z, (int64_t)(q * kNT + tid) * 8, pc);
         const KeepCut cut{ord_key(zt), INT64_MAX};
         const int64_t i0 = (int64_t)(q * kNT + tid) * 8;
         float s = keep_cut(z[0], i0, cut) ? wexp(z[0], chi, clo, negks) : 0.0f;
@@ -1347,6 +1393,121 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   return true;
 }
 
+// The penalised summary kernel holds the first kHistRegs * kNT history ids
+// of its row in registers, with the raw logits at those ids, both loaded
+// before the row's own loads: waiting for them then leaves the row's loads in
+// flight (loads complete in issue order).
+constexpr int kHistRegs = 4;
+struct RowHist {
+  int64_t h0, h1;
+  int32_t id[kHistRegs];  // -1 past the end
+  uint16_t raw[kHistRegs];  // the raw bf16 logit at id (ids in [0, V))
+};
+
+// Parameter status, history bounds, the history ids and the raw logits at
+// them, issued before the row's loads.  Returns the row's status.
+__device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row, const arcs_row_params& P,
+                                                PenCtx& pc, RowHist& hs) {
+  const int tid = threadIdx.x;
+  const int status = row_param_status(P);
+  pc.on = false;
+  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
+  pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  hs.h0 = 0; hs.h1 = 0;
+  if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
+    const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on;
+    hs.h0 = a.hist_offsets[row];
+    hs.h1 = a.hist_offsets[row + 1];
+    pc.on = active && hs.h1 > hs.h0;
+  }
+  // branch-free: buffer loads past a resource's size return 0 without a
+  // memory access (rows without active penalties get an empty resource; ids
+  // outside [0, V) read past the row's resource and are skipped later)
+  const int64_t n = pc.on ? hs.h1 - hs.h0 : 0;
+  const int64_t nreg = n < (int64_t)kHistRegs * kNT ? n : (int64_t)kHistRegs * kNT;
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(pc.on ? a.hist_ids + hs.h0 : a.hist_ids), (short)0, (int)(nreg * 4), 0x00020000);
+#pragma unroll
+  for (int k = 0; k < kHistRegs; ++k) {
+    const int j = k * kNT + tid;
+    const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(hr, j * 4, 0, 0);
+    hs.id[k] = (int64_t)j < nreg ? v : -1;
+  }
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)a.logits + row * a.stride * 2), (short)0, pc.on ? (int)(a.V * 2) : 0, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < kHistRegs; ++k)
+    hs.raw[k] = __builtin_amdgcn_raw_buffer_load_b16(rr, (int)((uint32_t)hs.id[k] * 2u), 0, 0);
+  return status;
+}
+
+// Visits the row's history ids in [0, V), with their raw logits when
+// WITH_RAW: those held in registers, then any beyond them from memory.
+template <bool WITH_RAW, class Fn>
+__device__ __forceinline__ void for_each_hist_id(const SampleArgs& a, int64_t row, const RowHist& hs, Fn&& f) {
+#pragma unroll
+  for (int k = 0; k < kHistRegs; ++k)
+    if (hs.id[k] >= 0 && (int64_t)hs.id[k] < a.V) f((uint32_t)hs.id[k], WITH_RAW ? bf16_to_f32(hs.raw[k]) : 0.0f);
+  const uint16_t* rowp = (const uint16_t*)((const char*)a.logits + row * a.stride * 2);
+  for (int64_t i = hs.h0 + (int64_t)kHistRegs * kNT + threadIdx.x; i < hs.h1; i += kNT) {
+    const int32_t id = a.hist_ids[i];
+    if (id >= 0 && (int64_t)id < a.V) f((uint32_t)id, WITH_RAW ? bf16_to_f32(rowp[id]) : 0.0f);
+  }
+}
+
+// Penalty tables of the summary path, built while the row's loads are in
+// flight (LDS-only barriers): the bitmap of the history ids over [0, V), the
+// number of distinct ids before each bitmap word, and per distinct id (by
+// rank, in id order) its penalised logit, from its occurrence count (counted
+// in the candidate area, free here) and its raw logit.  Returns false when
+// the row is finished (its status written).
+__device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh,
+                                                   int status, PenCtx& pc, const RowHist& hs, uint32_t& path) {
+  const int tid = threadIdx.x;
+  pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen;
+  if (status == ARCS_ROW_OK && pc.on) {
+    const uint32_t bw = a.bitmap_words;
+    for (uint32_t i = tid; i < bw; i += kNT) sm.bitmap[i] = 0u;
+    lds_barrier();
+    for_each_hist_id<false>(a, row, hs, [&](uint32_t id, float) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
+    lds_barrier();
+    const uint32_t per = (bw + kNT - 1) / kNT;
+    const uint32_t w0 = tid * per, w1 = (w0 + per < bw) ? w0 + per : bw;
+    uint32_t c = 0;
+    for (uint32_t w = w0; w < w1; ++w) c += (uint32_t)__builtin_popcount(sm.bitmap[w]);
+    uint32_t total;
+    const uint32_t incl = block_incl_scan_u32<true>(c, sh.bs, total);
+    if (total <= (uint32_t)kMaxDistinct) {
+      uint32_t run = incl - c;
+      for (uint32_t w = w0; w < w1; ++w) {
+        sm.wprefix[w] = (uint16_t)run;
+        run += (uint32_t)__builtin_popcount(sm.bitmap[w]);
+      }
+      for (uint32_t i = tid; i < total; i += kNT) sm.pcount[i] = 0u;
+      lds_barrier();
+      for_each_hist_id<false>(a, row, hs, [&](uint32_t id, float) {
+        atomicAdd(&sm.pcount[pen_rank(id, sm.bitmap, sm.wprefix)], 1u);
+      });
+      lds_barrier();
+      // every occurrence of an id writes the same penalised value
+      for_each_hist_id<true>(a, row, hs, [&](uint32_t id, float raw) {
+        const uint32_t rk = pen_rank(id, sm.bitmap, sm.wprefix);
+        sm.zpen[rk] = penalize(canon_nan(raw), sm.pcount[rk], pc);
+      });
+      lds_barrier();
+    } else {
+      status = ARCS_ROW_HISTORY_TOO_LONG;
+      pc.on = false;
+    }
+  }
+  if (status != ARCS_ROW_OK) {
+    write_row_failure(a, row, status);
+    return false;
+  }
+  path = pc.on ? ARCS_PATH_PENALTY : 0u;
+  return true;
+}
+
 template <bool PEN>
 __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -1356,20 +1517,32 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
   const int ngroups = (int)(a.V / 8);
   const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
   u32x4 d[kQ];
-  // Without penalty tables the row's loads go out right after the parameter
-  // record's, so that validating it overlaps their latency.
   arcs_row_params P = a.params[row];
-  __builtin_amdgcn_sched_barrier(0);
-  if (!PEN) issue_row_loads(rv, ngroups, d);
+  const RowRng rng = load_row_rng(a, row);
   PenCtx pc;
   uint32_t path;
-  if (!row_prologue<true, PEN>(a, row, sm, sh, P, pc, path)) return;
-  // With penalty tables the loads go out once the tables are built (the
-  // build's barriers would otherwise wait for them).
-  if (PEN) issue_row_loads(rv, ngroups, d);
-  if (!stream_row<PEN>(a, row, P, pc, path, sm, sh, d)) {
-    __syncthreads();
-    generic_row<true, true>(a, row, P, pc, path, sm, sh);
+  if (!PEN) {
+    // the row's loads go out right after the parameter record's, so that
+    // validating it overlaps their latency
+    __builtin_amdgcn_sched_barrier(0);
+    issue_row_loads(rv, ngroups, d);
+    if (!row_prologue<true, false>(a, row, sm, sh, P, pc, path)) return;
+    if (!stream_row<false>(a, row, P, rng, pc, path, sm, sh, d)) {
+      __syncthreads();
+      generic_row<true, true>(a, row, P, pc, path, sm, sh);
+    }
+  } else {
+    // history ids and the raw logits at them first, then the row's loads;
+    // the tables are built while those are in flight
+    RowHist hs;
+    const int status = load_row_history(a, row, P, pc, hs);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_row_loads(rv, ngroups, d);
+    if (!summary_pen_tables(a, row, sm, sh, status, pc, hs, path)) return;
+    if (!stream_row<true>(a, row, P, rng, pc, path, sm, sh, d)) {
+      __syncthreads();
+      generic_row<true, true>(a, row, P, pc, path, sm, sh);
+    }
   }
 }
 

@@ -260,6 +260,52 @@ def test_sample_penalties_small(arcs):
         assert bool(stats[b]["path"] & 32) == on
 
 
+def test_penalised_rows_long_histories_and_fallback(arcs):
+    """Penalised bf16 rows on the single-pass kernel: histories longer than the
+    ids it keeps in registers (with duplicates and ids outside [0, V)), empty
+    histories, penalties off, and filters whose candidate sets overflow the
+    on-chip list so the row is redone by the general pipeline with the
+    penalised values."""
+    B, V = 12, 129_280
+    rng = np.random.default_rng(41)
+    w = make_workload("zipf_b512_bf16_mixed_penalties", B=B, V=V, hist_len=8)
+    lens = [5000, 6100, 0, 4096, 4097, 300, 5000, 1024, 9000, 2, 4500, 700]
+    hs = []
+    for b, n in enumerate(lens):
+        pool = rng.integers(0, V, 3000 if b % 2 == 0 else 4000)
+        h = rng.choice(pool, n).astype(np.int32)
+        if n > 10:
+            h[3] = -1
+            h[7] = V + 5
+        hs.append(h)
+    w.hist_ids = np.concatenate(hs).astype(np.int32)
+    w.hist_offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    p = make_params(B, temperature=1.0)
+    modes = [(1.0, 6000, 1.0, 0.0), (2.0, -1, 0.99, 0.0), (0.8, 50, 0.9, 0.05), (0.0, -1, 1.0, 0.0),
+             (1.0, -1, 1.0, 0.0), (0.7, -1, 0.9, 0.02), (1.5, 5000, 0.95, 0.0), (0.6, 200, 1.0, 0.0),
+             (2.5, -1, 0.995, 0.0), (1.0, 20, 1.0, 0.0), (1.2, -1, 1.0, 1e-3), (0.9, 8000, 1.0, 0.0)]
+    pens = [(0.5, 0.3, 1.1), (0.0, 0.2, 1.0), (0.4, 0.0, 0.0), (0.5, 0.3, 1.1), (0.0, 0.0, 1.0),
+            (-0.6, 0.1, 1.3), (0.5, 0.3, 1.1), (0.2, 0.2, 0.9), (0.5, 0.3, 1.1), (0.5, 0.3, 1.1),
+            (0.0, 0.5, 1.0), (0.3, 0.0, 1.2)]
+    for b in range(B):
+        (p[b]["temperature"], p[b]["top_k"], p[b]["top_p"], p[b]["min_p"]) = modes[b]
+        (p[b]["presence"], p[b]["frequency"], p[b]["repetition"]) = pens[b]
+    w.params = p
+    ids, status, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "long histories")
+    active = [oracle.penalties_active(*pens[b]) and lens[b] > 0 for b in range(B)]
+    for b in range(B):
+        assert bool(stats[b]["path"] & 32) == active[b], (b, int(stats[b]["path"]))
+    # some penalised rows were redone by the general pipeline
+    redone = [b for b in range(B) if active[b] and not stats[b]["path"] & arcs.PATH_RESIDENT]
+    assert redone, [int(x) for x in stats["path"]]
+    logits = to_device_logits(w.logits, w.dtype)
+    hi, ho = hist_to_device(w)
+    got = arcs.sample(logits, arcs.params_to_device(w.params), hi, ho, seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
+
+
 def test_sample_penalties_f32_and_greedy_with_penalty(arcs):
     w = make_workload("zipf_b512_bf16_mixed_penalties", B=16, V=9_001, hist_len=64)
     w.logits = w.logits.astype(np.uint32) << 16
