@@ -80,6 +80,8 @@ def kernel_name(w) -> str:
         return "argmax_fast_kernel" if fits else "argmax_kernel"
     if fits:
         return "sample_summary_kernel"
+    if w.dtype == "f32" and w.V % 4 == 0 and w.V <= 131072 and w.hist_ids is None:
+        return "sample_f32_kernel"
     return "sample_kernel"
 
 

@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     PATH_MINP_FLOOR,
     PATH_PENALTY,
     PATH_RESIDENT,
+    PATH_REREAD,
     PATH_SORT_SKIP,
     PATH_SPECIAL,
     PATH_TIE_SPLIT,

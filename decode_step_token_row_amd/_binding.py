@@ -42,6 +42,7 @@ PATH_TIE_SPLIT = 16
 PATH_PENALTY = 32
 PATH_SPECIAL = 64
 PATH_RESIDENT = 128
+PATH_REREAD = 256
 
 # struct arcs_row_params (32 bytes)
 ROW_PARAMS_DTYPE = np.dtype(

@@ -1547,6 +1547,734 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 kernel
+// ---------------------------------------------------------------------------
+// fp32 rows (16-byte aligned, V % 4 == 0, V <= kF32MaxV, no penalty tables).
+// An fp32 row (517 KB at V = 129,280) does not fit the register file, and its
+// top-p nucleus can hold most of the vocabulary, so the row is read twice:
+//   pass 1 (HBM): the row maximum, the total mass S and, for rows with top-k
+//     or top-p, an LDS histogram of counts and (fixed-point) masses over bins of log2
+//     weight (kFR bins per unit below an origin O set from the first quarter
+//     of the row, O = floor(max * c) + 1 there);
+//   the bin b* where the first filter's target is crossed (top-k count, top-p
+//     mass, or the min-p threshold's bin);
+//   pass 2 (re-read, from cache): per thread the exact mass and count of the
+//     elements in bins above b*, which are kept for sure, and the elements of
+//     b* gathered into LDS as candidates;
+//   the exact cut among the candidates (radix select over their value keys);
+//   the id-order draw: each wave keeps, per round, its total over the 64
+//     groups it read (ids in order: round, wave, lane), a scan of those 512
+//     totals finds the wave-round holding u * S_K, that wave re-reads its 1 KB
+//     of the round and a lane walks its group.
+// Weights are exp2(z * c - O) in fp32 (c = log2(e) / T), summed in fp64 per
+// 4-element group; candidate weights are exact 2^-50 fixed point.  Bins come
+// from one fma of z, so they never decrease as z decreases: bins above b*
+// hold only values above every candidate.  Rows without filters skip pass 2;
+// rows with min-p alone keep z >= the min-p threshold and gather nothing.
+// Special values, masses out of range and candidate sets over kCandCap run
+// the general pipeline in the same workgroup.
+constexpr int kFQ = 32;                                  // 16-byte rounds per thread
+constexpr int kFC = 4;                                   // rounds per chunk (loads in flight per buffer)
+constexpr int kFN = kFQ / kFC;                           // chunks per row
+constexpr int64_t kF32MaxV = (int64_t)kFQ * kNT * 4;     // 131072
+constexpr int kFB = 2048;                                // histogram bins
+constexpr float kFR = 32.0f;                             // bins per unit of log2 weight
+constexpr int kFS = kFQ * kNW;                           // wave-round slots (512)
+static_assert(kFS == 8 * kWave, "the draw's slot scan gives each lane 8 slots");
+// dynamic LDS of the fp32 kernel (bytes):
+//   [0, 8K)     histogram counts u32[kFB]; then the cut's digit counts (sm.hcnt)
+//   [8K, 16K)   histogram masses u32[kFB] (fixed point, per-bin scale); then the
+//               cut's digit masses (sm.hmass, 512 u64)
+//   [16K, 20K)  pass 1 wave-round weight totals f64[kFS] (slot q * kNW + wave)
+//   [20K, 24K)  pass 2 wave-round totals of the elements kept for sure f64[kFS]
+//   [24K, 28K)  wave-round fixed-point mass of kept candidates u64[kFS]
+//   [28K, 76K)  candidates: keys u64[kCandCap], weights f32[kCandCap]
+//   [76K, ...)  tie ids of the cut
+// The general pipeline (fallback) uses [0, kUnionGeneric).
+constexpr size_t kF32OffHmass = (size_t)kFB * 4;
+constexpr size_t kF32OffW1 = kF32OffHmass + (size_t)kFB * 4;
+constexpr size_t kF32OffW2 = kF32OffW1 + (size_t)kFS * 8;
+constexpr size_t kF32OffWfix = kF32OffW2 + (size_t)kFS * 8;
+constexpr size_t kF32OffCand = kF32OffWfix + (size_t)kFS * 8;
+constexpr size_t kF32OffSort = kF32OffCand + (size_t)kCandCap * 12;
+constexpr size_t kF32Lds = kF32OffSort + (size_t)kSmallSort * 12;
+static_assert(kF32OffCand >= kUnionGeneric && kF32OffW1 >= (size_t)kMaxBins * 4 + 512 * 8,
+              "fp32 LDS layout: the cut's digit bins end before the wave-round totals");
+
+__device__ __forceinline__ Smem carve_f32(unsigned char* raw) {
+  Smem sm = carve_smem(raw, false, 0);
+  sm.ckey = (uint64_t*)(raw + kF32OffCand);
+  sm.cw = (float*)(raw + kF32OffCand + (size_t)kCandCap * 8);
+  sm.skey = (uint64_t*)(raw + kF32OffSort);
+  sm.sw = (float*)(raw + kF32OffSort + (size_t)kSmallSort * 8);
+  return sm;
+}
+
+// Chunk c of this thread's rounds: round q = c * kFC + r reads group
+// q * kNT + tid (ids 4 * (q * kNT + tid) .. + 3) through a buffer resource
+// covering the rest of the row; lanes past its end read zeros without a
+// memory access and are masked by the caller.  Default cache policy: the row
+// is read again from cache.
+__device__ __forceinline__ void issue_f32_chunk(const u32x4* rv, int ngroups, int c, u32x4 (&d)[kFC]) {
+  const int voff = threadIdx.x * 16;
+#pragma unroll
+  for (int r = 0; r < kFC; ++r) {
+    const int q = c * kFC + r;
+    const int left = (ngroups - q * kNT) * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(rv + (left > 0 ? q * kNT : 0)), (short)0, left > 0 ? left : 0, 0x00020000);
+    d[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void unpack4(u32x4 d, float (&z)[4]) {
+  z[0] = __uint_as_float(d.x); z[1] = __uint_as_float(d.y);
+  z[2] = __uint_as_float(d.z); z[3] = __uint_as_float(d.w);
+}
+
+// Bin of z: (O - z c) kFR clamped to [0, kFB - 1] (NaN -> 0, -inf -> last).
+// Weights in bin b lie in (2^-(b+1)/kFR, 2^-b/kFR] (bin 0 also holds any above
+// the origin), so the mass histogram stores w * 2^(b/32 + 1 + 13) rounded to
+// an integer, at most 2^14 per element below the origin: a u32 bin holds
+// 2^17 elements.  Integer LDS atomics are far faster than float ones.
+__device__ __forceinline__ uint32_t f32_bin(float z, float ncR, float OR) {
+  float b = __builtin_fmaf(z, ncR, OR);
+  b = __builtin_fmaxf(b, 0.0f);
+  b = __builtin_fminf(b, (float)(kFB - 1));
+  return (uint32_t)b;
+}
+// Only bin 0 can hold weights above 1 (elements above the origin); there
+// an element adds at most 4 (2^16 units) and the caller keeps the excess
+// max(w - 4, 0) aside.
+constexpr int kFMassBits = 13;
+__device__ __forceinline__ uint32_t f32_bin_mass(float w, uint32_t b) {
+  const float x = __builtin_ldexpf(w, (int)(b >> 5) + 1 + kFMassBits) + 0.5f;
+  return (uint32_t)__builtin_fminf(x, 65536.0f);
+}
+__device__ __forceinline__ double f32_bin_mass_value(uint32_t s, int b) {
+  return __builtin_ldexp((double)s, -((b >> 5) + 1 + kFMassBits));
+}
+
+// Chunks 2.. of the row, with chunks 0 and 1 already in flight in d0 / d1:
+// f(d, c) consumes chunk c while the next chunk's loads are in flight.
+template <class F>
+__device__ __forceinline__ void f32_stream_rest(const u32x4* rv, int ngroups, u32x4 (&d0)[kFC], u32x4 (&d1)[kFC],
+                                                F&& f) {
+#pragma unroll
+  for (int c = 0; c < kFN; c += 2) {
+    f(d0, c);
+    if (c + 2 < kFN) issue_f32_chunk(rv, ngroups, c + 2, d0);
+    f(d1, c + 1);
+    if (c + 3 < kFN) issue_f32_chunk(rv, ngroups, c + 3, d1);
+  }
+}
+// The whole row in kFN chunks of kFC rounds, two chunks' loads in flight.
+template <class F>
+__device__ __forceinline__ void f32_stream(const u32x4* rv, int ngroups, u32x4 (&d0)[kFC], u32x4 (&d1)[kFC],
+                                           F&& f) {
+  issue_f32_chunk(rv, ngroups, 0, d0);
+  issue_f32_chunk(rv, ngroups, 1, d1);
+  f32_stream_rest(rv, ngroups, d0, d1, f);
+}
+
+// Row values broadcast through LDS after a pass: per-wave records reduced
+// by every thread in the same order (identical results in all threads).
+// Each call site uses its own slots, so that a wave running ahead into the
+// next reduction cannot overwrite a record another wave has yet to read.
+__device__ __forceinline__ float f32_block_max(float v, float* slots) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = dpp_wave_max_f32(v);
+  if (lane == 0) slots[wid] = v;
+  lds_barrier();
+  float m = slots[0];
+#pragma unroll
+  for (int w = 1; w < kNW; ++w) m = max2f(m, slots[w]);
+  return m;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// This wave's total of one round's group values, stored at slot
+// q * kNW + wave (every lane of the wave calls it).
+__device__ __forceinline__ void f32_round_sum(double* W, int q, float gs) {
+  const double s = dpp_wave_sum_f64((double)gs);
+  if ((threadIdx.x & (kWave - 1)) == 0) W[q * kNW + threadIdx.x / kWave] = s;
+}
+// The sum of the kFS slot totals, the same in every wave.
+__device__ __forceinline__ double f32_slot_total(const double* W) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += W[lane * 8 + i];
+  return dpp_wave_sum_f64(s);
+}
+
+// Greedy rows: the lowest index of the maximum (NaN never wins; -0 = +0;
+// a row of -inf and NaN gives 0).
+__device__ __forceinline__ void f32_greedy(const SampleArgs& a, int64_t row, const u32x4* rv, int ngroups,
+                                           u32x4 (&d0)[kFC], u32x4 (&d1)[kFC], Shared& sh, uint32_t path) {
+  const int tid = threadIdx.x;
+  float best = -__builtin_inff();
+  int bidx = INT_MAX;
+  auto f = [&](const u32x4 (&d)[kFC], int c) {
+#pragma unroll
+    for (int r = 0; r < kFC; ++r) {
+      const int q = c * kFC + r;
+      if (tid < ngroups - q * kNT) {
+        float z[4];
+        unpack4(d[r], z);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (z[e] > best) { best = z[e]; bidx = (q * kNT + tid) * 4 + e; }
+      }
+    }
+  };
+  f32_stream_rest(rv, ngroups, d0, d1, f);  // chunks 0 and 1 are in flight
+  if (tid == 0) sh.i32[5] = INT_MAX;
+  const float m = f32_block_max(best, sh.w_max);
+  if (best == m && bidx != INT_MAX) atomicMin(&sh.i32[5], bidx);
+  lds_barrier();
+  const int64_t id = m == -__builtin_inff() ? 0 : (int64_t)sh.i32[5];
+  path |= ARCS_PATH_GREEDY;
+  if (m == __builtin_inff()) path |= ARCS_PATH_SPECIAL;
+  if (tid == 0) {
+    a.out_ids[row] = (int32_t)id;
+    if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+    if (a.stats) {
+      arcs_row_stats st = {};
+      st.id = (int32_t)id; st.argmax = (int32_t)id; st.kept = 0; st.cut_index = (int32_t)id;
+      st.cut_value = m; st.max_logit = m; st.status = 0; st.path = path;
+      st.mass_total = 0.0; st.mass_kept = 0.0; st.uniform = -1.0;
+      a.stats[row] = st;
+    }
+  }
+  if (a.out_probs)
+    for (int64_t i = tid; i < a.V; i += kNT) a.out_probs[row * a.V + i] = (i == id) ? 1.0f : 0.0f;
+}
+
+// How a sampled row ends after pass 1.
+enum F32Mode : int32_t { kF32Fallback = 0, kF32NoFilter = 1, kF32Thresh = 2, kF32Cand = 3 };
+
+// The draw over the kept set in id order.  W holds each wave-round's kept
+// total (fp64 sums of the sure elements' 4-element fp32 group sums), Wfix
+// (or null) its kept candidates' fixed-point weights (times fscale).  Every
+// wave scans the 512 slot totals (identical results), the wave of the
+// crossing slot re-reads its 64 groups of that round and the crossing lane
+// walks its group.  Kept elements are those `cut` keeps; an element in bin
+// bstar is a candidate (weight from fixed point), one in a bin above it (or
+// any kept element when bstar < 0) weighs its fp32 weight.  Returns the id,
+// or -1 (uniformly) when the kept mass is not positive.
+__device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const double* W, const uint64_t* Wfix,
+                                            double u, const KeepCut& cut, int bstar, float ncR, float OR, float chi,
+                                            float clo, float negO, float cscale, double fscale, Shared& sh,
+                                            double& S_K) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  double vs[8];
+  double ls = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = lane * 8 + i;
+    vs[i] = W[s] + (Wfix ? (double)Wfix[s] * fscale : 0.0);
+    ls += vs[i];
+  }
+  const double incl = dpp_wave_incl_scan_f64(ls);
+  const double tot = readlane63_f64(incl);
+  S_K = tot;
+  if (!(tot > 0.0) || !(tot < 1e300)) return -1;
+  const double t = u * tot;
+  // the lane holding the crossing slot (rounding: the last lane with weight)
+  const uint64_t cross = __ballot(incl > t && ls > 0.0);
+  const uint64_t pos = __ballot(ls > 0.0);
+  const int kl = cross ? __builtin_ctzll(cross) : 63 - __builtin_clzll(pos);
+  // in that lane: the first slot whose running total passes t (rounding:
+  // its last slot with weight) and the running total before it
+  int sl = -1;
+  double acc = incl - ls, sbase = 0.0;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (!found && vs[i] > 0.0) {
+      sl = lane * 8 + i;
+      sbase = acc;
+      acc += vs[i];
+      found = acc > t;
+    }
+  }
+  const int sstar = __builtin_amdgcn_readlane(sl, kl);
+  const double base = readlane_f64(sbase, kl);
+  const int qs = sstar / kNW, ws = sstar % kNW;
+  if (wid == ws) {
+    // lane l takes group qs * kNT + ws * 64 + l (ids in order)
+    const int g = qs * kNT + ws * kWave + lane;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint64_t fx[4] = {0ull, 0ull, 0ull, 0ull};
+    if (g < ngroups) {
+      const u32x4 dd = rv[g];
+      float z[4];
+      unpack4(dd, z);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t idx = (int64_t)g * 4 + e;
+        const float w = wexp(z[e], chi, clo, negO);
+        if (bstar < 0) {
+          s[e] = keep_cut(z[e], idx, cut) ? w : 0.0f;
+        } else {
+          const int b = (int)f32_bin(z[e], ncR, OR);
+          s[e] = b < bstar ? w : 0.0f;
+          fx[e] = (b == bstar && keep_cut(z[e], idx, cut)) ? to_fix50(w * cscale) : 0ull;
+        }
+      }
+    }
+    const float gs = (s[0] + s[1]) + (s[2] + s[3]);
+    const uint64_t cf = (fx[0] + fx[1]) + (fx[2] + fx[3]);
+    const double v = (double)gs + (double)cf * fscale;
+    const double vin = dpp_wave_incl_scan_f64(v);
+    const uint64_t lc = __ballot(base + vin > t && v > 0.0);
+    const uint64_t lp = __ballot(v > 0.0);
+    const int el = lc ? __builtin_ctzll(lc) : (lp ? 63 - __builtin_clzll(lp) : -1);
+    if (el < 0 && lane == 0) sh.u64[15] = ~0ull;
+    if (lane == el) {
+      double a2 = base + vin - v;
+      int64_t id = -1, last = -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double we = s[e] > 0.0f ? (double)s[e] : (double)fx[e] * fscale;
+        if (we > 0.0 && id < 0) {
+          a2 += we;
+          last = (int64_t)g * 4 + e;
+          if (a2 > t) id = last;
+        }
+      }
+      sh.u64[15] = (uint64_t)(id >= 0 ? id : last);
+    }
+  }
+  lds_barrier();
+  return (int64_t)sh.u64[15];
+}
+
+// Pass 1 of a sampled row after the origin is known: chunk 0 (in d0),
+// chunk 1 (in flight in d1) and the chunks after them.  Per group of 4:
+// the maximum, the fp32 weights and their sum (each wave's round total into
+// W1), and with HC / HM the histogram counts / masses (exc: the weight
+// above bin 0's per-element limit).
+template <bool HC, bool HM>
+__device__ __forceinline__ void f32_pass1(const u32x4* rv, int ngroups, u32x4 (&d0)[kFC], u32x4 (&d1)[kFC],
+                                          float chi, float clo, float negO, float ncR, float OR, uint32_t* hc,
+                                          uint32_t* hm, double* W1, float& tmax, float& exc) {
+  const int tid = threadIdx.x;
+  auto weigh = [&](const u32x4 (&d)[kFC], int ch) {
+#pragma unroll
+    for (int r = 0; r < kFC; ++r) {
+      const int q = ch * kFC + r;
+      float gs = 0.0f;
+      if (tid < ngroups - q * kNT) {
+        float z[4];
+        unpack4(d[r], z);
+        tmax = max3f(tmax, max2f(z[0], z[1]), max2f(z[2], z[3]));
+        float w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = wexp(z[e], chi, clo, negO);
+        gs = (w[0] + w[1]) + (w[2] + w[3]);
+        if (HC || HM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t b = f32_bin(z[e], ncR, OR);
+            if (HC) atomicAdd(&hc[b], 1u);
+            if (HM) {
+              atomicAdd(&hm[b], f32_bin_mass(w[e], b));
+              exc += __builtin_fmaxf(w[e] - 4.0f, 0.0f);
+            }
+          }
+        }
+      }
+      f32_round_sum(W1, q, gs);
+    }
+  };
+  f32_stream_rest(rv, ngroups, d0, d1, weigh);
+}
+
+// Pass 2 of a row with candidates: each wave's round totals of the elements
+// in bins above bstar into W2 (kept for sure), the elements of bin bstar
+// gathered into LDS (keys and weights times cscale; their number in
+// sh.i32[5], possibly above kCandCap), and per thread the number of sure
+// elements and of candidates at or above zt.
+__device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, int bstar, float zt, float chi, float clo,
+                                           float negO, float ncR, float OR, float cscale, const Smem& sm, double* W2,
+                                           Shared& sh, uint32_t& cnt, uint32_t& cge) {
+  const int tid = threadIdx.x;
+  u32x4 d0[kFC], d1[kFC];
+  f32_stream(rv, ngroups, d0, d1, [&](const u32x4 (&d)[kFC], int ch) {
+#pragma unroll
+    for (int r = 0; r < kFC; ++r) {
+      const int q = ch * kFC + r;
+      float gs = 0.0f;
+      if (tid < ngroups - q * kNT) {
+        float z[4], s[4];
+        unpack4(d[r], z);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = (int)f32_bin(z[e], ncR, OR);
+          const float w = wexp(z[e], chi, clo, negO);
+          s[e] = b < bstar ? w : 0.0f;
+          cnt += b < bstar ? 1u : 0u;
+          if (b == bstar) {
+            cge += z[e] >= zt ? 1u : 0u;
+            const int slot = atomicAdd(&sh.i32[5], 1);
+            if (slot < kCandCap) {
+              sm.ckey[slot] = cand_key(z[e], (int64_t)(q * kNT + tid) * 4 + e);
+              sm.cw[slot] = w * cscale;
+            }
+          }
+        }
+        gs = (s[0] + s[1]) + (s[2] + s[3]);
+      }
+      f32_round_sum(W2, q, gs);
+    }
+  });
+}
+
+// The sampled row on the fast path.  Returns false (uniformly) when the row
+// needs the general pipeline; nothing is written then.
+__device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
+                                               const RowRng& rng, uint32_t path, unsigned char* smem_raw,
+                                               Shared& sh, u32x4 (&d0)[kFC], u32x4 (&d1)[kFC]) {
+  const int tid = threadIdx.x;
+  const int64_t V = a.V;
+  const int ngroups = (int)(V / 4);
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 4);
+  const bool kon = P.top_k >= 1 && (int64_t)P.top_k < V;
+  const bool pon = P.top_p < 1.0f;
+  const bool mon = P.min_p > 0.0f;
+  const bool nofilter = !kon && !pon && !mon;
+  const bool hist = kon || pon;
+  path |= ARCS_PATH_REREAD;
+  const Smem sm = carve_f32(smem_raw);
+  uint32_t* hc = (uint32_t*)smem_raw;
+  uint32_t* hm = (uint32_t*)(smem_raw + kF32OffHmass);
+  double* W1 = (double*)(smem_raw + kF32OffW1);
+  double* W2 = (double*)(smem_raw + kF32OffW2);
+  uint64_t* Wfix = (uint64_t*)(smem_raw + kF32OffWfix);
+
+  // c = log2(e) / T = chi + clo, chi rounded down, clo > 0 (weights and bins
+  // never decrease with z)
+  const double c = 1.4426950408889634 / (double)P.temperature;
+  if (!(c >= 1e-30 && c <= 1e30)) return false;
+  float chi = (float)c;
+  if ((double)chi >= c) chi = key_value(ord_key(chi) - 1u);
+  float clo = (float)(c - (double)chi);
+  if (!(clo > 0.0f)) clo = 1e-30f;
+  chi = uniform_f32(chi);
+  clo = uniform_f32(clo);
+  const double tdl = mon ? uniform_f64((double)P.temperature * log((double)P.min_p)) : 0.0;
+  double u;
+  if (rng.override_on) {
+    u = rng.u_override;
+  } else {
+    const uint64_t x = splitmix64_counter_output(rng.seed, (uint64_t)row, rng.step);
+    u = (double)(x >> 11) * 0x1p-53;
+  }
+  u = uniform_f64(u);
+
+  if (hist)
+    for (int i = tid; i < kFB; i += kNT) { hc[i] = 0u; hm[i] = 0u; }
+  // ---- pass 1: the origin from chunk 0's maximum, then weights, sums, bins --
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < kFC; ++r) {
+    if (tid < ngroups - r * kNT) {
+      float z[4];
+      unpack4(d0[r], z);
+      tmax = max3f(tmax, max2f(z[0], z[1]), max2f(z[2], z[3]));
+    }
+  }
+  const float mA = f32_block_max(tmax, sh.w_negk);
+  const double Od = __builtin_floor((double)mA * c) + 1.0;
+  if (!(Od > -8388608.0 && Od < 8388608.0)) return false;
+  const float negO = uniform_f32((float)-Od);
+  const float OR = uniform_f32((float)(Od * (double)kFR));
+  const float ncR = uniform_f32(-(float)(c * (double)kFR));
+  float exc = 0.0f;
+  if (kon && pon) f32_pass1<true, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else if (kon) f32_pass1<true, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else if (pon) f32_pass1<false, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else f32_pass1<false, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  if (pon) {
+    const double we = dpp_wave_sum_f64((double)exc);
+    if ((tid & (kWave - 1)) == 0) sh.w_sum[tid / kWave] = we;
+  }
+  const float m = f32_block_max(tmax, sh.w_max);
+  const double S = f32_slot_total(W1);
+  if (!(m > -__builtin_inff() && m < __builtin_inff()) || !(S > 0.0 && S < 1e300)) return false;
+  const float tm = wexp(m, chi, clo, negO);  // the maximum's weight (> 1/2 unless m lies above O)
+  if (!(tm > 0.0f && tm < 1e30f)) return false;
+  int ex = 0;
+  if (tm >= 1.0f) (void)__builtin_frexpf(tm, &ex);
+  const float cscale = __builtin_ldexpf(1.0f, -ex);    // candidate weights * cscale < 1
+  const double fscale = __builtin_ldexp(1.0, ex - 50);  // 2^-50 fixed point back to the O frame
+
+  int32_t mode = nofilter ? kF32NoFilter : (hist ? kF32Cand : kF32Thresh);
+  int bstar = -1;
+  float zt = -__builtin_inff();
+  if (mon) {
+    bool ok;
+    zt = minp_threshold(m, tdl, ok);
+    if (!ok) return false;
+  }
+  if (mode == kF32Cand) {
+    // wave 0: the first bin (from the top) where the top-k count or the
+    // top-p mass target is reached; lane l sums bins 32l .. 32l + 31
+    constexpr int PER = kFB / kWave;
+    const int lane = tid & (kWave - 1);
+    if (tid < kWave) {
+      const double Pm = pon ? (double)P.top_p * S : 0.0;
+      uint32_t lc = 0;
+      double lm = 0.0, exc0 = 0.0;
+      if (pon) {
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) exc0 += sh.w_sum[w];
+      }
+#pragma unroll 8
+      for (int j = 0; j < PER; ++j) {
+        lc += hc[lane * PER + j];
+        lm += f32_bin_mass_value(hm[lane * PER + j], lane * PER + j);
+      }
+      if (lane == 0) lm += exc0;
+      const uint32_t ic = dpp_wave_incl_scan_u32(lc);
+      const double im = dpp_wave_incl_scan_f64(lm);
+      const uint64_t hk = __ballot(kon && ic >= (uint32_t)P.top_k);
+      const uint64_t hp = __ballot(pon && im >= Pm);
+      if (lane == 0) { sh.i32[6] = kFB; sh.i32[7] = kFB; }
+      if (hk && lane == __builtin_ctzll(hk)) {
+        uint32_t cc = ic - lc;
+        int bk = lane * PER + PER - 1;
+        for (int j = 0; j < PER; ++j) {
+          cc += hc[lane * PER + j];
+          if (cc >= (uint32_t)P.top_k) { bk = lane * PER + j; break; }
+        }
+        sh.i32[6] = bk;
+      }
+      if (hp && lane == __builtin_ctzll(hp)) {
+        double cm = im - lm + (lane == 0 ? exc0 : 0.0);
+        int bp = lane * PER + PER - 1;
+        for (int j = 0; j < PER; ++j) {
+          cm += f32_bin_mass_value(hm[lane * PER + j], lane * PER + j);
+          if (cm >= Pm) { bp = lane * PER + j; break; }
+        }
+        sh.i32[7] = bp;
+      }
+    }
+    lds_barrier();
+    const int bk = kon ? sh.i32[6] : kFB;
+    const int bp = pon ? sh.i32[7] : kFB;
+    const int bm = mon ? (int)f32_bin(zt, ncR, OR) : kFB;
+    bstar = bk < bp ? bk : bp;
+    bstar = bm < bstar ? bm : bstar;
+    // no crossing found (top-p alone, its float masses short of the target
+    // by rounding)
+    if (bstar >= kFB) return false;
+  }
+
+  // ---- pass 2: sure masses per thread, candidates of bin b* ---------------------
+  KeepCut cut;
+  cut.th = 0u;
+  cut.istar = INT64_MAX;
+  int64_t L = V;
+  if (mode != kF32NoFilter) {
+    uint32_t cnt = 0;  // elements kept for sure
+    uint32_t cge = 0;  // candidates at or above the min-p threshold
+    if (mode == kF32Thresh) {
+      cut.th = ord_key(zt);
+      f32_stream(rv, ngroups, d0, d1, [&](const u32x4 (&d)[kFC], int ch) {
+#pragma unroll
+        for (int r = 0; r < kFC; ++r) {
+          const int q = ch * kFC + r;
+          float gs = 0.0f;
+          if (tid < ngroups - q * kNT) {
+            float z[4], s[4];
+            unpack4(d[r], z);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool k = z[e] >= zt;
+              s[e] = k ? wexp(z[e], chi, clo, negO) : 0.0f;
+              cnt += k ? 1u : 0u;
+            }
+            gs = (s[0] + s[1]) + (s[2] + s[3]);
+          }
+          f32_round_sum(W2, q, gs);
+        }
+      });
+      path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
+      __syncthreads();
+      L = (int64_t)block_sum_u64(cnt, sh.bs);
+    } else {
+      // The histogram places b* from rounded masses; the exact sums decide.
+      // A crossing found one bin off (the target within rounding of a bin
+      // edge) moves b* by one bin and gathers again, once.  (Written as a
+      // second call rather than a loop: a loop lets the compiler hoist the
+      // rounds' load descriptors out of it and spill.)
+      path |= ARCS_PATH_CUTOFF;
+      const int bm = mon ? (int)f32_bin(zt, ncR, OR) : kFB;
+      // returns 0 when the cut is found, -1 / +1 when the crossing lies one
+      // bin above / below b*, 2 when the row needs the general pipeline
+      auto try_cut = [&]() -> int {
+        cnt = 0;
+        cge = 0;
+        if (tid == 0) sh.i32[5] = 0;
+        if (tid < kFS) Wfix[tid] = 0ull;
+        lds_barrier();
+        f32_gather(rv, ngroups, bstar, zt, chi, clo, negO, ncR, OR, cscale, sm, W2, sh, cnt, cge);
+        __syncthreads();
+        const int nc = sh.i32[5];
+        const double A = f32_slot_total(W2);
+        const uint64_t sums = block_sum_u64((uint64_t)cnt | ((uint64_t)cge << 32), sh.bs);
+        const uint32_t above = (uint32_t)sums;
+        L = (int64_t)above;
+        if (nc > kCandCap) return 2;
+        const bool binding_m = bstar == bm;
+        // step: 0 done, -1 the crossing lies above b*, +1 below it
+        int step = 0;
+        const double need = pon ? ((double)P.top_p * S - A) * (double)cscale : 0.0;
+        if (pon && !(need > 0.0)) {
+          step = -1;
+        } else if (mon && (sums >> 32) == 0) {
+          // no candidate reaches the min-p threshold (b* is its bin): the kept
+          // set is the sure set, exactly the elements at or above it (top-k
+          // and top-p keep at least one candidate more, so min-p binds)
+          if (!binding_m) return 2;
+          cut.th = ord_key(zt);
+          path |= ARCS_PATH_MINP_FLOOR;
+        } else if (nc == 0) {
+          step = 1;
+        } else {
+          int64_t Lc = 0;
+          double kmass = 0.0;
+          if (!large_cut_select(sm, sh, nc, 0, kon, kon ? P.top_k - (int)above : 0, pon, need, mon, zt, cut, Lc,
+                                kmass, pon)) {
+            step = 1;  // only top-p can miss its target here
+          } else {
+            L += Lc;
+            if (cut.istar != INT64_MAX) path |= ARCS_PATH_TIE_SPLIT;
+            if (binding_m) path |= ARCS_PATH_MINP_FLOOR;
+            // kept candidates' fixed-point weights, summed per wave-round slot
+            // (group g = idx / 4 is read in round g / kNT by wave (g % kNT) / 64)
+#pragma unroll
+            for (int r = 0; r < kCandCap / kNT; ++r) {
+              const int i = tid + r * kNT;
+              if (i < nc) {
+                const uint64_t k = sm.ckey[i];
+                const uint32_t idx = (uint32_t)k;
+                const float z = key_value(~(uint32_t)(k >> 32));
+                const uint32_t g = idx >> 2;
+                if (keep_cut(z, (int64_t)idx, cut))
+                  atomicAdd((unsigned long long*)&Wfix[(g / kNT) * kNW + (g % kNT) / kWave],
+                            (unsigned long long)to_fix50(sm.cw[i]));
+              }
+            }
+          }
+        }
+        return step;
+      };
+      int st = try_cut();
+      if (st == 1 || st == -1) {
+        bstar += st;
+        st = 2;
+        if (bstar >= 0 && bstar < kFB) {
+          __syncthreads();
+          st = try_cut();
+        }
+      }
+      if (st != 0) return false;
+      lds_barrier();
+    }
+  } else {
+    path |= ARCS_PATH_SORT_SKIP;
+  }
+  double S_K = 0.0;
+  const int64_t id = f32_draw(rv, ngroups, mode == kF32NoFilter ? W1 : W2, mode == kF32Cand ? Wfix : nullptr, u,
+                              cut, mode == kF32Cand ? bstar : -1, ncR, OR, chi, clo, negO, cscale, fscale, sh, S_K);
+  if (id < 0) return false;
+  if (tid == 0) {
+    a.out_ids[row] = (int32_t)id;
+    if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+  }
+  // ---- debug outputs ------------------------------------------------------------
+  if (a.stats || a.out_probs) {
+    const double inv_sk = 1.0 / S_K;
+    uint32_t kmin = 0xFFFFFFFFu;
+    int64_t kmin_idx = -1;
+    int amin = INT_MAX;
+    for (int g = tid; g < ngroups; g += kNT) {
+      float z[4];
+      unpack4(rv[g], z);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t idx = (int64_t)g * 4 + e;
+        const bool kept = keep_cut(z[e], idx, cut);
+        if (a.out_probs)
+          a.out_probs[row * V + idx] = kept ? (float)((double)wexp(z[e], chi, clo, negO) * inv_sk) : 0.0f;
+        if (kept) {
+          const uint32_t k = ord_key(z[e]);
+          if (k < kmin || (k == kmin && idx > kmin_idx)) { kmin = k; kmin_idx = idx; }
+        }
+        if (z[e] == m && amin == INT_MAX) amin = (int)idx;
+      }
+    }
+    if (a.stats) {
+      if (tid == 0) { sh.u64[9] = ~0ull; sh.i32[5] = INT_MAX; }
+      __syncthreads();
+      const uint64_t packed =
+          ((uint64_t)kmin << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(kmin_idx < 0 ? 0 : kmin_idx));
+      if (kmin_idx >= 0) atomicMin((unsigned long long*)&sh.u64[9], (unsigned long long)packed);
+      if (amin != INT_MAX) atomicMin(&sh.i32[5], amin);
+      __syncthreads();
+      if (tid == 0) {
+        const uint64_t pk = sh.u64[9];
+        arcs_row_stats st = {};
+        st.id = (int32_t)id; st.argmax = sh.i32[5]; st.kept = (int32_t)L;
+        st.cut_index = (int32_t)(0xFFFFFFFFu - (uint32_t)(pk & 0xFFFFFFFFu));
+        st.cut_value = key_value((uint32_t)(pk >> 32));
+        st.max_logit = m; st.status = 0; st.path = path;
+        st.mass_total = S / (double)tm;
+        st.mass_kept = S_K / (double)tm;
+        st.uniform = u;
+        a.stats[row] = st;
+      }
+    }
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(kNT) void sample_f32_kernel(SampleArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  __shared__ Shared sh;
+  const int64_t row = blockIdx.x;
+  const int ngroups = (int)(a.V / 4);
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 4);
+  arcs_row_params P = a.params[row];
+  const RowRng rng = load_row_rng(a, row);
+  u32x4 d0[kFC], d1[kFC];
+  __builtin_amdgcn_sched_barrier(0);
+  issue_f32_chunk(rv, ngroups, 0, d0);
+  issue_f32_chunk(rv, ngroups, 1, d1);
+  __builtin_amdgcn_sched_barrier(0);
+  const Smem smg = carve_smem(smem_raw, false, 0);
+  PenCtx pc;
+  uint32_t path;
+  if (!row_prologue<false, false>(a, row, smg, sh, P, pc, path)) return;
+  if (P.temperature == 0.0f || P.top_k == 1) {
+    f32_greedy(a, row, rv, ngroups, d0, d1, sh, path);
+    return;
+  }
+  if (!f32_sample_row(a, row, P, rng, path, smem_raw, sh, d0, d1)) {
+    __syncthreads();
+    generic_row<false, true>(a, row, P, pc, path, smg, sh);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 template <class Kern>
@@ -1569,6 +2297,17 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hi
     const size_t lds = sample_lds_bytes(true, pen, a.V);
     return pen ? launch_one(sample_summary_kernel<true>, true, a, B, lds, stream, done[0])
                : launch_one(sample_summary_kernel<false>, true, a, B, lds, stream, done[1]);
+  }
+  if (dtype == ARCS_DTYPE_F32 && vec && !pen && a.V <= kF32MaxV && a.V % 4 == 0) {
+    static std::atomic<int> f32_done{0};
+    if (!f32_done.load(std::memory_order_acquire)) {
+      hipError_t e = hipFuncSetAttribute((const void*)sample_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)kF32Lds);
+      if (e != hipSuccess) return e;
+      f32_done.store(1, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(sample_f32_kernel, dim3((unsigned)B), dim3(kNT), kF32Lds, stream, a);
+    return hipGetLastError();
   }
   const size_t lds = sample_lds_bytes(false, pen, a.V);
   if (dtype == ARCS_DTYPE_BF16) {

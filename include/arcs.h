@@ -126,7 +126,8 @@ enum {
   ARCS_PATH_TIE_SPLIT = 16u,  /* the boundary value's ties were split by id    */
   ARCS_PATH_PENALTY = 32u,    /* penalties applied                             */
   ARCS_PATH_SPECIAL = 64u,    /* special values (all -inf, +inf or NaN) seen   */
-  ARCS_PATH_RESIDENT = 128u   /* the row was kept in registers (single HBM read) */
+  ARCS_PATH_RESIDENT = 128u,  /* the row was kept in registers (single HBM read) */
+  ARCS_PATH_REREAD = 256u     /* fp32 row: one HBM read, then one re-read from cache */
 };
 
 /*

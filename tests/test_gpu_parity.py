@@ -626,6 +626,57 @@ def test_full_flat_b1024_f32_sampled_rows(arcs):
     _compare_rows(ids[rows], stats[rows], refs, "flat_b1024_f32")
     kept = stats["kept"]
     assert kept.min() > 10_000  # the nucleus spans tens of thousands of tokens
+    # every row on the two-read fp32 path (none redone by the general pipeline),
+    # including rows whose top-p crossing lies within rounding of a bin edge
+    # (row 1022) and rows whose maximum lies far above the first chunk's
+    assert np.all(stats["path"] & arcs.PATH_REREAD), np.nonzero((stats["path"] & arcs.PATH_REREAD) == 0)[0]
+
+
+def test_f32_two_read_path_edge_rows(arcs):
+    """fp32 rows on the two-read path: maxima far above the first chunk's
+    (the histogram origin) with top-p alone, top-p at several levels, top-k
+    deep in the row, min-p binding with no candidate reaching it, top-k with
+    ties at the cut, and rows of equal values."""
+    B, V = 32, 129_280
+    w = make_workload("flat_b1024_f32_t1_p0.95", B=B, V=V, seed=9, step=4)
+    z = w.logits.copy()
+    rng = np.random.default_rng(17)
+    p = make_params(B, temperature=1.0)
+    for b in range(B):
+        mode = b % 8
+        if mode in (0, 1):
+            # a maximum late in the row, several units above everything else
+            z[b, 100_000 + b] = z[b].max() + 3.0 + b * 0.25
+            p[b]["top_p"] = [0.95, 0.5][mode]
+            p[b]["temperature"] = [1.0, 0.6][mode]
+        elif mode == 2:
+            p[b]["top_p"] = float(rng.uniform(0.05, 0.999))
+        elif mode == 3:
+            p[b]["top_k"] = int(rng.integers(20_000, 120_000))
+            p[b]["temperature"] = float(rng.uniform(0.5, 1.5))
+        elif mode == 4:
+            p[b]["min_p"] = float(rng.uniform(0.001, 0.3))
+            p[b]["top_k"] = int(rng.integers(50, 5000))
+        elif mode == 5:
+            # ties at the top-k cut: values rounded to a coarse grid
+            z[b] = np.round(z[b] * 8.0) / 8.0
+            p[b]["top_k"] = int(rng.integers(10, 3000))
+        elif mode == 6:
+            z[b] = 0.75  # every value equal
+            p[b]["top_p"] = 0.3
+        else:
+            p[b]["top_p"] = 0.9
+            p[b]["min_p"] = 0.02
+            p[b]["temperature"] = 0.35
+    w.logits = z.astype(np.float32)
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "f32 edge rows")
+    # rows whose cut bin holds at most 4096 elements stay on the two-read path
+    # (the grid and equal-value rows may exceed it and take the general one)
+    fast = [b for b in range(B) if b % 8 not in (5, 6)]
+    assert np.all(stats["path"][fast] & arcs.PATH_REREAD), [(b, int(stats[b]["path"])) for b in fast]
 
 
 def test_id_mismatch_rate_over_100k_rows(arcs):
