@@ -1620,7 +1620,10 @@ __device__ __forceinline__ void issue_f32_chunk(const u32x4* rv, int ngroups, in
 #pragma unroll
   for (int r = 0; r < kFC; ++r) {
     const int q = c * kFC + r;
-    const int left = (ngroups - q * kNT) * 16;
+    // the round's descriptor is formed here, not hoisted: 32 rounds of
+    // descriptors held at once would crowd out the scalar registers
+    int left = (ngroups - q * kNT) * 16;
+    asm volatile("" : "+s"(left));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rv + (left > 0 ? q * kNT : 0)), (short)0, left > 0 ? left : 0, 0x00020000);
     d[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
