@@ -72,6 +72,7 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   a.scale = (float)((double)(int64_t(1) << a.F));
   a.pen_tables = (hist_ids != nullptr && V <= ARCS_MAX_PENALTY_VOCAB) ? 1 : 0;
   a.bitmap_words = a.pen_tables ? (uint32_t)((V + 31) / 32) : 0u;
+  a.deferred_only = 0;
   hipError_t e = arcs::launch_sample(a, dtype, B, rows_16b_aligned(logits, dtype, row_stride),
                                      (hipStream_t)stream);
   return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;

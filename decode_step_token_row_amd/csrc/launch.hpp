@@ -29,7 +29,12 @@ struct SampleArgs {
   float scale;         // 2^F
   int pen_tables;      // LDS penalty tables present in this launch
   uint32_t bitmap_words;
+  int deferred_only;   // general kernel: only rows whose out_ids holds kDeferredId
 };
+
+// out_ids value the fp32 kernel leaves for a row it hands to the general
+// kernel launched after it on the same stream (never a valid id or status).
+constexpr int32_t kDeferredId = INT32_MIN;
 
 hipError_t launch_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
                          bool vec, int32_t* out, hipStream_t stream);

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
+  if (a.deferred_only && a.out_ids[row] != kDeferredId) return;
   const Smem sm = carve_smem(smem_raw, false, a.bitmap_words);
   arcs_row_params P = a.params[row];
   PenCtx pc;
@@ -519,16 +520,17 @@ __device__ __forceinline__ int small_cut_draw(const SampleArgs& a, int64_t row, 
 constexpr double kFixScale = 1125899906842624.0;  // 2^50: weights < 2, at most 4096 of them
 __device__ __forceinline__ uint64_t to_fix50(float w) { return (uint64_t)((double)w * kFixScale); }
 
+template <int NT = kNT>
 __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int nc, int lowbit, bool kon, int top_k,
                                                  bool pon, double Pm, bool minp_complete, float zt, KeepCut& cut,
                                                  int64_t& L, double& kept_mass,
                                                  bool track_mass) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  constexpr int ENT = kCandCap / kNT;
+  constexpr int ENT = kCandCap / NT;
   uint32_t* hc = sm.hcnt;
   uint64_t* hm = sm.hmass;
   constexpr uint64_t NONE = ~0ull;
-  for (int i = tid; i < 512; i += kNT) { hc[i] = 0u; hm[i] = 0ull; }
+  for (int i = tid; i < 512; i += NT) { hc[i] = 0u; hm[i] = 0ull; }
   if (tid == 0) { sh.u64[13] = 0ull; sh.u64[14] = 0ull; sh.i32[1] = INT_MIN; sh.i32[2] = INT_MAX; }
   __syncthreads();
   // the span of the value keys: min and max (as int atomics on flipped keys)
@@ -536,7 +538,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int r = 0; r < ENT; ++r) {
-      const int i = tid + r * kNT;
+      const int i = tid + r * NT;
       if (i < nc) {
         const uint32_t vk = ~(uint32_t)(sm.ckey[i] >> 32);
         kmin = vk < kmin ? vk : kmin;
@@ -555,7 +557,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     uint32_t c = 0;
 #pragma unroll
     for (int r = 0; r < ENT; ++r) {
-      const int i = tid + r * kNT;
+      const int i = tid + r * NT;
       if (i < nc && key_value(~(uint32_t)(sm.ckey[i] >> 32)) >= zt) ++c;
     }
     const uint32_t wc = dpp_wave_sum_u32(c);
@@ -577,7 +579,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     const uint32_t dmask = (1u << (top - shf + 1)) - 1u;
 #pragma unroll
     for (int r = 0; r < ENT; ++r) {
-      const int i = tid + r * kNT;
+      const int i = tid + r * NT;
       if (i < nc) {
         const uint32_t vk = ~(uint32_t)(sm.ckey[i] >> 32);
         if (top == 31 || (vk >> (top + 1)) == (pref >> (top + 1))) {
@@ -636,7 +638,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     uint64_t m = 0;
 #pragma unroll
     for (int r = 0; r < ENT; ++r) {
-      const int i = tid + r * kNT;
+      const int i = tid + r * NT;
       if (i < nc) m += to_fix50(sm.cw[i]);
     }
     m = wave_sum_u64(m);
@@ -673,7 +675,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     uint32_t* ids = (uint32_t*)sm.skey;
 #pragma unroll
     for (int q = 0; q < ENT; ++q) {
-      const int i = tid + q * kNT;
+      const int i = tid + q * NT;
       if (i < nc) {
         const uint64_t k = sm.ckey[i];
         if (~(uint32_t)(k >> 32) == th) {
@@ -699,7 +701,7 @@ __device__ __forceinline__ bool large_cut_select(const Smem& sm, Shared& sh, int
     for (int lev = 0; lev < 2; ++lev) {
 #pragma unroll
       for (int q = 0; q < ENT; ++q) {
-        const int i = tid + q * kNT;
+        const int i = tid + q * NT;
         if (i < nc) {
           const uint64_t k = sm.ckey[i];
           const uint32_t id = (uint32_t)k;
@@ -1571,34 +1573,41 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
 // from one fma of z, so they never decrease as z decreases: bins above b*
 // hold only values above every candidate.  Rows without filters skip pass 2;
 // rows with min-p alone keep z >= the min-p threshold and gather nothing.
-// Special values, masses out of range and candidate sets over kCandCap run
-// the general pipeline in the same workgroup.
-constexpr int kFQ = 32;                                  // 16-byte rounds per thread
+// Rows it cannot finish (special values, masses out of range, candidate sets
+// over kCandCap, a crossing more than one bin off) are left as kDeferredId in
+// out_ids for the general kernel launched right after it, which skips every
+// other row: inlined here, the general pipeline's register needs pushed this
+// kernel into spills.
+constexpr int kFT = 512;                                 // threads per row: two rows share a CU
+constexpr int kFW = kFT / kWave;                         // waves per row (8)
+constexpr int kFQ = 64;                                  // 16-byte rounds per thread
 constexpr int kFC = 4;                                   // rounds per chunk (loads in flight per buffer)
 constexpr int kFN = kFQ / kFC;                           // chunks per row
-constexpr int64_t kF32MaxV = (int64_t)kFQ * kNT * 4;     // 131072
+constexpr int64_t kF32MaxV = (int64_t)kFQ * kFT * 4;     // 131072
 constexpr int kFB = 2048;                                // histogram bins
 constexpr float kFR = 32.0f;                             // bins per unit of log2 weight
-constexpr int kFS = kFQ * kNW;                           // wave-round slots (512)
+constexpr int kFS = kFQ * kFW;                           // wave-round slots (512)
 static_assert(kFS == 8 * kWave, "the draw's slot scan gives each lane 8 slots");
 // dynamic LDS of the fp32 kernel (bytes):
 //   [0, 8K)     histogram counts u32[kFB]; then the cut's digit counts (sm.hcnt)
 //   [8K, 16K)   histogram masses u32[kFB] (fixed point, per-bin scale); then the
 //               cut's digit masses (sm.hmass, 512 u64)
-//   [16K, 20K)  pass 1 wave-round weight totals f64[kFS] (slot q * kNW + wave)
+//   [16K, 20K)  pass 1 wave-round weight totals f64[kFS] (slot q * kFW + wave)
 //   [20K, 24K)  pass 2 wave-round totals of the elements kept for sure f64[kFS]
 //   [24K, 28K)  wave-round fixed-point mass of kept candidates u64[kFS]
 //   [28K, 76K)  candidates: keys u64[kCandCap], weights f32[kCandCap]
-//   [76K, ...)  tie ids of the cut
-// The general pipeline (fallback) uses [0, kUnionGeneric).
+// The cut's tie ids go to the pass 1 totals' area (free once S is known).
+// Two workgroups (rows) fit one CU's LDS.
 constexpr size_t kF32OffHmass = (size_t)kFB * 4;
 constexpr size_t kF32OffW1 = kF32OffHmass + (size_t)kFB * 4;
 constexpr size_t kF32OffW2 = kF32OffW1 + (size_t)kFS * 8;
 constexpr size_t kF32OffWfix = kF32OffW2 + (size_t)kFS * 8;
 constexpr size_t kF32OffCand = kF32OffWfix + (size_t)kFS * 8;
-constexpr size_t kF32OffSort = kF32OffCand + (size_t)kCandCap * 12;
-constexpr size_t kF32Lds = kF32OffSort + (size_t)kSmallSort * 12;
-static_assert(kF32OffCand >= kUnionGeneric && kF32OffW1 >= (size_t)kMaxBins * 4 + 512 * 8,
+constexpr size_t kF32OffSort = kF32OffW1;
+constexpr size_t kF32Lds = kF32OffCand + (size_t)kCandCap * 12;
+static_assert((size_t)kSmallSort * 12 <= (size_t)kFS * 8, "tie ids fit the pass 1 totals' area");
+static_assert(2 * (kF32Lds + sizeof(Shared)) <= 160 * 1024, "two fp32 rows per CU");
+static_assert(kF32OffW1 >= (size_t)kMaxBins * 4 + 512 * 8,
               "fp32 LDS layout: the cut's digit bins end before the wave-round totals");
 
 __device__ __forceinline__ Smem carve_f32(unsigned char* raw) {
@@ -1611,7 +1620,7 @@ __device__ __forceinline__ Smem carve_f32(unsigned char* raw) {
 }
 
 // Chunk c of this thread's rounds: round q = c * kFC + r reads group
-// q * kNT + tid (ids 4 * (q * kNT + tid) .. + 3) through a buffer resource
+// q * kFT + tid (ids 4 * (q * kFT + tid) .. + 3) through a buffer resource
 // covering the rest of the row; lanes past its end read zeros without a
 // memory access and are masked by the caller.  Default cache policy: the row
 // is read again from cache.
@@ -1620,12 +1629,12 @@ __device__ __forceinline__ void issue_f32_chunk(const u32x4* rv, int ngroups, in
 #pragma unroll
   for (int r = 0; r < kFC; ++r) {
     const int q = c * kFC + r;
-    // the round's descriptor is formed here, not hoisted: 32 rounds of
+    // the round's descriptor is formed here, not hoisted: 64 rounds of
     // descriptors held at once would crowd out the scalar registers
-    int left = (ngroups - q * kNT) * 16;
+    int left = __builtin_amdgcn_readfirstlane((ngroups - q * kFT) * 16);
     asm volatile("" : "+s"(left));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(rv + (left > 0 ? q * kNT : 0)), (short)0, left > 0 ? left : 0, 0x00020000);
+        (void*)(rv + (left > 0 ? q * kFT : 0)), (short)0, left > 0 ? left : 0, 0x00020000);
     d[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
   }
 }
@@ -1691,7 +1700,7 @@ __device__ __forceinline__ float f32_block_max(float v, float* slots) {
   lds_barrier();
   float m = slots[0];
 #pragma unroll
-  for (int w = 1; w < kNW; ++w) m = max2f(m, slots[w]);
+  for (int w = 1; w < kFW; ++w) m = max2f(m, slots[w]);
   return m;
 }
 __device__ __forceinline__ double readlane_f64(double v, int l) {
@@ -1700,11 +1709,24 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+// Block sum over the kFT threads of an fp32 row (every thread gets it).
+__device__ __forceinline__ uint64_t f32_block_sum_u64(uint64_t v, uint64_t* slots) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if (lane == 0) slots[wid] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kFW; ++w) t += slots[w];
+  return t;
+}
+
 // This wave's total of one round's group values, stored at slot
-// q * kNW + wave (every lane of the wave calls it).
+// q * kFW + wave (every lane of the wave calls it).
 __device__ __forceinline__ void f32_round_sum(double* W, int q, float gs) {
   const double s = dpp_wave_sum_f64((double)gs);
-  if ((threadIdx.x & (kWave - 1)) == 0) W[q * kNW + threadIdx.x / kWave] = s;
+  if ((threadIdx.x & (kWave - 1)) == 0) W[q * kFW + threadIdx.x / kWave] = s;
 }
 // The sum of the kFS slot totals, the same in every wave.
 __device__ __forceinline__ double f32_slot_total(const double* W) {
@@ -1726,12 +1748,12 @@ __device__ __forceinline__ void f32_greedy(const SampleArgs& a, int64_t row, con
 #pragma unroll
     for (int r = 0; r < kFC; ++r) {
       const int q = c * kFC + r;
-      if (tid < ngroups - q * kNT) {
+      if (tid < ngroups - q * kFT) {
         float z[4];
         unpack4(d[r], z);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (z[e] > best) { best = z[e]; bidx = (q * kNT + tid) * 4 + e; }
+          if (z[e] > best) { best = z[e]; bidx = (q * kFT + tid) * 4 + e; }
       }
     }
   };
@@ -1755,7 +1777,7 @@ __device__ __forceinline__ void f32_greedy(const SampleArgs& a, int64_t row, con
     }
   }
   if (a.out_probs)
-    for (int64_t i = tid; i < a.V; i += kNT) a.out_probs[row * a.V + i] = (i == id) ? 1.0f : 0.0f;
+    for (int64_t i = tid; i < a.V; i += kFT) a.out_probs[row * a.V + i] = (i == id) ? 1.0f : 0.0f;
 }
 
 // How a sampled row ends after pass 1.
@@ -1808,10 +1830,10 @@ __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const 
   }
   const int sstar = __builtin_amdgcn_readlane(sl, kl);
   const double base = readlane_f64(sbase, kl);
-  const int qs = sstar / kNW, ws = sstar % kNW;
+  const int qs = sstar / kFW, ws = sstar % kFW;
   if (wid == ws) {
-    // lane l takes group qs * kNT + ws * 64 + l (ids in order)
-    const int g = qs * kNT + ws * kWave + lane;
+    // lane l takes group qs * kFT + ws * 64 + l (ids in order)
+    const int g = qs * kFT + ws * kWave + lane;
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     uint64_t fx[4] = {0ull, 0ull, 0ull, 0ull};
     if (g < ngroups) {
@@ -1873,7 +1895,7 @@ __device__ __forceinline__ void f32_pass1(const u32x4* rv, int ngroups, u32x4 (&
     for (int r = 0; r < kFC; ++r) {
       const int q = ch * kFC + r;
       float gs = 0.0f;
-      if (tid < ngroups - q * kNT) {
+      if (tid < ngroups - q * kFT) {
         float z[4];
         unpack4(d[r], z);
         tmax = max3f(tmax, max2f(z[0], z[1]), max2f(z[2], z[3]));
@@ -1914,7 +1936,7 @@ __device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, int bst
     for (int r = 0; r < kFC; ++r) {
       const int q = ch * kFC + r;
       float gs = 0.0f;
-      if (tid < ngroups - q * kNT) {
+      if (tid < ngroups - q * kFT) {
         float z[4], s[4];
         unpack4(d[r], z);
 #pragma unroll
@@ -1927,7 +1949,7 @@ __device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, int bst
             cge += z[e] >= zt ? 1u : 0u;
             const int slot = atomicAdd(&sh.i32[5], 1);
             if (slot < kCandCap) {
-              sm.ckey[slot] = cand_key(z[e], (int64_t)(q * kNT + tid) * 4 + e);
+              sm.ckey[slot] = cand_key(z[e], (int64_t)(q * kFT + tid) * 4 + e);
               sm.cw[slot] = w * cscale;
             }
           }
@@ -1982,12 +2004,12 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   u = uniform_f64(u);
 
   if (hist)
-    for (int i = tid; i < kFB; i += kNT) { hc[i] = 0u; hm[i] = 0u; }
+    for (int i = tid; i < kFB; i += kFT) { hc[i] = 0u; hm[i] = 0u; }
   // ---- pass 1: the origin from chunk 0's maximum, then weights, sums, bins --
   float tmax = -__builtin_inff();
 #pragma unroll
   for (int r = 0; r < kFC; ++r) {
-    if (tid < ngroups - r * kNT) {
+    if (tid < ngroups - r * kFT) {
       float z[4];
       unpack4(d0[r], z);
       tmax = max3f(tmax, max2f(z[0], z[1]), max2f(z[2], z[3]));
@@ -2037,7 +2059,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
       double lm = 0.0, exc0 = 0.0;
       if (pon) {
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) exc0 += sh.w_sum[w];
+        for (int w = 0; w < kFW; ++w) exc0 += sh.w_sum[w];
       }
 #pragma unroll 8
       for (int j = 0; j < PER; ++j) {
@@ -2095,7 +2117,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         for (int r = 0; r < kFC; ++r) {
           const int q = ch * kFC + r;
           float gs = 0.0f;
-          if (tid < ngroups - q * kNT) {
+          if (tid < ngroups - q * kFT) {
             float z[4], s[4];
             unpack4(d[r], z);
 #pragma unroll
@@ -2111,7 +2133,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
       });
       path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
       __syncthreads();
-      L = (int64_t)block_sum_u64(cnt, sh.bs);
+      L = (int64_t)f32_block_sum_u64(cnt, sh.bs.u64);
     } else {
       // The histogram places b* from rounded masses; the exact sums decide.
       // A crossing found one bin off (the target within rounding of a bin
@@ -2122,7 +2144,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
       const int bm = mon ? (int)f32_bin(zt, ncR, OR) : kFB;
       // returns 0 when the cut is found, -1 / +1 when the crossing lies one
       // bin above / below b*, 2 when the row needs the general pipeline
-      auto try_cut = [&]() -> int {
+      auto try_cut = [&]() __attribute__((always_inline)) -> int {
         cnt = 0;
         cge = 0;
         if (tid == 0) sh.i32[5] = 0;
@@ -2132,7 +2154,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         __syncthreads();
         const int nc = sh.i32[5];
         const double A = f32_slot_total(W2);
-        const uint64_t sums = block_sum_u64((uint64_t)cnt | ((uint64_t)cge << 32), sh.bs);
+        const uint64_t sums = f32_block_sum_u64((uint64_t)cnt | ((uint64_t)cge << 32), sh.bs.u64);
         const uint32_t above = (uint32_t)sums;
         L = (int64_t)above;
         if (nc > kCandCap) return 2;
@@ -2154,7 +2176,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         } else {
           int64_t Lc = 0;
           double kmass = 0.0;
-          if (!large_cut_select(sm, sh, nc, 0, kon, kon ? P.top_k - (int)above : 0, pon, need, mon, zt, cut, Lc,
+          if (!large_cut_select<kFT>(sm, sh, nc, 0, kon, kon ? P.top_k - (int)above : 0, pon, need, mon, zt, cut, Lc,
                                 kmass, pon)) {
             step = 1;  // only top-p can miss its target here
           } else {
@@ -2162,17 +2184,17 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
             if (cut.istar != INT64_MAX) path |= ARCS_PATH_TIE_SPLIT;
             if (binding_m) path |= ARCS_PATH_MINP_FLOOR;
             // kept candidates' fixed-point weights, summed per wave-round slot
-            // (group g = idx / 4 is read in round g / kNT by wave (g % kNT) / 64)
+            // (group g = idx / 4 is read in round g / kFT by wave (g % kFT) / 64)
 #pragma unroll
-            for (int r = 0; r < kCandCap / kNT; ++r) {
-              const int i = tid + r * kNT;
+            for (int r = 0; r < kCandCap / kFT; ++r) {
+              const int i = tid + r * kFT;
               if (i < nc) {
                 const uint64_t k = sm.ckey[i];
                 const uint32_t idx = (uint32_t)k;
                 const float z = key_value(~(uint32_t)(k >> 32));
                 const uint32_t g = idx >> 2;
                 if (keep_cut(z, (int64_t)idx, cut))
-                  atomicAdd((unsigned long long*)&Wfix[(g / kNT) * kNW + (g % kNT) / kWave],
+                  atomicAdd((unsigned long long*)&Wfix[(g / kFT) * kFW + (g % kFT) / kWave],
                             (unsigned long long)to_fix50(sm.cw[i]));
               }
             }
@@ -2209,7 +2231,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
     uint32_t kmin = 0xFFFFFFFFu;
     int64_t kmin_idx = -1;
     int amin = INT_MAX;
-    for (int g = tid; g < ngroups; g += kNT) {
+    for (int g = tid; g < ngroups; g += kFT) {
       float z[4];
       unpack4(rv[g], z);
 #pragma unroll
@@ -2250,7 +2272,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   return true;
 }
 
-__global__ __launch_bounds__(kNT) void sample_f32_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kFT, 4) void sample_f32_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   __shared__ Shared sh;
   const int64_t row = blockIdx.x;
@@ -2263,18 +2285,29 @@ __global__ __launch_bounds__(kNT) void sample_f32_kernel(SampleArgs a) {
   issue_f32_chunk(rv, ngroups, 0, d0);
   issue_f32_chunk(rv, ngroups, 1, d1);
   __builtin_amdgcn_sched_barrier(0);
-  const Smem smg = carve_smem(smem_raw, false, 0);
-  PenCtx pc;
-  uint32_t path;
-  if (!row_prologue<false, false>(a, row, smg, sh, P, pc, path)) return;
+  // parameters (rows with history never reach this kernel)
+  const int status = row_param_status(P);
+  if (status != ARCS_ROW_OK) {
+    if (threadIdx.x == 0) {
+      a.out_ids[row] = -1;
+      if (a.out_status) a.out_status[row] = status;
+      if (a.stats) {
+        arcs_row_stats st = {};
+        st.id = -1; st.argmax = -1; st.status = status;
+        a.stats[row] = st;
+      }
+    }
+    if (a.out_probs)
+      for (int64_t i = threadIdx.x; i < a.V; i += kFT) a.out_probs[row * a.V + i] = 0.0f;
+    return;
+  }
+  const uint32_t path = 0u;
   if (P.temperature == 0.0f || P.top_k == 1) {
     f32_greedy(a, row, rv, ngroups, d0, d1, sh, path);
     return;
   }
-  if (!f32_sample_row(a, row, P, rng, path, smem_raw, sh, d0, d1)) {
-    __syncthreads();
-    generic_row<false, true>(a, row, P, pc, path, smg, sh);
-  }
+  if (!f32_sample_row(a, row, P, rng, path, smem_raw, sh, d0, d1) && threadIdx.x == 0)
+    a.out_ids[row] = kDeferredId;
 }
 
 // ---------------------------------------------------------------------------
@@ -2309,8 +2342,14 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hi
       if (e != hipSuccess) return e;
       f32_done.store(1, std::memory_order_release);
     }
-    hipLaunchKernelGGL(sample_f32_kernel, dim3((unsigned)B), dim3(kNT), kF32Lds, stream, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL(sample_f32_kernel, dim3((unsigned)B), dim3(kFT), kF32Lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the rows it handed back (a row's block exits at once otherwise)
+    SampleArgs g = a;
+    g.deferred_only = 1;
+    return launch_one(sample_kernel<false, true, false>, false, g, B, sample_lds_bytes(false, false, a.V), stream,
+                      done[7]);
   }
   const size_t lds = sample_lds_bytes(false, pen, a.V);
   if (dtype == ARCS_DTYPE_BF16) {
