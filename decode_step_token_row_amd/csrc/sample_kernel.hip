@@ -1667,6 +1667,26 @@ __device__ __forceinline__ double f32_bin_mass_value(uint32_t s, int b) {
   return __builtin_ldexp((double)s, -((b >> 5) + 1 + kFMassBits));
 }
 
+// Bin edges as values: E(n) = the largest float z with fma(z, ncR, OR) >= n,
+// so that f32_bin(z) >= n exactly when z <= E(n) (the fma falls as z rises);
+// E(0) = +inf, E(kFB) = -inf.  The 64 lanes of the wave test 64 consecutive
+// floats around the estimate with the same fma; every lane gets the result.
+// ok = false if the edge lies outside the window (never expected).
+__device__ __forceinline__ float f32_bin_edge(int n, float ncR, float OR, bool& ok) {
+  ok = true;
+  if (n <= 0) return __builtin_inff();
+  if (n >= kFB) return -__builtin_inff();
+  const int lane = threadIdx.x & (kWave - 1);
+  const double est = ((double)OR - (double)n) / -(double)ncR;
+  const float z0 = est > (double)FLT_MAX ? FLT_MAX : (est < -(double)FLT_MAX ? -FLT_MAX : (float)est);
+  const uint32_t k0 = ord_key(z0) - 32u;
+  const float zl = key_value(k0 + (uint32_t)lane);
+  const uint64_t ge = __ballot(__builtin_fmaf(zl, ncR, OR) >= (float)n);
+  // true for the low lanes (small z), false above: a non-empty proper prefix
+  ok = ge != 0 && ~ge != 0 && (ge & (ge + 1)) == 0;
+  return key_value(k0 + (uint32_t)(ok ? 63 - __builtin_clzll(ge) : 0));
+}
+
 // Chunks 2.. of the row, with chunks 0 and 1 already in flight in d0 / d1:
 // f(d, c) consumes chunk c while the next chunk's loads are in flight.
 template <class F>
@@ -1790,10 +1810,12 @@ enum F32Mode : int32_t { kF32Fallback = 0, kF32NoFilter = 1, kF32Thresh = 2, kF3
 // crossing slot re-reads its 64 groups of that round and the crossing lane
 // walks its group.  Kept elements are those `cut` keeps; an element in bin
 // bstar is a candidate (weight from fixed point), one in a bin above it (or
-// any kept element when bstar < 0) weighs its fp32 weight.  Returns the id,
+// any kept element when bstar < 0) weighs its fp32 weight; eb / ec are the
+// edges E(bstar) / E(bstar + 1): above eb a bin above bstar, in (ec, eb]
+// bin bstar.  Returns the id,
 // or -1 (uniformly) when the kept mass is not positive.
 __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const double* W, const uint64_t* Wfix,
-                                            double u, const KeepCut& cut, int bstar, float ncR, float OR, float chi,
+                                            double u, const KeepCut& cut, int bstar, float eb, float ec, float chi,
                                             float clo, float negO, float cscale, double fscale, Shared& sh,
                                             double& S_K) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -1847,9 +1869,8 @@ __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const 
         if (bstar < 0) {
           s[e] = keep_cut(z[e], idx, cut) ? w : 0.0f;
         } else {
-          const int b = (int)f32_bin(z[e], ncR, OR);
-          s[e] = b < bstar ? w : 0.0f;
-          fx[e] = (b == bstar && keep_cut(z[e], idx, cut)) ? to_fix50(w * cscale) : 0ull;
+          s[e] = z[e] > eb ? w : 0.0f;
+          fx[e] = (z[e] > ec && !(z[e] > eb) && keep_cut(z[e], idx, cut)) ? to_fix50(w * cscale) : 0ull;
         }
       }
     }
@@ -1922,12 +1943,13 @@ __device__ __forceinline__ void f32_pass1(const u32x4* rv, int ngroups, u32x4 (&
 }
 
 // Pass 2 of a row with candidates: each wave's round totals of the elements
-// in bins above bstar into W2 (kept for sure), the elements of bin bstar
+// in bins above bstar (z > eb) into W2 (kept for sure), the elements of bin
+// bstar (ec < z <= eb)
 // gathered into LDS (keys and weights times cscale; their number in
 // sh.i32[5], possibly above kCandCap), and per thread the number of sure
 // elements and of candidates at or above zt.
-__device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, int bstar, float zt, float chi, float clo,
-                                           float negO, float ncR, float OR, float cscale, const Smem& sm, double* W2,
+__device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, float eb, float ec, float zt, float chi,
+                                           float clo, float negO, float cscale, const Smem& sm, double* W2,
                                            Shared& sh, uint32_t& cnt, uint32_t& cge) {
   const int tid = threadIdx.x;
   u32x4 d0[kFC], d1[kFC];
@@ -1941,11 +1963,11 @@ __device__ __forceinline__ void f32_gather(const u32x4* rv, int ngroups, int bst
         unpack4(d[r], z);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int b = (int)f32_bin(z[e], ncR, OR);
+          const bool sure = z[e] > eb;
           const float w = wexp(z[e], chi, clo, negO);
-          s[e] = b < bstar ? w : 0.0f;
-          cnt += b < bstar ? 1u : 0u;
-          if (b == bstar) {
+          s[e] = sure ? w : 0.0f;
+          cnt += sure ? 1u : 0u;
+          if (z[e] > ec && !sure) {
             cge += z[e] >= zt ? 1u : 0u;
             const int slot = atomicAdd(&sh.i32[5], 1);
             if (slot < kCandCap) {
@@ -2106,6 +2128,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   KeepCut cut;
   cut.th = 0u;
   cut.istar = INT64_MAX;
+  float eb = 0.0f, ec = 0.0f;  // edges of bin b* (candidate rows)
   int64_t L = V;
   if (mode != kF32NoFilter) {
     uint32_t cnt = 0;  // elements kept for sure
@@ -2150,7 +2173,11 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         if (tid == 0) sh.i32[5] = 0;
         if (tid < kFS) Wfix[tid] = 0ull;
         lds_barrier();
-        f32_gather(rv, ngroups, bstar, zt, chi, clo, negO, ncR, OR, cscale, sm, W2, sh, cnt, cge);
+        bool eok, cok;
+        eb = f32_bin_edge(bstar, ncR, OR, eok);
+        ec = f32_bin_edge(bstar + 1, ncR, OR, cok);
+        if (!eok || !cok) return 2;
+        f32_gather(rv, ngroups, eb, ec, zt, chi, clo, negO, cscale, sm, W2, sh, cnt, cge);
         __syncthreads();
         const int nc = sh.i32[5];
         const double A = f32_slot_total(W2);
@@ -2219,7 +2246,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   }
   double S_K = 0.0;
   const int64_t id = f32_draw(rv, ngroups, mode == kF32NoFilter ? W1 : W2, mode == kF32Cand ? Wfix : nullptr, u,
-                              cut, mode == kF32Cand ? bstar : -1, ncR, OR, chi, clo, negO, cscale, fscale, sh, S_K);
+                              cut, mode == kF32Cand ? bstar : -1, eb, ec, chi, clo, negO, cscale, fscale, sh, S_K);
   if (id < 0) return false;
   if (tid == 0) {
     a.out_ids[row] = (int32_t)id;
