@@ -2063,7 +2063,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   const double fscale = __builtin_ldexp(1.0, ex - 50);  // 2^-50 fixed point back to the O frame
 
   int32_t mode = nofilter ? kF32NoFilter : (hist ? kF32Cand : kF32Thresh);
-  int bstar = -1;
+  int bstar = -1, bhi = -1;  // candidate rows: the bins gathered, bstar .. bhi
   float zt = -__builtin_inff();
   if (mon) {
     bool ok;
@@ -2103,14 +2103,19 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         }
         sh.i32[6] = bk;
       }
+      if (lane == 0) sh.i32[3] = 0;
       if (hp && lane == __builtin_ctzll(hp)) {
-        double cm = im - lm + (lane == 0 ? exc0 : 0.0);
+        double cm = im - lm + (lane == 0 ? exc0 : 0.0), before = cm;
         int bp = lane * PER + PER - 1;
         for (int j = 0; j < PER; ++j) {
+          before = cm;
           cm += f32_bin_mass_value(hm[lane * PER + j], lane * PER + j);
           if (cm >= Pm) { bp = lane * PER + j; break; }
         }
         sh.i32[7] = bp;
+        // the target within the masses' rounding of an edge of the bin: the
+        // neighbouring bin is gathered too (1: the bin above, 2: below)
+        sh.i32[3] = (Pm - before <= 2e-5 * Pm ? 1 : 0) | (cm - Pm <= 2e-5 * Pm ? 2 : 0);
       }
     }
     lds_barrier();
@@ -2122,6 +2127,12 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
     // no crossing found (top-p alone, its float masses short of the target
     // by rounding)
     if (bstar >= kFB) return false;
+    bhi = bstar;
+    if (pon && bstar == bp) {
+      const int near = sh.i32[3];
+      if ((near & 1) && bstar > 0) bstar -= 1;
+      if ((near & 2) && bhi < kFB - 1) bhi += 1;
+    }
   }
 
   // ---- pass 2: sure masses per thread, candidates of bin b* ---------------------
@@ -2175,7 +2186,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         lds_barrier();
         bool eok, cok;
         eb = f32_bin_edge(bstar, ncR, OR, eok);
-        ec = f32_bin_edge(bstar + 1, ncR, OR, cok);
+        ec = f32_bin_edge(bhi + 1, ncR, OR, cok);
         if (!eok || !cok) return 2;
         f32_gather(rv, ngroups, eb, ec, zt, chi, clo, negO, cscale, sm, W2, sh, cnt, cge);
         __syncthreads();
@@ -2185,7 +2196,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
         const uint32_t above = (uint32_t)sums;
         L = (int64_t)above;
         if (nc > kCandCap) return 2;
-        const bool binding_m = bstar == bm;
+        const bool binding_m = bm >= bstar && bm <= bhi;
         // step: 0 done, -1 the crossing lies above b*, +1 below it
         int step = 0;
         const double need = pon ? ((double)P.top_p * S - A) * (double)cscale : 0.0;
@@ -2231,7 +2242,8 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
       };
       int st = try_cut();
       if (st == 1 || st == -1) {
-        bstar += st;
+        bstar = st < 0 ? bstar - 1 : bhi + 1;
+        bhi = bstar;
         st = 2;
         if (bstar >= 0 && bstar < kFB) {
           __syncthreads();
