@@ -1551,33 +1551,39 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 kernel
 // ---------------------------------------------------------------------------
-// fp32 rows (16-byte aligned, V % 4 == 0, V <= kF32MaxV, no penalty tables).
-// An fp32 row (517 KB at V = 129,280) does not fit the register file, and its
-// top-p nucleus can hold most of the vocabulary, so the row is read twice:
+// fp32 rows (16-byte aligned, V % 4 == 0, V <= kF32MaxV, no penalty tables),
+// one 512-thread workgroup per row, two rows resident per CU so that one
+// row's cut and draw overlap the other's HBM read.  An fp32 row (517 KB at
+// V = 129,280) does not fit the register file, and its top-p nucleus can hold
+// most of the vocabulary, so the row is read twice:
 //   pass 1 (HBM): the row maximum, the total mass S and, for rows with top-k
-//     or top-p, an LDS histogram of counts and (fixed-point) masses over bins of log2
-//     weight (kFR bins per unit below an origin O set from the first quarter
-//     of the row, O = floor(max * c) + 1 there);
+//     or top-p, an LDS histogram of counts and fixed-point masses over bins of
+//     log2 weight (kFR bins per unit below an origin O = floor(max0 * c) + 1,
+//     max0 the maximum of the first chunk of the row);
 //   the bin b* where the first filter's target is crossed (top-k count, top-p
-//     mass, or the min-p threshold's bin);
-//   pass 2 (re-read, from cache): per thread the exact mass and count of the
-//     elements in bins above b*, which are kept for sure, and the elements of
-//     b* gathered into LDS as candidates;
+//     mass, or the min-p threshold's bin), widened by one bin on the side of a
+//     top-p target that lies within the masses' rounding of the bin's edge;
+//   pass 2 (re-read, from cache): the elements above the gathered bins (kept
+//     for sure: their wave-round totals and count) and the elements of the
+//     gathered bins, placed in LDS as candidates, both told apart by the
+//     bins' value edges;
 //   the exact cut among the candidates (radix select over their value keys);
+//     a crossing found outside the gathered bins moves them by one bin and
+//     gathers again, once;
 //   the id-order draw: each wave keeps, per round, its total over the 64
 //     groups it read (ids in order: round, wave, lane), a scan of those 512
 //     totals finds the wave-round holding u * S_K, that wave re-reads its 1 KB
 //     of the round and a lane walks its group.
 // Weights are exp2(z * c - O) in fp32 (c = log2(e) / T), summed in fp64 per
 // 4-element group; candidate weights are exact 2^-50 fixed point.  Bins come
-// from one fma of z, so they never decrease as z decreases: bins above b*
-// hold only values above every candidate.  Rows without filters skip pass 2;
-// rows with min-p alone keep z >= the min-p threshold and gather nothing.
-// Rows it cannot finish (special values, masses out of range, candidate sets
-// over kCandCap, a crossing more than one bin off) are left as kDeferredId in
-// out_ids for the general kernel launched right after it, which skips every
-// other row: inlined here, the general pipeline's register needs pushed this
-// kernel into spills.
+// from one fma of z, so they never decrease as z decreases: bins above the
+// gathered ones hold only values above every candidate.  Rows without filters
+// skip pass 2; rows with min-p alone keep z >= the min-p threshold and gather
+// nothing.  Rows it cannot finish (special values, masses out of range,
+// candidate sets over kCandCap, a crossing further off) are left as
+// kDeferredId in out_ids for the general kernel launched right after it, which
+// skips every other row: inlined here, the general pipeline's register needs
+// pushed this kernel into spills.
 constexpr int kFT = 512;                                 // threads per row: two rows share a CU
 constexpr int kFW = kFT / kWave;                         // waves per row (8)
 constexpr int kFQ = 64;                                  // 16-byte rounds per thread
@@ -1585,7 +1591,8 @@ constexpr int kFC = 4;                                   // rounds per chunk (lo
 constexpr int kFN = kFQ / kFC;                           // chunks per row
 constexpr int64_t kF32MaxV = (int64_t)kFQ * kFT * 4;     // 131072
 constexpr int kFB = 2048;                                // histogram bins
-constexpr float kFR = 32.0f;                             // bins per unit of log2 weight
+constexpr int kFRLog = 5;                                // 2^kFRLog bins per unit of log2 weight
+constexpr float kFR = (float)(1 << kFRLog);
 constexpr int kFS = kFQ * kFW;                           // wave-round slots (512)
 static_assert(kFS == 8 * kWave, "the draw's slot scan gives each lane 8 slots");
 // dynamic LDS of the fp32 kernel (bytes):
@@ -1646,9 +1653,9 @@ __device__ __forceinline__ void unpack4(u32x4 d, float (&z)[4]) {
 
 // Bin of z: (O - z c) kFR clamped to [0, kFB - 1] (NaN -> 0, -inf -> last).
 // Weights in bin b lie in (2^-(b+1)/kFR, 2^-b/kFR] (bin 0 also holds any above
-// the origin), so the mass histogram stores w * 2^(b/32 + 1 + 13) rounded to
-// an integer, at most 2^14 per element below the origin: a u32 bin holds
-// 2^17 elements.  Integer LDS atomics are far faster than float ones.
+// the origin), so the mass histogram stores w * 2^(floor(b / kFR) + 1 + 13)
+// rounded to an integer, at most 2^14 per element below the origin: a u32 bin
+// holds 2^17 elements.  Integer LDS atomics are far faster than float ones.
 __device__ __forceinline__ uint32_t f32_bin(float z, float ncR, float OR) {
   float b = __builtin_fmaf(z, ncR, OR);
   b = __builtin_fmaxf(b, 0.0f);
@@ -1660,11 +1667,11 @@ __device__ __forceinline__ uint32_t f32_bin(float z, float ncR, float OR) {
 // max(w - 4, 0) aside.
 constexpr int kFMassBits = 13;
 __device__ __forceinline__ uint32_t f32_bin_mass(float w, uint32_t b) {
-  const float x = __builtin_ldexpf(w, (int)(b >> 5) + 1 + kFMassBits) + 0.5f;
+  const float x = __builtin_ldexpf(w, (int)(b >> kFRLog) + 1 + kFMassBits) + 0.5f;
   return (uint32_t)__builtin_fminf(x, 65536.0f);
 }
 __device__ __forceinline__ double f32_bin_mass_value(uint32_t s, int b) {
-  return __builtin_ldexp((double)s, -((b >> 5) + 1 + kFMassBits));
+  return __builtin_ldexp((double)s, -((b >> kFRLog) + 1 + kFMassBits));
 }
 
 // Bin edges as values: E(n) = the largest float z with fma(z, ncR, OR) >= n,
@@ -2139,7 +2146,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   KeepCut cut;
   cut.th = 0u;
   cut.istar = INT64_MAX;
-  float eb = 0.0f, ec = 0.0f;  // edges of bin b* (candidate rows)
+  float eb = 0.0f, ec = 0.0f;  // value edges of the gathered bins (candidate rows)
   int64_t L = V;
   if (mode != kF32NoFilter) {
     uint32_t cnt = 0;  // elements kept for sure
