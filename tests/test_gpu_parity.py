@@ -587,6 +587,52 @@ def test_keyed_sampling_matches_by_value_key_eager_and_in_a_graph(arcs):
         torch.cuda.synchronize()
 
 
+def test_f32_rows_with_deferred_rows_in_a_graph(arcs):
+    """fp32 rows take two kernels per call: the two-read kernel, then the
+    general one for the rows it hands back (here rows with NaN / +inf and an
+    all-equal row whose cut bin overflows the candidate list). Captured with
+    arcs_sample_keyed, every replay gives the eager ids of the next step."""
+    import torch
+    B, V, seed, s0 = 32, 30_000, 99, 2
+    w = make_workload("flat_b1024_f32_t1_p0.95", B=B, V=V, seed=4, step=0)
+    z = w.logits.copy()
+    z[3, 1234] = np.nan
+    z[5, 77] = np.inf
+    z[7] = 0.5
+    w.logits = z.astype(np.float32)
+    p = make_params(B, temperature=1.0, top_p=0.9)
+    p[1::4]["top_k"] = 500
+    p[2::4]["min_p"] = 0.01
+    w.params = p
+    logits = to_device_logits(w.logits, "f32")
+    params = arcs.params_to_device(w.params)
+    want = [arcs.sample(logits, params, seed=seed, step=s0 + i).cpu().numpy() for i in range(6)]
+    # the deferred rows match the oracle too
+    w.seed, w.step = seed, s0
+    ids, _, stats, _ = _run_debug(arcs, w)
+    _compare_rows(ids, stats, _oracle(w), "f32 deferred rows")
+    assert np.array_equal(ids, want[0])
+    assert not stats["path"][7] & arcs.PATH_REREAD and stats["path"][0] & arcs.PATH_REREAD
+    key = arcs.make_key(seed, s0)
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        arcs.sample_keyed(logits, params, key, advance=False, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arcs.sample_keyed(logits, params, key, out=out)
+    for i in range(6):
+        out.fill_(-5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want[i]), i
+        arcs.sample(logits, params, seed=1, step=i)  # eager work in between
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # the named workloads at full size
 # --------------------------------------------------------------------------
