@@ -68,8 +68,8 @@ __host__ __device__ inline size_t pen_prefix_bytes(uint32_t bitmap_words) { retu
 
 // The penalty tables follow the union area of the kernel's path: the general
 // kernel keeps per distinct id its count and its penalised logit; the summary
-// kernel keeps only the penalised logits, its counts live in the candidate
-// area while the tables are built (it is free then).
+// kernel keeps only the counts (its pass penalises each history id from its
+// own logit and count).
 inline size_t sample_lds_bytes(bool summary, bool pen_tables, int64_t V) {
   size_t b = summary ? kUnionSummary : kUnionGeneric;
   if (pen_tables) {
@@ -85,7 +85,8 @@ struct PenCtx {
   float pres, freq, rep;
   const uint32_t* bitmap;
   const uint16_t* wprefix;
-  const float* zpen;
+  const float* zpen;       // general path: penalised logit per distinct id
+  const uint32_t* pcount;  // summary path: occurrence count per distinct id
 };
 
 // Rank of a history id among the row's distinct history ids (id order).
@@ -335,8 +336,11 @@ __device__ __forceinline__ Smem carve_smem(unsigned char* raw, bool summary, uin
   sm.wprefix = (uint16_t*)(pen_base + (size_t)bitmap_words * 4);
   unsigned char* after = pen_base + (size_t)bitmap_words * 4 + pen_prefix_bytes(bitmap_words);
   if (summary) {
-    sm.pcount = (uint32_t*)(raw + kOffCand);  // only while the tables are built
-    sm.zpen = (float*)after;
+    // counts kept for the whole row (the pass penalises from them); the
+    // penalised logits only for a row handed to the general pipeline, in the
+    // candidate area (free then)
+    sm.pcount = (uint32_t*)after;
+    sm.zpen = (float*)(raw + kOffCand);
   } else {
     sm.pcount = (uint32_t*)after;
     sm.zpen = (float*)(after + (size_t)kMaxDistinct * 4);
@@ -413,7 +417,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   pc.on = false;
   pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
   pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
-  pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen;
+  pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   int64_t h0 = 0, h1 = 0;
   if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
     const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on;

@@ -89,9 +89,10 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
 
 
 // The history ids among the 8 elements of the group at g0 (a multiple of 8)
-// take their penalised values from the LDS tables: one pass of the loop per
-// history id in the group (groups without one cost a bitmap read), rather
-// than a branch per element.
+// are penalised from their own logit and their occurrence count in the LDS
+// tables: one pass of the loop per history id in the group (groups without
+// one cost a bitmap read), rather than a branch per element.  The operations
+// are those of the general path's table (the same binary32 sequence).
 __device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCtx& pc) {
   const uint32_t w = (uint32_t)(g0 >> 5), s5 = (uint32_t)(g0 & 31);
   const uint32_t word = pc.bitmap[w];
@@ -101,7 +102,11 @@ __device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCt
   do {
     const int e = __builtin_ctz(bits);
     bits &= bits - 1u;
-    const float pz = pc.zpen[r++];
+    const uint32_t cnt = pc.pcount[r++];
+    float ze = z[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) ze = e == k ? z[k] : ze;
+    const float pz = penalize(canon_nan(ze), cnt, pc);
 #pragma unroll
     for (int k = 0; k < 8; ++k) z[k] = e == k ? pz : z[k];
   } while (bits);
@@ -1396,18 +1401,16 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
 }
 
 // The penalised summary kernel holds the first kHistRegs * kNT history ids
-// of its row in registers, with the raw logits at those ids, both loaded
-// before the row's own loads: waiting for them then leaves the row's loads in
-// flight (loads complete in issue order).
+// of its row in registers, loaded just before the row's own loads: waiting for
+// them then leaves the row's loads in flight (loads complete in issue order).
 constexpr int kHistRegs = 4;
 struct RowHist {
   int64_t h0, h1;
   int32_t id[kHistRegs];  // -1 past the end
-  uint16_t raw[kHistRegs];  // the raw bf16 logit at id (ids in [0, V))
 };
 
-// Parameter status, history bounds, the history ids and the raw logits at
-// them, issued before the row's loads.  Returns the row's status.
+// Parameter status, history bounds and the history ids, issued before the
+// row's loads.  Returns the row's status.
 __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row, const arcs_row_params& P,
                                                 PenCtx& pc, RowHist& hs) {
   const int tid = threadIdx.x;
@@ -1415,6 +1418,7 @@ __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row
   pc.on = false;
   pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
   pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  pc.zpen = nullptr; pc.pcount = nullptr;
   hs.h0 = 0; hs.h1 = 0;
   if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
     const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on;
@@ -1435,22 +1439,17 @@ __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row
     const int32_t v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(hr, j * 4, 0, 0);
     hs.id[k] = (int64_t)j < nreg ? v : -1;
   }
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)a.logits + row * a.stride * 2), (short)0, pc.on ? (int)(a.V * 2) : 0, 0x00020000);
-#pragma unroll
-  for (int k = 0; k < kHistRegs; ++k)
-    hs.raw[k] = __builtin_amdgcn_raw_buffer_load_b16(rr, (int)((uint32_t)hs.id[k] * 2u), 0, 0);
   return status;
 }
 
-// Visits the row's history ids in [0, V), with their raw logits when
-// WITH_RAW: those held in registers, then any beyond them from memory.
+// Visits the row's history ids in [0, V), with their raw logits (read from
+// memory) when WITH_RAW: those held in registers, then any beyond them.
 template <bool WITH_RAW, class Fn>
 __device__ __forceinline__ void for_each_hist_id(const SampleArgs& a, int64_t row, const RowHist& hs, Fn&& f) {
+  const uint16_t* rowp = (const uint16_t*)((const char*)a.logits + row * a.stride * 2);
 #pragma unroll
   for (int k = 0; k < kHistRegs; ++k)
-    if (hs.id[k] >= 0 && (int64_t)hs.id[k] < a.V) f((uint32_t)hs.id[k], WITH_RAW ? bf16_to_f32(hs.raw[k]) : 0.0f);
-  const uint16_t* rowp = (const uint16_t*)((const char*)a.logits + row * a.stride * 2);
+    if (hs.id[k] >= 0 && (int64_t)hs.id[k] < a.V) f((uint32_t)hs.id[k], WITH_RAW ? bf16_to_f32(rowp[hs.id[k]]) : 0.0f);
   for (int64_t i = hs.h0 + (int64_t)kHistRegs * kNT + threadIdx.x; i < hs.h1; i += kNT) {
     const int32_t id = a.hist_ids[i];
     if (id >= 0 && (int64_t)id < a.V) f((uint32_t)id, WITH_RAW ? bf16_to_f32(rowp[id]) : 0.0f);
@@ -1460,13 +1459,13 @@ __device__ __forceinline__ void for_each_hist_id(const SampleArgs& a, int64_t ro
 // Penalty tables of the summary path, built while the row's loads are in
 // flight (LDS-only barriers): the bitmap of the history ids over [0, V), the
 // number of distinct ids before each bitmap word, and per distinct id (by
-// rank, in id order) its penalised logit, from its occurrence count (counted
-// in the candidate area, free here) and its raw logit.  Returns false when
-// the row is finished (its status written).
+// rank, in id order) its occurrence count.  No logit is read here: the pass
+// penalises each history id from its own logit.  Returns false when the row
+// is finished (its status written).
 __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh,
                                                    int status, PenCtx& pc, const RowHist& hs, uint32_t& path) {
   const int tid = threadIdx.x;
-  pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen;
+  pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   if (status == ARCS_ROW_OK && pc.on) {
     const uint32_t bw = a.bitmap_words;
     for (uint32_t i = tid; i < bw; i += kNT) sm.bitmap[i] = 0u;
@@ -1489,12 +1488,6 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
       lds_barrier();
       for_each_hist_id<false>(a, row, hs, [&](uint32_t id, float) {
         atomicAdd(&sm.pcount[pen_rank(id, sm.bitmap, sm.wprefix)], 1u);
-      });
-      lds_barrier();
-      // every occurrence of an id writes the same penalised value
-      for_each_hist_id<true>(a, row, hs, [&](uint32_t id, float raw) {
-        const uint32_t rk = pen_rank(id, sm.bitmap, sm.wprefix);
-        sm.zpen[rk] = penalize(canon_nan(raw), sm.pcount[rk], pc);
       });
       lds_barrier();
     } else {
@@ -1543,6 +1536,16 @@ __global__ __launch_bounds__(kNT) void sample_summary_kernel(SampleArgs a) {
     if (!summary_pen_tables(a, row, sm, sh, status, pc, hs, path)) return;
     if (!stream_row<true>(a, row, P, rng, pc, path, sm, sh, d)) {
       __syncthreads();
+      if (pc.on) {
+        // the general pipeline reads penalised logits per distinct id: built
+        // here from the counts and the raw logits (every occurrence of an id
+        // writes the same value)
+        for_each_hist_id<true>(a, row, hs, [&](uint32_t id, float raw) {
+          const uint32_t rk = pen_rank(id, sm.bitmap, sm.wprefix);
+          sm.zpen[rk] = penalize(canon_nan(raw), sm.pcount[rk], pc);
+        });
+        __syncthreads();
+      }
       generic_row<true, true>(a, row, P, pc, path, sm, sh);
     }
   }
