@@ -587,6 +587,40 @@ def test_keyed_sampling_matches_by_value_key_eager_and_in_a_graph(arcs):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("V", [4_096, 50_000, 129_280])
+def test_f32_random_parameters(arcs, V):
+    """fp32 rows with random filter mixes and temperatures over flat, peaked,
+    normal and coarsely rounded (tied) logits, against the oracle."""
+    B = 48
+    rng = np.random.default_rng(1000 + V)
+    w = make_workload("flat_b1024_f32_t1_p0.95", B=B, V=V, seed=21, step=9)
+    z = w.logits.copy()
+    for b in range(B):
+        kind = b % 4
+        if kind == 1:
+            z[b] = (z[b] * 3.0).astype(np.float32)  # peaked
+        elif kind == 2:
+            z[b] = rng.normal(0.0, 2.0, V).astype(np.float32)
+        elif kind == 3:
+            z[b] = (np.round(z[b] * 16.0) / 16.0).astype(np.float32)  # ties
+    w.logits = z
+    p = make_params(B, temperature=1.0)
+    for b in range(B):
+        p[b]["temperature"] = float(rng.uniform(0.2, 2.0))
+        if rng.random() < 0.5:
+            p[b]["top_k"] = int(rng.integers(1, V))
+        if rng.random() < 0.5:
+            p[b]["top_p"] = float(rng.uniform(0.05, 0.999))
+        if rng.random() < 0.4:
+            p[b]["min_p"] = float(10 ** rng.uniform(-4, -0.5))
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    _compare_rows(ids, stats, _oracle(w), f"f32 random V={V}")
+    logits = to_device_logits(w.logits, "f32")
+    got = arcs.sample(logits, arcs.params_to_device(w.params), seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
+
+
 def test_f32_rows_with_deferred_rows_in_a_graph(arcs):
     """fp32 rows take two kernels per call: the two-read kernel, then the
     general one for the rows it hands back (here rows with NaN / +inf and an
