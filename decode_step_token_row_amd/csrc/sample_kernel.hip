@@ -2053,12 +2053,19 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   const float negO = uniform_f32((float)-Od);
   const float OR = uniform_f32((float)(Od * (double)kFR));
   const float ncR = uniform_f32(-(float)(c * (double)kFR));
+  // top-k <= the row's thread count: every cut lies within the bins down to
+  // that of the k-th largest thread maximum (at least k elements are at or
+  // above it, so the top-k prefix, and any shorter one, is there); those bins
+  // come from the thread maxima alone, and the pass needs no histogram
+  const bool kwin = kon && P.top_k <= (ngroups < kFT ? ngroups : kFT);
+  const bool hcount = kon && !kwin, hmass = pon && !kwin;
   float exc = 0.0f;
-  if (kon && pon) f32_pass1<true, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
-  else if (kon) f32_pass1<true, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
-  else if (pon) f32_pass1<false, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  if (hcount && hmass) f32_pass1<true, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else if (hcount) f32_pass1<true, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else if (hmass) f32_pass1<false, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
   else f32_pass1<false, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
-  if (pon) {
+  if (kwin && tid < ngroups) atomicAdd(&hc[f32_bin(tmax, ncR, OR)], 1u);
+  if (hmass) {
     const double we = dpp_wave_sum_f64((double)exc);
     if ((tid & (kWave - 1)) == 0) sh.w_sum[tid / kWave] = we;
   }
@@ -2081,15 +2088,16 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
     if (!ok) return false;
   }
   if (mode == kF32Cand) {
-    // wave 0: the first bin (from the top) where the top-k count or the
-    // top-p mass target is reached; lane l sums bins 32l .. 32l + 31
+    // wave 0: the first bin (from the top) where the top-k count (of elements,
+    // or of thread maxima for kwin) or the top-p mass target is reached; lane l
+    // sums bins 32l .. 32l + 31
     constexpr int PER = kFB / kWave;
     const int lane = tid & (kWave - 1);
     if (tid < kWave) {
       const double Pm = pon ? (double)P.top_p * S : 0.0;
       uint32_t lc = 0;
       double lm = 0.0, exc0 = 0.0;
-      if (pon) {
+      if (hmass) {
 #pragma unroll
         for (int w = 0; w < kFW; ++w) exc0 += sh.w_sum[w];
       }
@@ -2102,7 +2110,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
       const uint32_t ic = dpp_wave_incl_scan_u32(lc);
       const double im = dpp_wave_incl_scan_f64(lm);
       const uint64_t hk = __ballot(kon && ic >= (uint32_t)P.top_k);
-      const uint64_t hp = __ballot(pon && im >= Pm);
+      const uint64_t hp = __ballot(hmass && im >= Pm);
       if (lane == 0) { sh.i32[6] = kFB; sh.i32[7] = kFB; }
       if (hk && lane == __builtin_ctzll(hk)) {
         uint32_t cc = ic - lc;
@@ -2138,7 +2146,9 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
     // by rounding)
     if (bstar >= kFB) return false;
     bhi = bstar;
-    if (pon && bstar == bp) {
+    if (kwin) {
+      bstar = 0;  // the whole window is gathered; nothing is kept for sure
+    } else if (pon && bstar == bp) {
       const int near = sh.i32[3];
       if ((near & 1) && bstar > 0) bstar -= 1;
       if ((near & 2) && bhi < kFB - 1) bhi += 1;
