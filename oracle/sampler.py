@@ -339,3 +339,56 @@ def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optiona
 def argmax(logits: np.ndarray, dtype: str) -> np.ndarray:
     """Row-wise argmax of the widened raw logits (no penalties)."""
     return np.array([argmax_first(widen(r, dtype)) for r in logits], dtype=np.int32)
+
+
+# --------------------------------------------------------------------------
+# top-n log-probabilities (the response feature next to the draw)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class TopLogprobs:
+    status: int
+    ids: np.ndarray        # int64 [n]
+    logprobs: np.ndarray   # float64 [n]
+
+
+def top_logprobs_row(raw_row: np.ndarray, dtype: str, T: float, n: int) -> TopLogprobs:
+    """The n most probable ids of a row and their log-probabilities.
+
+    Arc PR #222, section 3(c): next to the draw, the host sampler reports the
+    most probable tokens with their log-probabilities, found by a partial sort
+    of the probabilities.  Reading taken here: the distribution is that of the
+    widened logits at temperature T (no penalties, no filters), so with
+    m = max z and S = sum of w (step 5 above, math.fsum),
+    logprob_v = (z_v - m) / T - ln S, and 0 - ln S where z_v == m (which covers
+    +inf logits and a row of -inf, then uniform).  The ids are the first n of
+    the total order (step 4); a row shorter than n ends with id -1 and -inf.
+    T must be finite and > 0, else the row's status is ROW_BAD_TEMPERATURE
+    (ids -1, logprobs NaN).
+    """
+    if not (T > 0.0 and math.isfinite(T)):
+        return TopLogprobs(ROW_BAD_TEMPERATURE, np.full(n, -1, np.int64), np.full(n, np.nan))
+    z = widen(raw_row, dtype)
+    m, w = weights(z, T)
+    lnS = math.log(math.fsum(w.tolist()))
+    order = total_order(z)[:n]
+    ids = np.full(n, -1, np.int64)
+    lps = np.full(n, -np.inf)
+    for r, v in enumerate(order):
+        zv = float(z[v])
+        lw = 0.0 if zv == m else (zv - m) / T
+        ids[r] = int(v)
+        lps[r] = lw - lnS
+    return TopLogprobs(ROW_OK, ids, lps)
+
+
+def top_logprobs(logits: np.ndarray, dtype: str, temperature: Optional[Sequence[float]], n: int):
+    """Oracle over a batch: (ids [B, n] int64, logprobs [B, n] float64, status [B])."""
+    B = logits.shape[0]
+    ids = np.empty((B, n), np.int64)
+    lps = np.empty((B, n), np.float64)
+    st = np.empty(B, np.int32)
+    for b in range(B):
+        T = 1.0 if temperature is None else float(temperature[b])
+        r = top_logprobs_row(logits[b], dtype, T, n)
+        ids[b], lps[b], st[b] = r.ids, r.logprobs, r.status
+    return ids, lps, st

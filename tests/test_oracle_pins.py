@@ -465,3 +465,86 @@ def test_planted_mistakes_are_caught(monkeypatch):
             return c
         m.setattr(o, "cutoff", renorm)
         assert _red(test_combined_filters_take_the_shortest_prefix_without_renormalising)
+
+
+# --------------------------------------------------------------------------
+# top-n log-probabilities (Arc PR #222, section 3(c); reading in the oracle)
+# --------------------------------------------------------------------------
+def test_top_logprobs_uniform_row_closed_form():
+    # equal logits: every id has probability 1/V, the order is by id
+    V, n = 37, 10
+    row = np.full(V, 1.25, np.float32)
+    r = o.top_logprobs_row(row, "f32", 0.6, n)
+    assert r.status == o.ROW_OK
+    assert r.ids.tolist() == list(range(n))
+    assert np.allclose(r.logprobs, -math.log(V), rtol=0, atol=1e-15)
+
+
+def test_top_logprobs_two_levels_closed_form():
+    # k ids at value a, the rest at b < a: S = k + (V - k) exp((b - a) / T)
+    V, k, T, n = 50, 7, 0.8, 12
+    rng = np.random.default_rng(3)
+    hi = np.sort(rng.choice(V, k, replace=False))
+    row = np.full(V, -0.5, np.float32)
+    row[hi] = 2.0
+    S = k + (V - k) * math.exp((-0.5 - 2.0) / T)
+    r = o.top_logprobs_row(row, "f32", T, n)
+    lo_ids = [v for v in range(V) if v not in set(hi.tolist())][: n - k]
+    assert r.ids.tolist() == hi.tolist() + lo_ids
+    assert np.allclose(r.logprobs[:k], -math.log(S), rtol=0, atol=1e-14)
+    assert np.allclose(r.logprobs[k:], (-0.5 - 2.0) / T - math.log(S), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_logprobs_against_scipy_log_softmax(dtype):
+    # scipy's log_softmax of z / T and a stable sort of -z (first ids first)
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        V = int(rng.integers(1, 400))
+        T = float(rng.uniform(0.05, 3.0))
+        n = int(rng.integers(1, 65))
+        z = (rng.normal(0, 2, V) * (4 if trial % 3 == 0 else 1)).astype(np.float32)
+        if trial % 4 == 1:
+            z = np.round(z * 2) / 2  # many ties
+        raw = f32_to_bf16_bits(z) if dtype == "bf16" else z.astype(np.float32)
+        zw = o.widen(raw, dtype).astype(np.float64)
+        ref_lp = scipy.special.log_softmax(zw / T)
+        ref_ids = np.argsort(-zw, kind="stable")[:n]
+        r = o.top_logprobs_row(raw, dtype, T, n)
+        k = min(n, V)
+        assert r.ids[:k].tolist() == ref_ids.tolist()
+        assert np.allclose(r.logprobs[:k], ref_lp[ref_ids], rtol=1e-12, atol=1e-12)
+        assert (r.ids[k:] == -1).all() and np.isneginf(r.logprobs[k:]).all()
+
+
+def test_top_logprobs_full_row_sums_to_one():
+    rng = np.random.default_rng(5)
+    V = 300
+    z = rng.normal(0, 3, V).astype(np.float32)
+    r = o.top_logprobs_row(z, "f32", 0.7, V)
+    assert sorted(r.ids.tolist()) == list(range(V))
+    assert abs(math.fsum(np.exp(r.logprobs).tolist()) - 1.0) < 1e-13
+    assert np.all(np.diff(r.logprobs) <= 0)
+
+
+def test_top_logprobs_special_values():
+    # +inf logits share all the mass; NaN counts as -inf; a row of -inf is uniform
+    row = np.array([1.0, np.inf, np.nan, 3.0, np.inf, -np.inf], np.float32)
+    r = o.top_logprobs_row(row, "f32", 1.0, 6)
+    assert r.ids.tolist() == [1, 4, 3, 0, 2, 5]
+    assert np.allclose(r.logprobs[:2], -math.log(2), atol=1e-15)
+    assert np.isneginf(r.logprobs[2:]).all()
+    allneg = np.array([-np.inf, np.nan, -np.inf, -np.inf], np.float32)
+    r = o.top_logprobs_row(allneg, "f32", 2.0, 3)
+    assert r.ids.tolist() == [0, 1, 2]
+    assert np.allclose(r.logprobs, -math.log(4), atol=1e-15)
+    # -0 and +0 are one value: ties broken by id
+    r = o.top_logprobs_row(np.array([-0.0, 0.0, -1.0], np.float32), "f32", 1.0, 2)
+    assert r.ids.tolist() == [0, 1]
+
+
+def test_top_logprobs_bad_temperature():
+    for T in (0.0, -1.0, float("nan"), float("inf")):
+        r = o.top_logprobs_row(np.zeros(4, np.float32), "f32", T, 3)
+        assert r.status == o.ROW_BAD_TEMPERATURE
+        assert (r.ids == -1).all() and np.isnan(r.logprobs).all()
