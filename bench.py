@@ -44,7 +44,12 @@ ROTATE_BYTES = 512 * 2**20
 KERNEL_SOURCES = {
     "argmax": ["device_common.hpp", "launch.hpp", "api.hip", "argmax_kernel.hip"],
     "sample": ["device_common.hpp", "launch.hpp", "api.hip", "sample_common.hpp", "sample_kernel.hip"],
+    "logprobs": ["device_common.hpp", "launch.hpp", "api.hip", "logprobs_kernel.hip"],
 }
+
+
+def kernel_kind(w) -> str:
+    return "logprobs" if w.top_n else ("argmax" if w.greedy_only else "sample")
 
 
 def log(msg):
@@ -65,6 +70,8 @@ def algorithmic_bytes(w) -> int:
     """Bytes the step must move at least once: logits, per-row params,
     history ids and offsets (if any), output ids."""
     es = 2 if w.dtype == "bf16" else 4
+    if w.top_n:  # logits, per-row temperature, ids and logprobs
+        return int(w.B * w.V * es + w.B * 4 + w.B * w.top_n * 8)
     b = w.B * w.V * es + w.B * 4
     if not w.greedy_only:
         b += w.B * 32
@@ -76,6 +83,8 @@ def algorithmic_bytes(w) -> int:
 def kernel_name(w) -> str:
     """The kernel one step launches for this workload (as the launcher picks it)."""
     fits = w.dtype == "bf16" and w.V % 8 == 0 and w.V <= 131072
+    if w.top_n:
+        return "top_logprobs_kernel"
     if w.greedy_only:
         return "argmax_fast_kernel" if fits else "argmax_kernel"
     if fits:
@@ -110,7 +119,9 @@ def cpu_baseline(w, seconds: float):
     t0 = time.perf_counter()
     while True:
         i = rows % w.logits.shape[0]
-        if w.greedy_only:
+        if w.top_n:
+            oracle.top_logprobs_row(w.logits[i], w.dtype, float(w.params[i]["temperature"]), w.top_n)
+        elif w.greedy_only:
             oracle.argmax(w.logits[i:i + 1], w.dtype)
         else:
             hist = None
@@ -184,10 +195,16 @@ def main():
         hist_ids = torch.from_numpy(w.hist_ids).to(dev)
         hist_offs = torch.from_numpy(w.hist_offsets).to(dev)
     out = torch.empty(w.B, dtype=torch.int32, device=dev)
+    if w.top_n:
+        temps = torch.from_numpy(np.ascontiguousarray(w.params["temperature"], dtype=np.float32)).to(dev)
+        lp_ids = torch.empty((w.B, w.top_n), dtype=torch.int32, device=dev)
+        lp_vals = torch.empty((w.B, w.top_n), dtype=torch.float32, device=dev)
 
     def step(i):
         x = bufs[i % nbuf]
-        if w.greedy_only:
+        if w.top_n:
+            arcs.top_logprobs(x, w.top_n, temperature=temps, out_ids=lp_ids, out_logprobs=lp_vals)
+        elif w.greedy_only:
             arcs.argmax(x, out=out)
         else:
             arcs.sample(x, params, hist_ids, hist_offs, seed=w.seed, step=i, out=out)
@@ -226,7 +243,7 @@ def main():
     alg = algorithmic_bytes(w)
     # one launch per step: the average launch duration over the timed region
     achieved = alg / (ms_per_step * 1e-3) / 1e9
-    traffic = read_traffic(args.workload, "argmax" if w.greedy_only else "sample")
+    traffic = read_traffic(args.workload, kernel_kind(w))
     rows_per_s = w.B / (ms_per_step * 1e-3)
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step, launch avg {avg_launch_ms * 1e3:.2f} us "
         f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.2f}), {achieved:.0f} GB/s, wall {wall:.4f}s, "
@@ -260,7 +277,8 @@ def main():
             "B": w.B,
             "V": w.V,
             "logits_dtype": w.dtype,
-            "entry_point": "arcs_argmax" if w.greedy_only else "arcs_sample",
+            "entry_point": ("arcs_top_logprobs" if w.top_n else
+                            "arcs_argmax" if w.greedy_only else "arcs_sample"),
             "logit_buffers_rotated": nbuf,
             "parallelism": "single GPU, one workgroup per row",
         },

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     sample_debug,
     sample_keyed,
     status_string,
+    top_logprobs,
     version,
     workspace_bytes,
 )

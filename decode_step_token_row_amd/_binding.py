@@ -87,6 +87,8 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_keyed.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p]
         lib.arcs_sample_keyed.restype = c_i
+        lib.arcs_top_logprobs.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_i, c_p, c_p, c_p, c_p]
+        lib.arcs_top_logprobs.restype = c_i
         lib.arcs_sample_workspace_bytes.argtypes = [c_i64, c_i64, c_i]
         lib.arcs_sample_workspace_bytes.restype = ctypes.c_size_t
         lib.arcs_status_string.argtypes = [c_i]
@@ -165,6 +167,38 @@ def argmax(logits, out=None, stream=None):
     if st != OK:
         raise ArcsError(st, "arcs_argmax")
     return out
+
+
+def top_logprobs(logits, n: int, temperature=None, out_ids=None, out_logprobs=None, out_status=None,
+                 stream=None):
+    """arcs_top_logprobs: (ids int32 [B, n], logprobs float32 [B, n]) on device.
+
+    ``temperature`` is a device float32 tensor of B values or None (T = 1);
+    ``out_status`` an optional device int32 tensor of B values.
+    """
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    dev = logits.device
+    if temperature is not None and (temperature.dtype != torch.float32 or not temperature.is_cuda
+                                    or temperature.numel() != B or not temperature.is_contiguous()):
+        raise ValueError("temperature must be a contiguous device float32 tensor of B elements")
+    if out_ids is None:
+        out_ids = torch.empty((B, n), dtype=torch.int32, device=dev)
+    if out_logprobs is None:
+        out_logprobs = torch.empty((B, n), dtype=torch.float32, device=dev)
+    if out_ids.dtype != torch.int32 or out_ids.numel() != B * n or not out_ids.is_cuda:
+        raise ValueError("out_ids must be a device int32 tensor of B * n elements")
+    if out_logprobs.dtype != torch.float32 or out_logprobs.numel() != B * n or not out_logprobs.is_cuda:
+        raise ValueError("out_logprobs must be a device float32 tensor of B * n elements")
+    if out_status is not None and (out_status.dtype != torch.int32 or out_status.numel() != B
+                                   or not out_status.is_cuda):
+        raise ValueError("out_status must be a device int32 tensor of B elements")
+    st = library().arcs_top_logprobs(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(temperature),
+                                     int(n), _ptr(out_ids), _ptr(out_logprobs), _ptr(out_status),
+                                     _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_top_logprobs")
+    return out_ids, out_logprobs
 
 
 def _check_params(params, B):

@@ -124,6 +124,29 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
                      out_stats, stream);
 }
 
+int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const float* temperature, int n, int32_t* out_ids, float* out_logprobs,
+                      int32_t* out_status, void* stream) {
+  int st = check_common(logits, dtype, B, V, row_stride, out_ids);
+  if (st != ARCS_OK) return st;
+  if (out_logprobs == nullptr) return ARCS_ERR_NULL_POINTER;
+  if (n < 1 || n > ARCS_MAX_TOP_LOGPROBS) return ARCS_ERR_BAD_TOP_N;
+  if (V > ARCS_TOP_LOGPROBS_MAX_VOCAB) return ARCS_ERR_BAD_VOCAB;
+  if (((uintptr_t)temperature) % 4u != 0) return ARCS_ERR_MISALIGNED;
+  arcs::LogprobArgs a;
+  a.logits = logits;
+  a.V = V;
+  a.stride = row_stride;
+  a.temperature = temperature;
+  a.n = n;
+  a.out_ids = out_ids;
+  a.out_logprobs = out_logprobs;
+  a.out_status = out_status;
+  hipError_t e = arcs::launch_top_logprobs(a, dtype, B, rows_16b_aligned(logits, dtype, row_stride),
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
+}
+
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype) {
   (void)B;
   (void)V;
@@ -143,6 +166,7 @@ const char* arcs_status_string(int code) {
     case ARCS_ERR_LAUNCH: return "kernel launch failed";
     case ARCS_ERR_MISALIGNED: return "logits pointer not aligned to its element size";
     case ARCS_ERR_BAD_HISTORY: return "hist_ids and hist_offsets must both be NULL or both be set";
+    case ARCS_ERR_BAD_TOP_N: return "n must be in [1, ARCS_MAX_TOP_LOGPROBS]";
     case ARCS_ROW_BAD_TEMPERATURE: return "row: temperature is NaN or negative";
     case ARCS_ROW_BAD_TOP_P: return "row: top_p is NaN or <= 0";
     case ARCS_ROW_BAD_MIN_P: return "row: min_p is NaN or outside [0, 1]";

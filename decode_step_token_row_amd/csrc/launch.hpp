@@ -36,9 +36,22 @@ struct SampleArgs {
 // kernel launched after it on the same stream (never a valid id or status).
 constexpr int32_t kDeferredId = INT32_MIN;
 
+// One top-logprobs launch (arcs_top_logprobs).
+struct LogprobArgs {
+  const void* logits;
+  int64_t V;
+  int64_t stride;
+  const float* temperature;  // [B] or NULL (T = 1)
+  int n;
+  int32_t* out_ids;          // [B * n]
+  float* out_logprobs;       // [B * n]
+  int32_t* out_status;       // [B] or NULL
+};
+
 hipError_t launch_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
                          bool vec, int32_t* out, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream);
 hipError_t launch_advance_step(uint64_t* key, hipStream_t stream);
+hipError_t launch_top_logprobs(const LogprobArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream);
 
 }  // namespace arcs

@@ -1,0 +1,320 @@
+// Top-n log-probabilities per row over [B, V] logits (bf16 or fp32), one
+// workgroup per row.
+//
+// Next to the drawn token, the Arc engine's host sampler reports the most
+// probable tokens with their log-probabilities, found by a partial sort of
+// the probabilities (Arc PR #222, section 3(c)).  Per row, at temperature T:
+//   z    = logits widened to float32 (NaN -> -inf, -0 -> +0), m = max z;
+//   w_v  = exp((z_v - m) / T), with w = 1 where z_v == m (this covers +inf
+//          and a row of -inf, which is then uniform);
+//   S    = sum of w;  logprob_v = (z_v - m) / T - ln S (0 - ln S where z_v == m);
+// output: the first n ids of the order (z descending, id ascending) and
+// their logprobs.
+//
+// One HBM pass.  Each thread keeps its largest value with the first id that
+// holds it, and an online sum of its weights relative to its own maximum,
+// rescaled when that maximum grows, so the normaliser needs no second pass.
+// The thread maxima become 64-bit keys (value order key << 32 | ~id, all
+// distinct).  The n-th largest of them, beta, is a lower bound for the n-th
+// element of the row, and only the n threads whose maximum reaches it can
+// hold elements at or above it.  beta is found without sorting: each wave
+// finds the n-th largest of its 64 keys by a bitwise descent over ballots;
+// the largest of those 16 values is a lower bound for beta, the keys at or
+// above it (at most n per wave, about n in all) go to LDS, and their ranks
+// among themselves are their ranks in the row.  The units of those n threads are read again (from cache), spread
+// over the whole workgroup, and their elements at or above beta gathered
+// into LDS (at most n * 128); each candidate's rank among the candidates is
+// its position in the output.
+#include <atomic>
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace arcs {
+
+constexpr int kLpNT = 1024;
+constexpr int kLpNW = kLpNT / kWave;
+constexpr int kLpPerThread = 128;                                  // elements a thread owns at most
+static_assert((int64_t)kLpNT * kLpPerThread == ARCS_TOP_LOGPROBS_MAX_VOCAB, "vocabulary bound");
+constexpr int kLpCap = ARCS_MAX_TOP_LOGPROBS * kLpPerThread;       // candidates at most
+constexpr int kLpBatch = 16;                                       // loads in flight per thread
+constexpr size_t kLpLds = (size_t)kLpCap * 8 + (size_t)kLpNT * 8;  // candidates + survivors
+
+__device__ __forceinline__ uint64_t lp_key(float z, uint32_t id) {
+  return ((uint64_t)ord_key(z) << 32) | (uint64_t)(~id);
+}
+
+// How many of the `cnt` keys in `list` (LDS, 16-byte aligned) exceed k,
+// stopping once `stop` is reached (checked every 16 keys).  Keys are read two
+// at a time, eight reads in flight; reads past the end are clamped to the
+// last pair and not counted.
+__device__ __forceinline__ int lp_rank(const uint64_t* list, int cnt, uint64_t k, int stop) {
+  const u32x4* pairs = (const u32x4*)list;
+  const int last = (cnt - 1) >> 1;
+  int r = 0;
+  for (int j0 = 0; j0 < cnt && r < stop; j0 += 16) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pj = (j0 >> 1) + u;
+      v[u] = pairs[pj < last ? pj : last];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + 2 * u;
+      const uint64_t a = ((uint64_t)v[u].y << 32) | v[u].x, b = ((uint64_t)v[u].w << 32) | v[u].z;
+      r += (int)((j < cnt) & (a > k)) + (int)((j + 1 < cnt) & (b > k));
+    }
+  }
+  return r;
+}
+
+// A thread's unit of the row: 16 bytes (8 bf16 or 4 fp32) on the vector
+// path, one element otherwise.
+template <bool BF16, bool VEC>
+struct LpUnit {
+  static constexpr int E = VEC ? (BF16 ? 8 : 4) : 1;
+  using Raw = typename std::conditional<VEC, u32x4, uint32_t>::type;
+  static __device__ __forceinline__ Raw load(const char* rowp, int g) {
+    if constexpr (VEC) {
+      return ((const u32x4*)rowp)[g];
+    } else if constexpr (BF16) {
+      return (uint32_t)((const uint16_t*)rowp)[g] << 16;
+    } else {
+      return ((const uint32_t*)rowp)[g];
+    }
+  }
+  // raw values: NaN and -0 as they are (the pass copes with both)
+  static __device__ __forceinline__ void unpack(const Raw& d, float (&z)[E]) {
+    if constexpr (VEC && BF16) {
+      z[0] = bf16_lo(d.x); z[1] = bf16_hi(d.x); z[2] = bf16_lo(d.y); z[3] = bf16_hi(d.y);
+      z[4] = bf16_lo(d.z); z[5] = bf16_hi(d.z); z[6] = bf16_lo(d.w); z[7] = bf16_hi(d.w);
+    } else if constexpr (VEC) {
+      z[0] = __uint_as_float(d.x); z[1] = __uint_as_float(d.y);
+      z[2] = __uint_as_float(d.z); z[3] = __uint_as_float(d.w);
+    } else {
+      z[0] = __uint_as_float(d);
+    }
+  }
+  static __device__ __forceinline__ void unpack_canon(const Raw& d, float (&z)[E]) {
+    unpack(d, z);
+#pragma unroll
+    for (int e = 0; e < E; ++e) z[e] = canon_nan(z[e]) + 0.0f;  // NaN -> -inf, -0 -> +0
+  }
+};
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
+  using U = LpUnit<BF16, VEC>;
+  constexpr int E = U::E;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lp_smem[];
+  uint64_t* cand = (uint64_t*)lp_smem;
+  uint64_t* surv = cand + kLpCap;
+  __shared__ float s_max[kLpNW];
+  __shared__ double s_sum[kLpNW];
+  __shared__ uint64_t s_beta;
+  __shared__ uint32_t s_cnt, s_nsurv;
+  __shared__ uint64_t s_wbound[kLpNW];
+  __shared__ int s_owner[ARCS_MAX_TOP_LOGPROBS];  // the threads whose maximum reaches beta
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int64_t row = blockIdx.x;
+  const int n = a.n;
+  int32_t* oid = a.out_ids + row * n;
+  float* olp = a.out_logprobs + row * n;
+
+  const float T = a.temperature ? a.temperature[row] : 1.0f;
+  if (!(T > 0.0f && T < __builtin_inff())) {
+    if (tid < n) { oid[tid] = -1; olp[tid] = __builtin_nanf(""); }
+    if (tid == 0 && a.out_status) a.out_status[row] = ARCS_ROW_BAD_TEMPERATURE;
+    return;
+  }
+  const double cd = 1.4426950408889634 / (double)T;  // log2(e) / T
+  const float c = (float)cd;
+
+  const char* rowp = (const char*)a.logits + row * a.stride * (BF16 ? 2 : 4);
+  const int ngroups = (int)(VEC ? a.V / E : a.V);
+  const int nq = (ngroups + kLpNT - 1) / kLpNT;
+
+  // ---- the pass: thread maximum (first id) and weights relative to it -------
+  // A NaN never wins a comparison, so the maximum is that of the row with NaN
+  // as -inf; a NaN weight, or an infinite maximum (inf - inf), leaves s
+  // wrong or NaN, and such a thread recounts its weights exactly after the pass.
+  float mt = -__builtin_inff();
+  double s = 0.0;
+  uint32_t first = (uint32_t)tid * E;
+  for (int q0 = 0; q0 < nq; q0 += kLpBatch) {
+    // unconditional loads (a lane past the row's end reads its last unit
+    // again and ignores it): a branch per load would serialise them
+    typename U::Raw d[kLpBatch];
+#pragma unroll
+    for (int r = 0; r < kLpBatch; ++r) {
+      const int g = (q0 + r) * kLpNT + tid;
+      d[r] = U::load(rowp, g < ngroups ? g : ngroups - 1);
+    }
+#pragma unroll
+    for (int r = 0; r < kLpBatch; ++r) {
+      const int g = (q0 + r) * kLpNT + tid;
+      if (g >= ngroups) continue;
+      float z[E];
+      U::unpack(d[r], z);
+      float gm = -__builtin_inff();
+      int ef = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ef = z[e] > gm ? e : ef;
+        gm = z[e] > gm ? z[e] : gm;
+      }
+      if (gm > mt) {
+        s *= (double)__builtin_amdgcn_exp2f((mt - gm) * c);  // 0 when mt is -inf or gm is +inf
+        mt = gm;
+        first = (uint32_t)g * E + (uint32_t)ef;
+      }
+      float ws = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ws += __builtin_amdgcn_exp2f((z[e] - mt) * c);
+      s += (double)ws;
+    }
+  }
+  const bool owns = tid < ngroups;
+  if (owns && !(s == s && __builtin_fabsf(mt) < __builtin_inff())) {
+    // exact weights: w = 1 where z == mt (+inf, or a thread of -inf), NaN as -inf
+    s = 0.0;
+    for (int q = 0; q < nq; ++q) {
+      const int g = q * kLpNT + tid;
+      if (g >= ngroups) break;
+      float z[E];
+      U::unpack_canon(U::load(rowp, g), z);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += z[e] == mt ? 1.0 : (double)__builtin_amdgcn_exp2f((z[e] - mt) * c);
+    }
+  }
+
+  // ---- row maximum and normaliser ------------------------------------------------
+  const float wm = dpp_wave_max_f32(mt);
+  if (lane == 0) s_max[wid] = wm;
+  __syncthreads();
+  float m = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kLpNW; ++w) m = s_max[w] > m ? s_max[w] : m;
+  const double f = mt == m ? 1.0 : exp2(((double)mt - (double)m) * cd);
+  const double ws = dpp_wave_sum_f64(owns ? s * f : 0.0);
+  if (lane == 0) s_sum[wid] = ws;
+  if (tid == 0) { s_cnt = 0u; s_nsurv = 0u; }
+  __syncthreads();
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kLpNW; ++w) S += s_sum[w];
+  const double lnS = log(S);
+
+  // ---- beta: the n-th largest thread maximum ----------------------------------
+  const uint64_t tkey = owns ? lp_key(mt, first) : 0ull;
+  uint64_t beta = 0ull;  // fewer threads hold elements than n: all are candidates
+  int nown = ngroups < n ? ngroups : n;
+  if (ngroups < n) {
+    if (tid < ngroups) s_owner[tid] = tid;
+    __syncthreads();
+  } else {
+    // the wave's n-th largest key: the largest p with n keys at or above it
+    uint64_t p = 0ull;
+#pragma unroll
+    for (int b = 63; b >= 0; --b) {
+      const uint64_t c1 = p | (1ull << b);
+      p = __builtin_popcountll(__ballot(tkey >= c1)) >= n ? c1 : p;
+    }
+    if (lane == 0) s_wbound[wid] = p;
+    __syncthreads();
+    uint64_t lb = s_wbound[0];
+#pragma unroll
+    for (int w = 1; w < kLpNW; ++w) lb = s_wbound[w] > lb ? s_wbound[w] : lb;
+    const bool keep = owns && tkey >= lb;
+    const uint64_t mask = __ballot(keep);
+    uint32_t base = 0;
+    if (lane == 0 && mask) base = atomicAdd(&s_nsurv, (uint32_t)__builtin_popcountll(mask));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+    if (keep) surv[base + (uint32_t)__builtin_popcountll(mask & ((1ull << lane) - 1ull))] = tkey;
+    __syncthreads();
+    const int ns = (int)s_nsurv;
+    if (tid < ns) {
+      const uint64_t k = surv[tid];
+      const int rr = lp_rank(surv, ns, k, ns);
+      if (rr == n - 1) s_beta = k;
+      if (rr < n) s_owner[rr] = (int)((~(uint32_t)k) / (uint32_t)E) % kLpNT;
+    }
+    __syncthreads();
+    beta = s_beta;
+  }
+
+  // ---- gather every element at or above beta ----------------------------------
+  const float vb = beta ? key_value((uint32_t)(beta >> 32)) : -__builtin_inff();
+  auto scan = [&](const typename U::Raw& dr, int g) {
+    float z[E];
+    U::unpack_canon(dr, z);
+    float gm = z[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) gm = z[e] > gm ? z[e] : gm;
+    if (gm >= vb) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint64_t k = lp_key(z[e], (uint32_t)g * E + (uint32_t)e);
+        if (k >= beta) {
+          const uint32_t slot = atomicAdd(&s_cnt, 1u);
+          if (slot < (uint32_t)kLpCap) cand[slot] = k;
+        }
+      }
+    }
+  };
+  // item (c, q): unit q of owner c, that is unit q * kLpNT + s_owner[c]
+  const int items = nown * nq;
+  for (int it = tid; it < items; it += kLpNT) {
+    const int q = it / nown;
+    const int g = q * kLpNT + s_owner[it - q * nown];
+    if (g < ngroups) scan(U::load(rowp, g), g);
+  }
+  __syncthreads();
+  const int nc = (int)(s_cnt < (uint32_t)kLpCap ? s_cnt : (uint32_t)kLpCap);
+
+  // ---- the first n candidates in order, and their logprobs --------------------
+  auto emit = [&](int r, uint64_t k) {
+    const float z = key_value((uint32_t)(k >> 32));
+    const double lw = z == m ? 0.0 : ((double)z - (double)m) / (double)T;
+    oid[r] = (int32_t)(~(uint32_t)k);
+    olp[r] = (float)(lw - lnS);
+  };
+  for (int i = tid; i < nc; i += kLpNT) {
+    const uint64_t k = cand[i];
+    const int r = lp_rank(cand, nc, k, n);
+    if (r < n) emit(r, k);
+  }
+  if (tid >= nc && tid < n) {  // the row has fewer than n elements
+    oid[tid] = -1;
+    olp[tid] = -__builtin_inff();
+  }
+  if (tid == 0 && a.out_status) a.out_status[row] = ARCS_ROW_OK;
+}
+
+hipError_t launch_top_logprobs(const LogprobArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream) {
+  const bool bf16 = dtype == ARCS_DTYPE_BF16;
+  const bool v = vec && a.V % (bf16 ? 8 : 4) == 0;
+  const void* fn = bf16 ? (v ? (const void*)top_logprobs_kernel<true, true> : (const void*)top_logprobs_kernel<true, false>)
+                        : (v ? (const void*)top_logprobs_kernel<false, true> : (const void*)top_logprobs_kernel<false, false>);
+  static std::atomic<int> done[4];
+  const int which = (bf16 ? 2 : 0) + (v ? 1 : 0);
+  if (!done[which].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLpLds);
+    if (e != hipSuccess) return e;
+    done[which].store(1, std::memory_order_release);
+  }
+  dim3 grid((unsigned)B), block(kLpNT);
+  if (bf16) {
+    if (v) hipLaunchKernelGGL((top_logprobs_kernel<true, true>), grid, block, kLpLds, stream, a);
+    else hipLaunchKernelGGL((top_logprobs_kernel<true, false>), grid, block, kLpLds, stream, a);
+  } else {
+    if (v) hipLaunchKernelGGL((top_logprobs_kernel<false, true>), grid, block, kLpLds, stream, a);
+    else hipLaunchKernelGGL((top_logprobs_kernel<false, false>), grid, block, kLpLds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace arcs

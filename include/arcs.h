@@ -50,7 +50,8 @@ typedef enum arcs_status {
   ARCS_ERR_WORKSPACE_TOO_SMALL = -6, /* workspace_bytes < arcs_sample_workspace_bytes() */
   ARCS_ERR_LAUNCH = -7,              /* the HIP runtime rejected a launch       */
   ARCS_ERR_MISALIGNED = -8,          /* logits not aligned to the element size  */
-  ARCS_ERR_BAD_HISTORY = -9          /* exactly one of hist_ids/hist_offsets is NULL */
+  ARCS_ERR_BAD_HISTORY = -9,         /* exactly one of hist_ids/hist_offsets is NULL */
+  ARCS_ERR_BAD_TOP_N = -10           /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
 } arcs_status;
 
 /* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
@@ -69,6 +70,10 @@ enum {
  * in [0, V) (the number of history entries itself is not limited) and V. */
 #define ARCS_MAX_HISTORY 4096
 #define ARCS_MAX_PENALTY_VOCAB 262144
+
+/* Limits of arcs_top_logprobs: entries per row, and V. */
+#define ARCS_MAX_TOP_LOGPROBS 64
+#define ARCS_TOP_LOGPROBS_MAX_VOCAB 131072
 
 /*
  * Per-row sampling parameters, 32 bytes, device array of B records.
@@ -210,6 +215,33 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
                       arcs_row_stats* out_stats, void* stream);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
+/*
+ * arcs_top_logprobs: the n most probable tokens of each row with their
+ * log-probabilities, next to the draw (Arc PR #222, section 3(c): the host
+ * sampler finds them by a partial sort of the probabilities).  Per row b, at
+ * temperature T = temperature[b] (1 when `temperature` is NULL):
+ *   z = logits widened to float32 (NaN -> -inf, -0 -> +0), m = max z,
+ *   w_v = exp((z_v - m) / T), w_v = 1 where z_v == m (so +inf logits share
+ *   the mass and a row of -inf is uniform), S = sum of w,
+ *   out_ids[b, r], r < n: the r-th id of the order (z desc, id asc);
+ *   out_logprobs[b, r] = ln(w / S) of that id, computed in binary64 and
+ *   rounded to binary32.
+ * No penalties or filters are applied: this is the distribution of the
+ * logits at temperature T.  Rows with V < n end with id -1 and -inf.
+ *   logits        device, [B, row_stride] of dtype
+ *   temperature   device, float[B], or NULL; a row whose T is NaN, <= 0 or
+ *                 +inf gets ids -1, logprobs NaN, status ARCS_ROW_BAD_TEMPERATURE
+ *   n             1 .. ARCS_MAX_TOP_LOGPROBS (else ARCS_ERR_BAD_TOP_N)
+ *   out_ids       device, int32[B * n] (row-major)
+ *   out_logprobs  device, float[B * n] (row-major)
+ *   out_status    device, int32[B], or NULL
+ * V must not exceed ARCS_TOP_LOGPROBS_MAX_VOCAB (else ARCS_ERR_BAD_VOCAB).
+ * Returns ARCS_OK or a negative arcs_status (nothing launched then).
+ */
+int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                      const float* temperature, int n, int32_t* out_ids, float* out_logprobs,
+                      int32_t* out_status, void* stream);
+
 int arcs_version(void);
 
 #ifdef __cplusplus

@@ -18,7 +18,7 @@ def arcs():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
-                 "arcs_status_string", "arcs_sample_debug", "arcs_version"):
+                 "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs"):
         assert name in fns
 
 
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol(arcs):
 
 
 def test_status_strings_and_version(arcs):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, 1, 2, 3, 4, 5, 6, 7]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, 1, 2, 3, 4, 5, 6, 7]:
         assert arcs.status_string(code) != "unknown status", code
     assert arcs.status_string(12345) == "unknown status"
     assert arcs.version() >= 100
@@ -74,3 +74,13 @@ def test_host_validation_rejects_before_launch(arcs):
     assert K(p, 0, 4, 10, 10, p, None, None, ctypes.c_void_p(base + 4), 1, p, None, None, 0, None) == -8
     assert K(p, 0, 4, 10, 10, None, None, None, p, 1, p, None, None, 0, None) == -1
     assert K(p, 0, 4, 10, 9, p, None, None, p, 0, p, None, None, 0, None) == -4
+    # top logprobs: n in [1, 64], V <= 131072, both outputs required
+    L = lib.arcs_top_logprobs
+    assert L(p, 0, 4, 10, 10, None, 5, p, None, None, None) == -1
+    assert L(p, 0, 4, 10, 10, None, 5, None, p, None, None) == -1
+    assert L(p, 0, 4, 10, 10, None, 0, p, p, None, None) == -10
+    assert L(p, 0, 4, 10, 10, None, 65, p, p, None, None) == -10
+    assert L(p, 0, 4, 131073, 131073, None, 5, p, p, None, None) == -3
+    assert L(p, 0, 4, 10, 10, ctypes.c_void_p(base + 2), 5, p, p, None, None) == -8
+    assert L(p, 0, 4, 10, 9, None, 5, p, p, None, None) == -4
+    assert L(p, 2, 4, 10, 10, None, 5, p, p, None, None) == -5

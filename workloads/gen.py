@@ -100,6 +100,7 @@ class Workload:
     step: int                   # sampling step
     rows: np.ndarray            # original row indices of the rows held here
     greedy_only: bool           # the workload is an argmax-only batch
+    top_n: int = 0              # > 0: a top-n logprobs batch (temperature from params)
 
     @property
     def nbytes_logits(self) -> int:
@@ -128,6 +129,7 @@ _SPECS = {
     "zipf_b256_bf16_t0.7_k50_p0.9_minp0.05": ("zipf", "bf16", 256, 1, False),
     "zipf_b512_bf16_mixed_penalties": ("zipf", "bf16", 512, 2, False),
     "flat_b1024_f32_t1_p0.95": ("flat", "f32", 1024, 3, False),
+    "zipf_b256_bf16_top_logprobs20": ("zipf", "bf16", 256, 1, False),
 }
 WORKLOAD_NAMES = tuple(_SPECS)
 
@@ -140,6 +142,8 @@ def _params_row(name: str, seed: int, row: int, B: int) -> tuple:
         return (0.0, -1, 1.0, 0.0, 0.0, 0.0, 1.0)
     if name == "zipf_b256_bf16_t0.7_k50_p0.9_minp0.05":
         return (0.7, 50, 0.9, 0.05, 0.0, 0.0, 1.0)
+    if name == "zipf_b256_bf16_top_logprobs20":
+        return (0.7, -1, 1.0, 0.0, 0.0, 0.0, 1.0)
     if name == "flat_b1024_f32_t1_p0.95":
         return (1.0, -1, 0.95, 0.0, 0.0, 0.0, 1.0)
     if name == "zipf_b512_bf16_mixed_penalties":
@@ -188,4 +192,5 @@ def make_workload(name: str, B: Optional[int] = None, V: int = V_DEFAULT,
         hist_offsets = np.arange(n + 1, dtype=np.int64) * hist_len
     return Workload(name=name, B=B, V=V, dtype=dtype, logits=logits, params=params,
                     hist_ids=hist_ids, hist_offsets=hist_offsets, seed=seed, step=step,
-                    rows=rows, greedy_only=greedy)
+                    rows=rows, greedy_only=greedy,
+                    top_n=20 if name == "zipf_b256_bf16_top_logprobs20" else 0)
