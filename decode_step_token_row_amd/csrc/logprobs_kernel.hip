@@ -236,9 +236,24 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
     if (keep) surv[base + (uint32_t)__builtin_popcountll(mask & ((1ull << lane) - 1ull))] = tkey;
     __syncthreads();
     const int ns = (int)s_nsurv;
-    if (tid < ns) {
-      const uint64_t k = surv[tid];
-      const int rr = lp_rank(surv, ns, k, ns);
+    // a survivor's rank: up to 256 survivors take a quad of threads each,
+    // every thread counting over a quarter of the list
+    const int split = ns <= kLpNT / 4 ? 4 : 1;
+    const int si = tid / split, part = tid - si * split;
+    const int chunk = ((ns + 2 * split - 1) / (2 * split)) * 2;  // even: pair reads stay aligned
+    const int j0 = part * chunk < ns ? part * chunk : ns;
+    const int j1 = j0 + chunk < ns ? j0 + chunk : ns;
+    uint64_t k = 0ull;
+    int rr = 0;
+    if (si < ns) {
+      k = surv[si];
+      rr = lp_rank(surv + j0, j1 - j0, k, kLpCap);
+    }
+    if (split == 4) {
+      rr += __shfl_xor(rr, 1);
+      rr += __shfl_xor(rr, 2);
+    }
+    if (si < ns && part == 0) {
       if (rr == n - 1) s_beta = k;
       if (rr < n) s_owner[rr] = (int)((~(uint32_t)k) / (uint32_t)E) % kLpNT;
     }
