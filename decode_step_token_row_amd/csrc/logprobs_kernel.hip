@@ -191,9 +191,25 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
     }
   }
 
-  // ---- row maximum and normaliser ------------------------------------------------
+  // ---- row maximum and the wave bounds, normaliser and survivors ------------------
+  // thread keys: value order key << 32 | ~first id (distinct); each wave's
+  // n-th largest key by a descent over ballots: the largest p with n keys at
+  // or above it.  With fewer threads holding elements than n, every element
+  // is a candidate (beta = 0).
+  const uint64_t tkey = owns ? lp_key(mt, first) : 0ull;
+  const bool few = ngroups < n;
+  uint64_t p = 0ull;
+  if (!few) {
+#pragma unroll
+    for (int b = 63; b >= 0; --b) {
+      const uint64_t c1 = p | (1ull << b);
+      p = __builtin_popcountll(__ballot(tkey >= c1)) >= n ? c1 : p;
+    }
+  }
   const float wm = dpp_wave_max_f32(mt);
-  if (lane == 0) s_max[wid] = wm;
+  if (lane == 0) { s_max[wid] = wm; s_wbound[wid] = p; }
+  if (tid == 0) { s_cnt = 0u; s_nsurv = 0u; }
+  if (few && tid < ngroups) s_owner[tid] = tid;
   __syncthreads();
   float m = s_max[0];
 #pragma unroll
@@ -201,30 +217,9 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   const double f = mt == m ? 1.0 : exp2(((double)mt - (double)m) * cd);
   const double ws = dpp_wave_sum_f64(owns ? s * f : 0.0);
   if (lane == 0) s_sum[wid] = ws;
-  if (tid == 0) { s_cnt = 0u; s_nsurv = 0u; }
-  __syncthreads();
-  double S = 0.0;
-#pragma unroll
-  for (int w = 0; w < kLpNW; ++w) S += s_sum[w];
-  const double lnS = log(S);
-
-  // ---- beta: the n-th largest thread maximum ----------------------------------
-  const uint64_t tkey = owns ? lp_key(mt, first) : 0ull;
-  uint64_t beta = 0ull;  // fewer threads hold elements than n: all are candidates
-  int nown = ngroups < n ? ngroups : n;
-  if (ngroups < n) {
-    if (tid < ngroups) s_owner[tid] = tid;
-    __syncthreads();
-  } else {
-    // the wave's n-th largest key: the largest p with n keys at or above it
-    uint64_t p = 0ull;
-#pragma unroll
-    for (int b = 63; b >= 0; --b) {
-      const uint64_t c1 = p | (1ull << b);
-      p = __builtin_popcountll(__ballot(tkey >= c1)) >= n ? c1 : p;
-    }
-    if (lane == 0) s_wbound[wid] = p;
-    __syncthreads();
+  if (!few) {
+    // the largest wave bound is a lower bound for beta: the keys at or above
+    // it (at most n per wave) go to LDS
     uint64_t lb = s_wbound[0];
 #pragma unroll
     for (int w = 1; w < kLpNW; ++w) lb = s_wbound[w] > lb ? s_wbound[w] : lb;
@@ -234,7 +229,17 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
     if (lane == 0 && mask) base = atomicAdd(&s_nsurv, (uint32_t)__builtin_popcountll(mask));
     base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
     if (keep) surv[base + (uint32_t)__builtin_popcountll(mask & ((1ull << lane) - 1ull))] = tkey;
-    __syncthreads();
+  }
+  __syncthreads();
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kLpNW; ++w) S += s_sum[w];
+  const double lnS = log(S);
+
+  // ---- beta: the n-th largest thread key ----------------------------------------
+  uint64_t beta = 0ull;
+  const int nown = few ? ngroups : n;
+  if (!few) {
     const int ns = (int)s_nsurv;
     // a survivor's rank: up to 256 survivors take a quad of threads each,
     // every thread counting over a quarter of the list
