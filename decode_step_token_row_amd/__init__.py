@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     ROW_PARAMS_DTYPE,
     ROW_STATS_DTYPE,
     argmax,
+    commit_tokens,
     library,
     make_key,
     params_to_device,

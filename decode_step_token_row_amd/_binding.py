@@ -89,6 +89,8 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_keyed.restype = c_i
         lib.arcs_top_logprobs.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_i, c_p, c_p, c_p, c_p]
         lib.arcs_top_logprobs.restype = c_i
+        lib.arcs_commit_tokens.argtypes = [c_p, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_p, c_p, c_p, c_p]
+        lib.arcs_commit_tokens.restype = c_i
         lib.arcs_sample_workspace_bytes.argtypes = [c_i64, c_i64, c_i]
         lib.arcs_sample_workspace_bytes.restype = ctypes.c_size_t
         lib.arcs_status_string.argtypes = [c_i]
@@ -199,6 +201,35 @@ def top_logprobs(logits, n: int, temperature=None, out_ids=None, out_logprobs=No
     if st != OK:
         raise ArcsError(st, "arcs_top_logprobs")
     return out_ids, out_logprobs
+
+
+def commit_tokens(ids, V: int, position, ring, published, drained, fault, next_input=None, stream=None):
+    """arcs_commit_tokens: publish one step's tokens into a pinned host ring.
+
+    ``ids`` device int32 [B]; ``position`` device int64 [1]; ``ring`` pinned
+    CPU int32 [capacity, B]; ``published`` and ``drained`` pinned CPU int64
+    [1]; ``fault`` pinned CPU int32 [1]; ``next_input`` device int32 [B] or None.
+    """
+    torch = _torch()
+    B = ids.numel()
+    if not ids.is_cuda or ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous device int32 tensor")
+    if not position.is_cuda or position.dtype != torch.int64 or position.numel() != 1:
+        raise ValueError("position must be a device int64 tensor of one element")
+    for name, t, dt in (("ring", ring, torch.int32), ("published", published, torch.int64),
+                        ("drained", drained, torch.int64), ("fault", fault, torch.int32)):
+        if t.is_cuda or not t.is_pinned() or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous pinned CPU tensor of {dt}")
+    if ring.numel() % B != 0:
+        raise ValueError("ring must hold capacity * B elements")
+    if next_input is not None and (not next_input.is_cuda or next_input.dtype != torch.int32
+                                   or next_input.numel() != B):
+        raise ValueError("next_input must be a device int32 tensor of B elements")
+    st = library().arcs_commit_tokens(_ptr(ids), B, int(V), _ptr(next_input), _ptr(position), _ptr(ring),
+                                      ring.numel() // B, _ptr(published), _ptr(drained), _ptr(fault),
+                                      _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_commit_tokens")
 
 
 def _check_params(params, B):

@@ -167,6 +167,7 @@ const char* arcs_status_string(int code) {
     case ARCS_ERR_MISALIGNED: return "logits pointer not aligned to its element size";
     case ARCS_ERR_BAD_HISTORY: return "hist_ids and hist_offsets must both be NULL or both be set";
     case ARCS_ERR_BAD_TOP_N: return "n must be in [1, ARCS_MAX_TOP_LOGPROBS]";
+    case ARCS_ERR_BAD_CAPACITY: return "ring capacity must be >= 1 and capacity * B must fit int64";
     case ARCS_ROW_BAD_TEMPERATURE: return "row: temperature is NaN or negative";
     case ARCS_ROW_BAD_TOP_P: return "row: top_p is NaN or <= 0";
     case ARCS_ROW_BAD_MIN_P: return "row: min_p is NaN or outside [0, 1]";

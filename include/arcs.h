@@ -51,7 +51,8 @@ typedef enum arcs_status {
   ARCS_ERR_LAUNCH = -7,              /* the HIP runtime rejected a launch       */
   ARCS_ERR_MISALIGNED = -8,          /* logits not aligned to the element size  */
   ARCS_ERR_BAD_HISTORY = -9,         /* exactly one of hist_ids/hist_offsets is NULL */
-  ARCS_ERR_BAD_TOP_N = -10           /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
+  ARCS_ERR_BAD_TOP_N = -10,          /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
+  ARCS_ERR_BAD_CAPACITY = -11        /* arcs_commit_tokens: capacity 0, or capacity * B too large */
 } arcs_status;
 
 /* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
@@ -70,6 +71,13 @@ enum {
  * in [0, V) (the number of history entries itself is not limited) and V. */
 #define ARCS_MAX_HISTORY 4096
 #define ARCS_MAX_PENALTY_VOCAB 262144
+
+/* Codes arcs_commit_tokens latches into its fault word (the first one stays). */
+enum {
+  ARCS_FAULT_NONE = 0,
+  ARCS_FAULT_TOKEN_RANGE = 1,        /* a token outside [0, V)                          */
+  ARCS_FAULT_RING_OVERRUN = 2        /* the ring slot still holds a step not drained yet */
+};
 
 /* Limits of arcs_top_logprobs: entries per row, and V. */
 #define ARCS_MAX_TOP_LOGPROBS 64
@@ -241,6 +249,38 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
 int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                       const float* temperature, int n, int32_t* out_ids, float* out_logprobs,
                       int32_t* out_status, void* stream);
+
+/*
+ * arcs_commit_tokens: publish the tokens of one decode step to the host
+ * without a synchronisation (Arc PR #217, "What this does", step 3: the
+ * token goes into the next step's input buffer, the device position moves on
+ * and the token is published into a pinned, mapped host ring; the fault
+ * handling there: the commit range-checks token and position before writing
+ * anything and latches a code into a pinned fault word).  One launch:
+ *   p = *position;
+ *   refused, with *fault set to the code if it was ARCS_FAULT_NONE, when a
+ *   token is outside [0, V) (ARCS_FAULT_TOKEN_RANGE) or the slot p % capacity
+ *   still holds a step the host has not drained, p - *drained >= capacity
+ *   (ARCS_FAULT_RING_OVERRUN); also refused, silently, while *fault is set
+ *   (a latched fault stops publication until the host clears it); nothing
+ *   else is written then;
+ *   otherwise next_input[b] = ids[b] (if next_input is not NULL),
+ *   ring[(p % capacity) * B + b] = ids[b], then, after a system-scope fence,
+ *   *published = p + 1 and *position = p + 1.
+ *   ids          device, int32[B] (e.g. out_ids of arcs_sample)
+ *   next_input   device, int32[B], or NULL
+ *   position     device, uint64: the step counter
+ *   ring         pinned host memory (hipHostMalloc), int32[capacity * B]
+ *   published    pinned host memory, uint64: steps whose tokens are in the ring
+ *   drained      pinned host memory, uint64, written by the host: steps consumed
+ *   fault        pinned host memory, uint32, sticky; the host clears it
+ * The host polls *published and *fault with plain volatile loads.  Calls on
+ * one stream run in order; the ring and words belong to that stream.
+ * Returns ARCS_OK or a negative arcs_status (nothing launched then).
+ */
+int arcs_commit_tokens(const int32_t* ids, int64_t B, int64_t V, int32_t* next_input, uint64_t* position,
+                       int32_t* ring, uint64_t capacity, uint64_t* published, const uint64_t* drained,
+                       uint32_t* fault, void* stream);
 
 int arcs_version(void);
 

@@ -18,7 +18,8 @@ def arcs():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
-                 "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs"):
+                 "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs",
+                 "arcs_commit_tokens"):
         assert name in fns
 
 
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol(arcs):
 
 
 def test_status_strings_and_version(arcs):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, 1, 2, 3, 4, 5, 6, 7]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, 1, 2, 3, 4, 5, 6, 7]:
         assert arcs.status_string(code) != "unknown status", code
     assert arcs.status_string(12345) == "unknown status"
     assert arcs.version() >= 100
@@ -84,3 +85,13 @@ def test_host_validation_rejects_before_launch(arcs):
     assert L(p, 0, 4, 10, 10, ctypes.c_void_p(base + 2), 5, p, p, None, None) == -8
     assert L(p, 0, 4, 10, 9, None, 5, p, p, None, None) == -4
     assert L(p, 2, 4, 10, 10, None, 5, p, p, None, None) == -5
+    # token commit: every word but next_input required, capacity >= 1, alignment
+    C = lib.arcs_commit_tokens
+    assert C(None, 4, 10, None, p, p, 2, p, p, p, None) == -1
+    assert C(p, 4, 10, None, p, p, 2, p, None, p, None) == -1
+    assert C(p, 4, 10, None, p, p, 2, p, p, None, None) == -1
+    assert C(p, 0, 10, None, p, p, 2, p, p, p, None) == -2
+    assert C(p, 4, 0, None, p, p, 2, p, p, p, None) == -3
+    assert C(p, 4, 10, None, p, p, 0, p, p, p, None) == -11
+    assert C(p, 4, 10, None, ctypes.c_void_p(base + 4), p, 2, p, p, p, None) == -8
+    assert C(ctypes.c_void_p(base + 2), 4, 10, None, p, p, 2, p, p, p, None) == -8
