@@ -11,11 +11,14 @@
 // output: the first n ids of the order (z descending, id ascending) and
 // their logprobs.
 //
-// One HBM pass.  Each thread keeps its largest value with the first id that
+// One HBM pass.  Each thread keeps its largest value with the first unit that
 // holds it, and an online sum of its weights relative to its own maximum,
 // rescaled when that maximum grows, so the normaliser needs no second pass.
-// The thread maxima become 64-bit keys (value order key << 32 | ~id, all
-// distinct).  The n-th largest of them, beta, is a lower bound for the n-th
+// The bound works at unit granularity: an element's coarse key is its value
+// order key << 32 | ~(first id of its unit), and the thread maxima become
+// such keys (distinct across threads).  The order (value desc, id asc) only
+// refines the coarse order, so the row's n first elements all have coarse
+// keys at or above the n-th largest thread key.  The n-th largest of them, beta, is a lower bound for the n-th
 // element of the row, and only the n threads whose maximum reaches it can
 // hold elements at or above it.  beta is found without sorting: each wave
 // finds the n-th largest of its 64 keys by a bitwise descent over ballots;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   // wrong or NaN, and such a thread recounts its weights exactly after the pass.
   float mt = -__builtin_inff();
   double s = 0.0;
-  uint32_t first = (uint32_t)tid * E;
+  uint32_t first = (uint32_t)tid * E;  // first id of the first unit holding mt
   for (int q0 = 0; q0 < nq; q0 += kLpBatch) {
     // unconditional loads (a lane past the row's end reads its last unit
     // again and ignores it): a branch per load would serialise them
@@ -160,16 +163,12 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
       float z[E];
       U::unpack(d[r], z);
       float gm = -__builtin_inff();
-      int ef = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ef = z[e] > gm ? e : ef;
-        gm = z[e] > gm ? z[e] : gm;
-      }
+      for (int e = 0; e < E; ++e) gm = __builtin_fmaxf(gm, z[e]);  // ignores NaN
       if (gm > mt) {
         s *= (double)__builtin_amdgcn_exp2f((mt - gm) * c);  // 0 when mt is -inf or gm is +inf
         mt = gm;
-        first = (uint32_t)g * E + (uint32_t)ef;
+        first = (uint32_t)g * E;
       }
       float ws = 0.0f;
 #pragma unroll
@@ -192,7 +191,7 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   }
 
   // ---- row maximum and the wave bounds, normaliser and survivors ------------------
-  // thread keys: value order key << 32 | ~first id (distinct); each wave's
+  // thread keys (coarse): value order key << 32 | ~(first id of the unit); each wave's
   // n-th largest key by a descent over ballots: the largest p with n keys at
   // or above it.  With fewer threads holding elements than n, every element
   // is a candidate (beta = 0).
@@ -277,10 +276,9 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
     if (gm >= vb) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const uint64_t k = lp_key(z[e], (uint32_t)g * E + (uint32_t)e);
-        if (k >= beta) {
+        if (lp_key(z[e], (uint32_t)g * E) >= beta) {  // coarse key: the unit's first id
           const uint32_t slot = atomicAdd(&s_cnt, 1u);
-          if (slot < (uint32_t)kLpCap) cand[slot] = k;
+          if (slot < (uint32_t)kLpCap) cand[slot] = lp_key(z[e], (uint32_t)g * E + (uint32_t)e);
         }
       }
     }
