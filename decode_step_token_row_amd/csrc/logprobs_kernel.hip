@@ -11,23 +11,26 @@
 // output: the first n ids of the order (z descending, id ascending) and
 // their logprobs.
 //
-// One HBM pass.  Each thread keeps its largest value with the first unit that
-// holds it, and an online sum of its weights relative to its own maximum,
-// rescaled when that maximum grows, so the normaliser needs no second pass.
+// One HBM pass.  Each thread keeps its largest value with the first unit
+// that holds it, and an online sum of its weights relative to its own
+// maximum, rescaled when that maximum grows, so the normaliser needs no
+// second pass.
+//
 // The bound works at unit granularity: an element's coarse key is its value
 // order key << 32 | ~(first id of its unit), and the thread maxima become
 // such keys (distinct across threads).  The order (value desc, id asc) only
-// refines the coarse order, so the row's n first elements all have coarse
-// keys at or above the n-th largest thread key.  The n-th largest of them, beta, is a lower bound for the n-th
-// element of the row, and only the n threads whose maximum reaches it can
-// hold elements at or above it.  beta is found without sorting: each wave
-// finds the n-th largest of its 64 keys by a bitwise descent over ballots;
-// the largest of those 16 values is a lower bound for beta, the keys at or
-// above it (at most n per wave, about n in all) go to LDS, and their ranks
-// among themselves are their ranks in the row.  The units of those n threads are read again (from cache), spread
-// over the whole workgroup, and their elements at or above beta gathered
-// into LDS (at most n * 128); each candidate's rank among the candidates is
-// its position in the output.
+// refines the coarse order, so the row's first n elements all have coarse
+// keys at or above beta, the n-th largest thread key, and only the n threads
+// whose key reaches beta can hold them.  beta is found without sorting: each
+// wave finds the n-th largest of its 64 keys by a bitwise descent over
+// ballots; the largest of those 16 values bounds beta from below; the keys at
+// or above it (at most n per wave) go to LDS, and the one of rank n - 1 among
+// them, counted by quads of threads, is beta.
+//
+// The units of those n threads are read again (from cache), spread over the
+// whole workgroup, and their elements with coarse key at or above beta are
+// gathered into LDS with their exact keys (at most n * 128); each
+// candidate's rank among the candidates is its position in the output.
 #include <atomic>
 #include <type_traits>
 
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   const int ngroups = (int)(VEC ? a.V / E : a.V);
   const int nq = (ngroups + kLpNT - 1) / kLpNT;
 
-  // ---- the pass: thread maximum (first id) and weights relative to it -------
+  // ---- the pass: thread maximum (first unit) and weights relative to it -----
   // A NaN never wins a comparison, so the maximum is that of the row with NaN
   // as -inf; a NaN weight, or an infinite maximum (inf - inf), leaves s
   // wrong or NaN, and such a thread recounts its weights exactly after the pass.
