@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   __shared__ double s_sum[kLpNW];
   __shared__ uint64_t s_beta;
   __shared__ uint32_t s_cnt, s_nsurv;
-  __shared__ uint64_t s_wbound[kLpNW], s_wbound4[kLpNW];
+  __shared__ uint64_t s_wbound[kLpNW], s_wbound8[kLpNW];
   __shared__ int s_owner[ARCS_MAX_TOP_LOGPROBS];  // the threads whose maximum reaches beta
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -200,21 +200,21 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   // is a candidate (beta = 0).
   const uint64_t tkey = owns ? lp_key(mt, first) : 0ull;
   const bool few = ngroups < n;
-  // Also each wave's ceil(n/4)-th largest key: four waves with that many keys
-  // at or above a value put n keys there, so the 4th largest of those 16
+  // Also each wave's ceil(n/8)-th largest key: eight waves with that many
+  // keys at or above a value put n keys there, so the 8th largest of those 16
   // values is a lower bound for beta too, and usually a much higher one.
-  uint64_t p = 0ull, p4 = 0ull;
+  uint64_t p = 0ull, p8 = 0ull;
   if (!few) {
-    const int n4 = (n + 3) / 4;
+    const int n8 = (n + 7) / 8;
 #pragma unroll
     for (int b = 63; b >= 0; --b) {
-      const uint64_t c1 = p | (1ull << b), c4 = p4 | (1ull << b);
+      const uint64_t c1 = p | (1ull << b), c8 = p8 | (1ull << b);
       p = __builtin_popcountll(__ballot(tkey >= c1)) >= n ? c1 : p;
-      p4 = __builtin_popcountll(__ballot(tkey >= c4)) >= n4 ? c4 : p4;
+      p8 = __builtin_popcountll(__ballot(tkey >= c8)) >= n8 ? c8 : p8;
     }
   }
   const float wm = dpp_wave_max_f32(mt);
-  if (lane == 0) { s_max[wid] = wm; s_wbound[wid] = p; s_wbound4[wid] = p4; }
+  if (lane == 0) { s_max[wid] = wm; s_wbound[wid] = p; s_wbound8[wid] = p8; }
   if (tid == 0) { s_cnt = 0u; s_nsurv = 0u; }
   if (few && tid < ngroups) s_owner[tid] = tid;
   __syncthreads();
@@ -231,17 +231,17 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
 #pragma unroll
     for (int w = 1; w < kLpNW; ++w) lb = s_wbound[w] > lb ? s_wbound[w] : lb;
     {
-      // the 4th largest wave value of p4: raise lb to it (ties count once each)
+      // the 8th largest wave value of p8: raise lb to it (ties count once each)
       uint64_t v[kLpNW];
 #pragma unroll
-      for (int w = 0; w < kLpNW; ++w) v[w] = s_wbound4[w];
+      for (int w = 0; w < kLpNW; ++w) v[w] = s_wbound8[w];
       uint64_t x = 0ull;
 #pragma unroll
       for (int w = 0; w < kLpNW; ++w) {
         int above = 0;  // values strictly above v[w], and equal ones before it
 #pragma unroll
         for (int u = 0; u < kLpNW; ++u) above += (v[u] > v[w] || (v[u] == v[w] && u < w)) ? 1 : 0;
-        x = above == 3 ? v[w] : x;
+        x = above == 7 ? v[w] : x;
       }
       lb = x > lb ? x : lb;
     }
