@@ -22,10 +22,11 @@
 // refines the coarse order, so the row's first n elements all have coarse
 // keys at or above beta, the n-th largest thread key, and only the n threads
 // whose key reaches beta can hold them.  beta is found without sorting: each
-// wave finds the n-th largest of its 64 keys by a bitwise descent over
-// ballots; the largest of those 16 values bounds beta from below; the keys at
-// or above it (at most n per wave) go to LDS, and the one of rank n - 1 among
-// them, counted by quads of threads, is beta.
+// wave finds the n-th and the ceil(n/8)-th largest of its 64 keys by bitwise
+// descents over ballots; the largest of the first 16 values and the 8th
+// largest of the second 16 both bound beta from below; the keys at or above
+// the higher bound (at most n per wave) go to LDS, and the one of rank n - 1
+// among them, counted by quads of threads, is beta.
 //
 // The units of those n threads are read again (from cache), spread over the
 // whole workgroup, and their elements with coarse key at or above beta are
