@@ -165,3 +165,36 @@ def test_top_logprobs_full_size_sampled_rows(arcs):
     assert (np.exp(lps.astype(np.float64)).sum(axis=1) <= 1.0 + 1e-5).all()
     rows = sorted(set(np.random.default_rng(0).choice(w.B, 12, replace=False).tolist()) | {0, w.B - 1})
     _check(ids, lps, st, w.logits, "bf16", temps, w.top_n, rows=rows, where="full")
+
+
+def test_top_logprobs_graph_replays_match_eager(arcs):
+    # captured once, replayed over logits rewritten in place between replays
+    import torch
+    B, V, n = 16, 20_000, 12
+    rows = [_rows(V, B, seed=s) for s in (21, 22, 23)]
+    x = to_device_logits(f32_to_bf16_bits(rows[0]), "bf16")
+    temps = torch.from_numpy(np.linspace(0.3, 1.7, B).astype(np.float32)).cuda()
+    ids = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    lps = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        arcs.top_logprobs(x, n, temperature=temps, out_ids=ids, out_logprobs=lps)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arcs.top_logprobs(x, n, temperature=temps, out_ids=ids, out_logprobs=lps)
+    for r in range(6):
+        z = rows[r % 3]
+        x.copy_(to_device_logits(f32_to_bf16_bits(z), "bf16"))
+        g.replay()
+        torch.cuda.synchronize()
+        want_ids, want_lps = arcs.top_logprobs(x, n, temperature=temps)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, want_ids), r
+        assert torch.equal(lps, want_lps), r
+        if r == 0:
+            raw = f32_to_bf16_bits(z)
+            _check(ids.cpu().numpy(), lps.cpu().numpy(), np.zeros(B, np.int32), raw, "bf16",
+                   temps.cpu().numpy(), n, rows=[0, 7, 15], where="graph")
