@@ -22,11 +22,11 @@
 // refines the coarse order, so the row's first n elements all have coarse
 // keys at or above beta, the n-th largest thread key, and only the n threads
 // whose key reaches beta can hold them.  beta is found without sorting: each
-// wave finds the n-th and the ceil(n/8)-th largest of its 64 keys by bitwise
-// descents over ballots; the largest of the first 16 values and the 8th
-// largest of the second 16 both bound beta from below; the keys at or above
-// the higher bound (at most n per wave) go to LDS, and the one of rank n - 1
-// among them, counted by quads of threads, is beta.
+// wave finds the n-th and the ceil(n/8)-th largest value halves of its 64
+// keys by bitwise descents over ballots; the largest of the first 16 values
+// and the 8th largest of the second 16 both bound beta from below; the keys
+// at or above the higher bound go to LDS, and the one of rank n - 1 among
+// them, counted by quads of threads, is beta.
 //
 // The units of those n threads are read again (from cache), spread over the
 // whole workgroup, and their elements with coarse key at or above beta are
@@ -204,18 +204,22 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   // Also each wave's ceil(n/8)-th largest key: eight waves with that many
   // keys at or above a value put n keys there, so the 8th largest of those 16
   // values is a lower bound for beta too, and usually a much higher one.
-  uint64_t p = 0ull, p8 = 0ull;
+  // The descents run on the value half of the keys (32 steps): n keys with
+  // value key >= v are n keys >= v << 32, so the bounds stay valid; value
+  // ties can let more keys survive, never more than the 1024 thread keys.
+  uint32_t p = 0u, p8 = 0u;
   if (!few) {
     const int n8 = (n + 7) / 8;
+    const uint32_t th = (uint32_t)(tkey >> 32);
 #pragma unroll
-    for (int b = 63; b >= 0; --b) {
-      const uint64_t c1 = p | (1ull << b), c8 = p8 | (1ull << b);
-      p = __builtin_popcountll(__ballot(tkey >= c1)) >= n ? c1 : p;
-      p8 = __builtin_popcountll(__ballot(tkey >= c8)) >= n8 ? c8 : p8;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c1 = p | (1u << b), c8 = p8 | (1u << b);
+      p = __builtin_popcountll(__ballot(th >= c1)) >= n ? c1 : p;
+      p8 = __builtin_popcountll(__ballot(th >= c8)) >= n8 ? c8 : p8;
     }
   }
   const float wm = dpp_wave_max_f32(mt);
-  if (lane == 0) { s_max[wid] = wm; s_wbound[wid] = p; s_wbound8[wid] = p8; }
+  if (lane == 0) { s_max[wid] = wm; s_wbound[wid] = (uint64_t)p << 32; s_wbound8[wid] = (uint64_t)p8 << 32; }
   if (tid == 0) { s_cnt = 0u; s_nsurv = 0u; }
   if (few && tid < ngroups) s_owner[tid] = tid;
   __syncthreads();
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   if (lane == 0) s_sum[wid] = ws;
   if (!few) {
     // the largest wave bound is a lower bound for beta: the keys at or above
-    // it (at most n per wave) go to LDS
+    // it (at most n per wave, save value ties) go to LDS
     uint64_t lb = s_wbound[0];
 #pragma unroll
     for (int w = 1; w < kLpNW; ++w) lb = s_wbound[w] > lb ? s_wbound[w] : lb;
