@@ -174,13 +174,6 @@ constexpr int kFastQ = 32;
 constexpr int64_t kFastGroups = (int64_t)kFastNT * kFastQ;
 static_assert(kFastQ <= 32, "round codes and the round switch cover 32 rounds");
 
-__device__ __forceinline__ s16x2 as_s16x2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
-__device__ __forceinline__ uint32_t pk_max_u(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2(a), as_s16x2(b)));
-}
-__device__ __forceinline__ uint32_t pk_min_u(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_s16x2(a), as_s16x2(b)));
-}
 
 __global__ __launch_bounds__(kFastNT) void argmax_fast_kernel(const void* __restrict__ logits, int64_t V,
                                                               int64_t stride, int32_t* __restrict__ out) {

@@ -54,6 +54,14 @@ __device__ __forceinline__ s16x2 bf16x2_keys(uint32_t x) {
 }
 __device__ __forceinline__ s16x2 max2(s16x2 a, s16x2 b) { return __builtin_elementwise_max(a, b); }
 __device__ __forceinline__ int max_halves(s16x2 a) { return a.x > a.y ? (int)a.x : (int)a.y; }
+// Packed signed 16-bit max / min of two pairs of raw bf16 patterns.
+__device__ __forceinline__ s16x2 as_s16x2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
+__device__ __forceinline__ uint32_t pk_max_u(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2(a), as_s16x2(b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_s16x2(a), as_s16x2(b)));
+}
 __device__ __forceinline__ int f32_key_signed(uint32_t b) {
   return (int)(b ^ ((uint32_t)((int32_t)b >> 31) & 0x7FFFFFFFu));
 }
@@ -215,6 +223,16 @@ __device__ __forceinline__ int dpp_wave_max_i32(int v) {
   t = (int)dpp_u32<0x142, 0xA>(id, (uint32_t)v); v = v > t ? v : t;
   t = (int)dpp_u32<0x143, 0xC>(id, (uint32_t)v); v = v > t ? v : t;
   return __builtin_amdgcn_readlane(v, 63);
+}
+// bitwise OR across the wave (same value in every lane)
+__device__ __forceinline__ uint32_t dpp_wave_or_u32(uint32_t v) {
+  v |= dpp_u32<0xB1>(0u, v);
+  v |= dpp_u32<0x4E>(0u, v);
+  v |= dpp_u32<0x141>(0u, v);
+  v |= dpp_u32<0x140>(0u, v);
+  v |= dpp_u32<0x142, 0xA>(0u, v);
+  v |= dpp_u32<0x143, 0xC>(0u, v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // sum across the wave (same value in every lane)
 __device__ __forceinline__ uint32_t dpp_wave_sum_u32(uint32_t v) {

@@ -214,6 +214,7 @@ struct BlockScratch {
   uint32_t u32[kNW];
 };
 
+template <int NT>
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& bs) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   v = wave_sum_u64(v);
@@ -222,11 +223,12 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, BlockScratch& bs) 
   __syncthreads();
   uint64_t t = 0;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) t += bs.u64[w];
+  for (int w = 0; w < (NT / kWave); ++w) t += bs.u64[w];
   return t;
 }
 
 // inclusive block scan; also returns the block total
+template <int NT>
 __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, BlockScratch& bs, uint64_t& total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   v = wave_incl_scan_u64(v, lane);
@@ -235,7 +237,7 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, BlockScratch
   __syncthreads();
   uint64_t off = 0, t = 0;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) {
+  for (int w = 0; w < (NT / kWave); ++w) {
     uint64_t x = bs.u64[w];
     off += (w < wid) ? x : 0;
     t += x;
@@ -253,7 +255,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool LDS_ONLY = false>
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_incl_scan_u32(uint32_t v, BlockScratch& bs, uint32_t& total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   v = wave_incl_scan_u32(v, lane);
@@ -262,7 +264,7 @@ __device__ __forceinline__ uint32_t block_incl_scan_u32(uint32_t v, BlockScratch
   if (LDS_ONLY) lds_barrier(); else __syncthreads();
   uint32_t off = 0, t = 0;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) {
+  for (int w = 0; w < (NT / kWave); ++w) {
     uint32_t x = bs.u32[w];
     off += (w < wid) ? x : 0;
     t += x;
@@ -275,21 +277,21 @@ __device__ __forceinline__ uint32_t block_incl_scan_u32(uint32_t v, BlockScratch
 // [t*kNT*EPL, (t+1)*kNT*EPL) and thread i the EPL ids starting at
 // (t*kNT + i)*EPL.  f(g0, z[], n) is called for this thread's group of each
 // tile (n may be 0 past the end; f must then do nothing).
-template <bool BF16, bool VEC, class Fn>
+template <int NT, bool BF16, bool VEC, class Fn>
 __device__ __forceinline__ void for_each_group(const char* rowp, int64_t V, const PenCtx& pc, Fn&& f) {
   constexpr int EPL = Group<BF16>::EPL;
-  const int64_t tile_elems = (int64_t)kNT * EPL;
+  const int64_t tile_elems = (int64_t)NT * EPL;
   const int64_t ntiles = (V + tile_elems - 1) / tile_elems;
   for (int64_t t0 = 0; t0 < ntiles; t0 += kTileUnroll) {
     Group<BF16> g[kTileUnroll];
 #pragma unroll
     for (int u = 0; u < kTileUnroll; ++u) {
-      int64_t g0 = ((t0 + u) * kNT + threadIdx.x) * EPL;
+      int64_t g0 = ((t0 + u) * NT + threadIdx.x) * EPL;
       load_group<BF16, VEC>(rowp, V, g0, g[u]);
     }
 #pragma unroll
     for (int u = 0; u < kTileUnroll; ++u) {
-      int64_t g0 = ((t0 + u) * kNT + threadIdx.x) * EPL;
+      int64_t g0 = ((t0 + u) * NT + threadIdx.x) * EPL;
       if (g[u].n > 0) {
         float z[EPL];
         decode_group<BF16>(g[u], g0, pc, z);
@@ -383,6 +385,7 @@ __device__ __forceinline__ int row_param_status(const arcs_row_params& P) {
 }
 
 // A row whose parameters or history failed: -1, its status, zeroed debug outputs.
+template <int NT>
 __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t row, int status) {
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -395,7 +398,7 @@ __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t r
     }
   }
   if (a.out_probs)
-    for (int64_t i = tid; i < a.V; i += kNT) a.out_probs[row * a.V + i] = 0.0f;
+    for (int64_t i = tid; i < a.V; i += NT) a.out_probs[row * a.V + i] = 0.0f;
 }
 
 // Parameter validation and penalty tables.  Returns false when the row is
@@ -406,7 +409,7 @@ __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t r
 // each bitmap word (a block scan of popcounts), and per distinct id its count
 // and its penalised logit, computed once here from the raw logit.  Looking
 // up an element is then one popcount and one LDS read.
-template <bool BF16, bool PEN>
+template <int NT, bool BF16, bool PEN>
 __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh,
                                              arcs_row_params& P, PenCtx& pc, uint32_t& path) {
   const int tid = threadIdx.x;
@@ -431,36 +434,36 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
 
   if (PEN && pc.on) {
     const uint32_t bw = a.bitmap_words;
-    for (uint32_t i = tid; i < bw; i += kNT) sm.bitmap[i] = 0u;
+    for (uint32_t i = tid; i < bw; i += NT) sm.bitmap[i] = 0u;
     __syncthreads();
-    for (int64_t i = h0 + tid; i < h1; i += kNT) {
+    for (int64_t i = h0 + tid; i < h1; i += NT) {
       const int32_t id = a.hist_ids[i];
       if (id >= 0 && (int64_t)id < V) atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31));
     }
     __syncthreads();
     // distinct ids before each word: contiguous chunks of words per thread
-    const uint32_t per = (bw + kNT - 1) / kNT;
+    const uint32_t per = (bw + NT - 1) / NT;
     const uint32_t w0 = tid * per, w1 = (w0 + per < bw) ? w0 + per : bw;
     uint32_t c = 0;
     for (uint32_t w = w0; w < w1; ++w) c += (uint32_t)__builtin_popcount(sm.bitmap[w]);
     uint32_t total;
-    const uint32_t incl = block_incl_scan_u32(c, sh.bs, total);
+    const uint32_t incl = block_incl_scan_u32<NT>(c, sh.bs, total);
     if (total <= (uint32_t)kMaxDistinct) {
       uint32_t run = incl - c;
       for (uint32_t w = w0; w < w1; ++w) {
         sm.wprefix[w] = (uint16_t)run;
         run += (uint32_t)__builtin_popcount(sm.bitmap[w]);
       }
-      for (uint32_t i = tid; i < total; i += kNT) sm.pcount[i] = 0u;
+      for (uint32_t i = tid; i < total; i += NT) sm.pcount[i] = 0u;
       __syncthreads();
-      for (int64_t i = h0 + tid; i < h1; i += kNT) {
+      for (int64_t i = h0 + tid; i < h1; i += NT) {
         const int32_t id = a.hist_ids[i];
         if (id >= 0 && (int64_t)id < V) atomicAdd(&sm.pcount[pen_rank((uint32_t)id, sm.bitmap, sm.wprefix)], 1u);
       }
       __syncthreads();
       // every occurrence of an id writes the same penalised value
       const char* rowp = (const char*)a.logits + row * a.stride * (BF16 ? 2 : 4);
-      for (int64_t i = h0 + tid; i < h1; i += kNT) {
+      for (int64_t i = h0 + tid; i < h1; i += NT) {
         const int32_t id = a.hist_ids[i];
         if (id >= 0 && (int64_t)id < V) {
           const uint32_t rk = pen_rank((uint32_t)id, sm.bitmap, sm.wprefix);
@@ -476,7 +479,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   }
 
   if (status != ARCS_ROW_OK) {
-    write_row_failure(a, row, status);
+    write_row_failure<NT>(a, row, status);
     return false;
   }
   path = pc.on ? ARCS_PATH_PENALTY : 0u;
@@ -485,7 +488,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
 
 // The general row pipeline from pass A on (see the file comment of
 // sample_kernel.hip).  All threads of the block call it together.
-template <bool BF16, bool VEC>
+template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, const arcs_row_params& P,
                                          const PenCtx& pc, uint32_t path, const Smem& sm, Shared& sh) {
   constexpr int EPL = Group<BF16>::EPL;
@@ -496,7 +499,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
   // ---- 1. pass A: max and first argmax -------------------------------------
   float best = -__builtin_inff();
   int64_t bidx = INT64_MAX;
-  for_each_group<BF16, VEC>(rowp, V, pc, [&](int64_t g0, const float* z, int n) {
+  for_each_group<NT, BF16, VEC>(rowp, V, pc, [&](int64_t g0, const float* z, int n) {
     for (int e = 0; e < n; ++e)
       if (z[e] > best) { best = z[e]; bidx = g0 + e; }
   });
@@ -507,7 +510,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
     __syncthreads();
     float m = sh.bs.f32[0];
 #pragma unroll
-    for (int w = 1; w < kNW; ++w) m = m > sh.bs.f32[w] ? m : sh.bs.f32[w];
+    for (int w = 1; w < (NT / kWave); ++w) m = m > sh.bs.f32[w] ? m : sh.bs.f32[w];
     if (best == m && bidx != INT64_MAX) atomicMin((unsigned long long*)&sh.u64[0], (unsigned long long)bidx);
     __syncthreads();
     if (tid == 0) { sh.f32[0] = m; sh.u64[1] = (m == -__builtin_inff()) ? 0 : sh.u64[0]; }
@@ -532,7 +535,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
       }
     }
     if (a.out_probs)
-      for (int64_t i = tid; i < V; i += kNT) a.out_probs[row * V + i] = (i == argmax) ? 1.0f : 0.0f;
+      for (int64_t i = tid; i < V; i += NT) a.out_probs[row * V + i] = (i == argmax) ? 1.0f : 0.0f;
     return;
   }
 
@@ -547,10 +550,10 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
   }
   const float scale = a.scale;
   uint64_t my_mass = 0;
-  for_each_group<BF16, VEC>(rowp, V, pc, [&](int64_t, const float* z, int n) {
+  for_each_group<NT, BF16, VEC>(rowp, V, pc, [&](int64_t, const float* z, int n) {
     for (int e = 0; e < n; ++e) my_mass += to_fixed(weight(z[e], wc), scale);
   });
-  const uint64_t S = block_sum_u64(my_mass, sh.bs);
+  const uint64_t S = block_sum_u64<NT>(my_mass, sh.bs);
 
   // ---- 3. cutoff -------------------------------------------------------------
   const bool kon = P.top_k >= 1 && (int64_t)P.top_k < V;
@@ -603,9 +606,9 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
       const int shf = key16 ? (lev == 0 ? 24 : 16) : (lev == 0 ? 21 : lev == 1 ? 10 : 0);
       const int bits = key16 ? 8 : (lev == 2 ? 10 : 11);
       const int nb = 1 << bits;
-      for (int i = tid; i < nb; i += kNT) { sm.hcnt[i] = 0u; sm.hmass[i] = 0ull; }
+      for (int i = tid; i < nb; i += NT) { sm.hcnt[i] = 0u; sm.hmass[i] = 0ull; }
       __syncthreads();
-      for_each_group<BF16, VEC>(rowp, V, pc, [&](int64_t, const float* z, int n) {
+      for_each_group<NT, BF16, VEC>(rowp, V, pc, [&](int64_t, const float* z, int n) {
         for (int e = 0; e < n; ++e) {
           uint32_t k = ord_key(z[e]);
           if (k < floor_key) continue;
@@ -686,10 +689,10 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
         // find the id of the r-th element (in id order) whose key is theta
         uint32_t running = 0;
         if (tid == 0) sh.u64[7] = (uint64_t)INT64_MAX;
-        const int64_t tile_elems = (int64_t)kNT * EPL;
+        const int64_t tile_elems = (int64_t)NT * EPL;
         const int64_t ntiles = (V + tile_elems - 1) / tile_elems;
         for (int64_t t = 0; t < ntiles; ++t) {
-          const int64_t g0 = (t * kNT + tid) * EPL;
+          const int64_t g0 = (t * NT + tid) * EPL;
           Group<BF16> g;
           load_group<BF16, VEC>(rowp, V, g0, g);
           float z[EPL];
@@ -699,7 +702,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
             for (int e = 0; e < g.n; ++e) c += ord_key(z[e]) == theta;
           }
           uint32_t tot;
-          uint32_t incl = block_incl_scan_u32(c, sh.bs, tot);
+          uint32_t incl = block_incl_scan_u32<NT>(c, sh.bs, tot);
           if ((uint64_t)running + tot >= r) {
             uint32_t excl = running + incl - c;
             if (c > 0 && excl < r && (uint64_t)running + incl >= r) {
@@ -734,10 +737,10 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
   {
     uint64_t running = 0;
     if (tid == 0) sh.u64[8] = (uint64_t)INT64_MAX;
-    const int64_t tile_elems = (int64_t)kNT * EPL;
+    const int64_t tile_elems = (int64_t)NT * EPL;
     const int64_t ntiles = (V + tile_elems - 1) / tile_elems;
     for (int64_t t = 0; t < ntiles; ++t) {
-      const int64_t g0 = (t * kNT + tid) * EPL;
+      const int64_t g0 = (t * NT + tid) * EPL;
       Group<BF16> g;
       load_group<BF16, VEC>(rowp, V, g0, g);
       float z[EPL];
@@ -751,7 +754,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
         }
       }
       uint64_t tot;
-      uint64_t incl = block_incl_scan_u64(c, sh.bs, tot);
+      uint64_t incl = block_incl_scan_u64<NT>(c, sh.bs, tot);
       if (running + tot > Tfix) {
         uint64_t acc = running + incl - c;
         if (c > 0 && acc <= Tfix && running + incl > Tfix) {
@@ -778,7 +781,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
     const double inv_sk = 1.0 / ((double)S_K * (double)(1.0f / scale));
     uint32_t kmin = 0xFFFFFFFFu;
     int64_t kmin_idx = -1;
-    for_each_group<BF16, VEC>(rowp, V, pc, [&](int64_t g0, const float* z, int n) {
+    for_each_group<NT, BF16, VEC>(rowp, V, pc, [&](int64_t g0, const float* z, int n) {
       for (int e = 0; e < n; ++e) {
         bool kept = is_kept(z[e], g0 + e, kc);
         if (a.out_probs)
