@@ -157,14 +157,21 @@ def params_to_device(params: np.ndarray, device="cuda"):
     return torch.from_numpy(arr.copy()).to(device)
 
 
+def _check_out(t, dtype, n: int, name: str):
+    """A caller-provided device buffer: dtype, element count and a dense layout
+    (the kernels write from the base pointer in row order)."""
+    torch = _torch()
+    if t.dtype != dtype or t.numel() != n or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device {dtype} tensor of {n} elements")
+
+
 def argmax(logits, out=None, stream=None):
     """out[b] = lowest index of the row maximum of logits[b] (int32, on device)."""
     torch = _torch()
     B, V, stride = _check_logits(logits)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=logits.device)
-    if out.dtype != torch.int32 or out.numel() != B or not out.is_cuda:
-        raise ValueError("out must be a device int32 tensor of B elements")
+    _check_out(out, torch.int32, B, "out")
     st = library().arcs_argmax(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(out), _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_argmax")
@@ -188,13 +195,13 @@ def top_logprobs(logits, n: int, temperature=None, out_ids=None, out_logprobs=No
         out_ids = torch.empty((B, n), dtype=torch.int32, device=dev)
     if out_logprobs is None:
         out_logprobs = torch.empty((B, n), dtype=torch.float32, device=dev)
-    if out_ids.dtype != torch.int32 or out_ids.numel() != B * n or not out_ids.is_cuda:
+    if out_ids.dtype != torch.int32 or out_ids.numel() != B * n or not out_ids.is_cuda or not out_ids.is_contiguous():
         raise ValueError("out_ids must be a device int32 tensor of B * n elements")
-    if out_logprobs.dtype != torch.float32 or out_logprobs.numel() != B * n or not out_logprobs.is_cuda:
+    if (out_logprobs.dtype != torch.float32 or out_logprobs.numel() != B * n or not out_logprobs.is_cuda
+            or not out_logprobs.is_contiguous()):
         raise ValueError("out_logprobs must be a device float32 tensor of B * n elements")
-    if out_status is not None and (out_status.dtype != torch.int32 or out_status.numel() != B
-                                   or not out_status.is_cuda):
-        raise ValueError("out_status must be a device int32 tensor of B elements")
+    if out_status is not None:
+        _check_out(out_status, torch.int32, B, "out_status")
     st = library().arcs_top_logprobs(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(temperature),
                                      int(n), _ptr(out_ids), _ptr(out_logprobs), _ptr(out_status),
                                      _stream_ptr(stream))
@@ -214,17 +221,15 @@ def commit_tokens(ids, V: int, position, ring, published, drained, fault, next_i
     B = ids.numel()
     if not ids.is_cuda or ids.dtype != torch.int32 or not ids.is_contiguous():
         raise ValueError("ids must be a contiguous device int32 tensor")
-    if not position.is_cuda or position.dtype != torch.int64 or position.numel() != 1:
-        raise ValueError("position must be a device int64 tensor of one element")
+    _check_out(position, torch.int64, 1, "position")
     for name, t, dt in (("ring", ring, torch.int32), ("published", published, torch.int64),
                         ("drained", drained, torch.int64), ("fault", fault, torch.int32)):
         if t.is_cuda or not t.is_pinned() or t.dtype != dt or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous pinned CPU tensor of {dt}")
     if ring.numel() % B != 0:
         raise ValueError("ring must hold capacity * B elements")
-    if next_input is not None and (not next_input.is_cuda or next_input.dtype != torch.int32
-                                   or next_input.numel() != B):
-        raise ValueError("next_input must be a device int32 tensor of B elements")
+    if next_input is not None:
+        _check_out(next_input, torch.int32, B, "next_input")
     st = library().arcs_commit_tokens(_ptr(ids), B, int(V), _ptr(next_input), _ptr(position), _ptr(ring),
                                       ring.numel() // B, _ptr(published), _ptr(drained), _ptr(fault),
                                       _stream_ptr(stream))
@@ -245,8 +250,7 @@ def _check_hist(hist_ids, hist_offsets, B):
     if hist_ids is not None:
         if hist_ids.dtype != torch.int32 or not hist_ids.is_cuda or not hist_ids.is_contiguous():
             raise ValueError("hist_ids must be a contiguous device int32 tensor")
-        if hist_offsets.dtype != torch.int64 or not hist_offsets.is_cuda or hist_offsets.numel() != B + 1:
-            raise ValueError("hist_offsets must be a device int64 tensor of B + 1 elements")
+        _check_out(hist_offsets, torch.int64, B + 1, "hist_offsets")
 
 
 def sample(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step: int = 0,
@@ -258,7 +262,12 @@ def sample(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step
     _check_hist(hist_ids, hist_offsets, B)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_out(out, torch.int32, B, "out")
+    if out_status is not None:
+        _check_out(out_status, torch.int32, B, "out_status")
     ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=logits.device)
@@ -293,7 +302,12 @@ def sample_keyed(logits, params, key, hist_ids=None, hist_offsets=None, advance:
         raise ValueError("key must be a contiguous device int64 tensor of 2 elements (seed, step)")
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_out(out, torch.int32, B, "out")
+    if out_status is not None:
+        _check_out(out_status, torch.int32, B, "out_status")
     ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if ws_need and workspace is None:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=logits.device)
@@ -320,8 +334,7 @@ def sample_debug(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0
     stats = torch.zeros(B * ROW_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
     probs = torch.empty((B, V), dtype=torch.float32, device=dev) if want_probs else None
     if uniforms is not None:
-        if uniforms.dtype != torch.float64 or not uniforms.is_cuda or uniforms.numel() != B:
-            raise ValueError("uniforms must be a device float64 tensor of B elements")
+        _check_out(uniforms, torch.float64, B, "uniforms")
     ws_need = workspace_bytes(B, V, _dtype_code(logits))
     workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev) if ws_need else None
     st = library().arcs_sample_debug(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),

@@ -36,7 +36,9 @@ __global__ __launch_bounds__(kCommitNT) void commit_tokens_kernel(const int32_t*
   int bad = 0;
   for (int64_t b = tid; b < B; b += kCommitNT) {
     const int32_t t = ids[b];
-    bad |= (t < 0 || (int64_t)t >= V) ? 1 : 0;
+    // -1 marks a row the sampler refused (its status says why): published as
+    // is, so one request's bad parameters do not stop the whole batch
+    bad |= ((t < 0 && t != -1) || (int64_t)t >= V) ? 1 : 0;
   }
   if (bad) s_bad = 1;  // any writer stores the same value
   __syncthreads();

@@ -161,6 +161,12 @@ __device__ __forceinline__ double readlane63_f64(double v) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, 63), hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), 63);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ double dpp_wave_sum_f64(double v) {
   v += dpp_f64<0xB1>(0.0, v);
   v += dpp_f64<0x4E>(0.0, v);
@@ -180,6 +186,26 @@ __device__ __forceinline__ float dpp_wave_max_f32(float v) {
   t = dpp_f32<0x142, 0xA>(ni, v); v = v > t ? v : t;
   t = dpp_f32<0x143, 0xC>(ni, v); v = v > t ? v : t;
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+// 2^t in double precision: t = n + f with n = rint(t) and |f| <= 1/2, 2^f
+// from the Taylor series of exp(f ln 2) to degree 9 (relative error about
+// 1e-11 over the interval), scaled by 2^n.  t below -1100, and -inf, give 0;
+// t above 1023 gives +inf.  The coefficients are (ln 2)^k / k!.
+__device__ __forceinline__ double exp2_f64(double t) {
+  t = t > -1100.0 ? t : -1100.0;
+  const double n = __builtin_rint(t);
+  const double f = t - n;
+  double p = 0x1.b5253d395e7c4p-24;
+  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
+  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
+  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
+  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
+  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
+  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
+  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
+  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
+  p = __builtin_fma(p, f, 1.0);
+  return __builtin_ldexp(p, (int)n);
 }
 // inclusive prefix sums across the wave (lane order)
 __device__ __forceinline__ double dpp_wave_incl_scan_f64(double v) {

@@ -25,22 +25,20 @@ constexpr int kBins = 256;                     // summary path: bound histogram 
 // Start of dynamic LDS ("union area"), used differently by the two paths:
 //   general path: radix histograms, counts [kMaxBins] u32 + masses [kMaxBins] u64;
 //   summary path: one f32 per group of the row, [kMaxGroups] (group j at
-//     j): its weight sum (rows without filters) or its maximum (filter
-//     rows); candidates (keys u64, weights f32) [kCandCap], or, for rows
-//     without filters (which gather no candidates), each thread's reference
-//     exponent [kNT] f32 at the same place; a bound histogram (counts u32,
-//     masses f32) [kBins]; a sorted copy of small candidate sets.
+//     j): its maximum (penalised filter rows) or its masked weight sum (min-p
+//     rows with many candidates), or for rows without filters each wave's
+//     double-precision weight total of each round; candidates (keys u64,
+//     weights f32) [kCandCap]; a bound histogram (counts u32, masses f32)
+//     [kBins]; a sorted copy of small candidate sets.
 constexpr size_t kUnionGeneric = (size_t)kMaxBins * 12;
 constexpr size_t kOffTsum = 0;
 constexpr size_t kOffCand = kOffTsum + (size_t)kMaxGroups * 4;
-constexpr size_t kOffKref = kOffCand;
 constexpr size_t kOffHist = kOffCand + (size_t)kCandCap * 12;
 constexpr size_t kOffSort = kOffHist + (size_t)kBins * 8;
 constexpr size_t kUnionSummary = kOffSort + (size_t)kSmallSort * 12;
 static_assert(kOffCand % 16 == 0 && kOffHist % 16 == 0 && kOffSort % 16 == 0,
               "summary LDS layout");
-static_assert((size_t)kCandCap * 12 >= (size_t)kMaxDistinct * 4 && (size_t)kCandCap * 12 >= (size_t)kNT * 4,
-              "the candidate area also holds the build-time counts and the reference exponents");
+static_assert((size_t)kCandCap * 12 >= (size_t)kMaxDistinct * 4, "the candidate area also holds the build-time counts");
 constexpr int64_t kMaxPenVocab = ARCS_MAX_PENALTY_VOCAB;
 
 // Dynamic LDS layout.
@@ -48,7 +46,6 @@ struct Smem {
   uint32_t* hcnt;      // [kMaxBins]               (general path)
   uint64_t* hmass;     // [kMaxBins]               (general path)
   float* tsum;         // [kMaxGroups] group weight sums or maxima (summary path)
-  float* kref;         // [kNT] per-thread reference exponents (summary path, no filter)
   uint64_t* ckey;      // [kCandCap] candidate sort keys   (summary path)
   float* cw;           // [kCandCap] candidate weights     (summary path)
   uint32_t* bcnt;      // [kBins] bound histogram counts   (summary path)
@@ -178,6 +175,8 @@ __device__ __forceinline__ void decode_group(const Group<BF16>& g, int64_t g0, c
 struct WeightCtx {
   float m, chi, clo;
   bool inf_row;
+  bool w64;   // rows without filters: weights in double precision
+  double c;   // log2(e) / T
 };
 __device__ __forceinline__ float weight(float z, const WeightCtx& wc) {
   if (wc.inf_row) return z == wc.m ? 1.0f : 0.0f;
@@ -186,6 +185,16 @@ __device__ __forceinline__ float weight(float z, const WeightCtx& wc) {
   float y = __builtin_fmaf(d, wc.chi, d * wc.clo);
   float w = __builtin_amdgcn_exp2f(y);
   return z == wc.m ? 1.0f : w;
+}
+
+// The weight in fixed point 2^-F.  Rows without filters compute it in double
+// precision, exp2((z - m) c): fp32 weights carry relative errors near 1e-7,
+// which on rows with heavy tokens ahead of long tails of tiny ones moves
+// many CDF boundaries by more than the tail tokens' widths.
+__device__ __forceinline__ uint64_t weight_fixed(float z, const WeightCtx& wc, float scale) {
+  if (!wc.w64 || wc.inf_row) return to_fixed(weight(z, wc), scale);
+  const double w = z == wc.m ? 1.0 : exp2_f64(((double)z - (double)wc.m) * wc.c);
+  return (uint64_t)(w * (double)scale);
 }
 
 // ceil(S * p) for p in (0, 1), exact (128-bit product).
@@ -326,7 +335,6 @@ __device__ __forceinline__ Smem carve_smem(unsigned char* raw, bool summary, uin
   sm.hcnt = (uint32_t*)raw;
   sm.hmass = (uint64_t*)(raw + (size_t)kMaxBins * 4);
   sm.tsum = (float*)(raw + kOffTsum);
-  sm.kref = (float*)(raw + kOffKref);
   sm.ckey = (uint64_t*)(raw + kOffCand);
   sm.cw = (float*)(raw + kOffCand + (size_t)kCandCap * 8);
   sm.bcnt = (uint32_t*)(raw + kOffHist);
@@ -547,11 +555,13 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
     wc.chi = (float)c;
     wc.clo = (float)(c - (double)wc.chi);
     wc.inf_row = (m == __builtin_inff());
+    wc.w64 = !(P.top_k >= 1 && (int64_t)P.top_k < V) && !(P.top_p < 1.0f) && !(P.min_p > 0.0f);
+    wc.c = c;
   }
   const float scale = a.scale;
   uint64_t my_mass = 0;
   for_each_group<NT, BF16, VEC>(rowp, V, pc, [&](int64_t, const float* z, int n) {
-    for (int e = 0; e < n; ++e) my_mass += to_fixed(weight(z[e], wc), scale);
+    for (int e = 0; e < n; ++e) my_mass += weight_fixed(z[e], wc, scale);
   });
   const uint64_t S = block_sum_u64<NT>(my_mass, sh.bs);
 
@@ -749,7 +759,7 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
       if (g.n > 0) {
         decode_group<BF16>(g, g0, pc, z);
         for (int e = 0; e < EPL; ++e) {
-          wv[e] = (e < g.n && is_kept(z[e], g0 + e, kc)) ? to_fixed(weight(z[e], wc), scale) : 0ull;
+          wv[e] = (e < g.n && is_kept(z[e], g0 + e, kc)) ? weight_fixed(z[e], wc, scale) : 0ull;
           c += wv[e];
         }
       }

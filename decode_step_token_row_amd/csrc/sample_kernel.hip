@@ -17,14 +17,15 @@
 //   the row is read from HBM exactly once, all 16 loads of 16 bytes per lane
 //   issued before any is used.  Each thread turns every group of 8 logits
 //   (penalised through LDS tables when the row has active penalties) into
-//   its maximum and, for rows without filters or with top-p, its weight
+//   its maximum and, for rows with top-p, its fp32 weight
 //   exp2(z*log2(e)/T - K_t) (K_t an integer reference exponent of the thread,
-//   so moving sums between frames is an exact power of two), and leaves one
-//   float per group in LDS: the weight sum for rows without filters, the
-//   maximum for the others.  After the pass, per-wave records and one wave
+//   so moving sums between frames is an exact power of two); rows without
+//   filters weigh every element in double precision instead and keep each
+//   wave's total per round.  After the pass, per-wave records and one wave
 //   give the row's maximum, mass and min-p threshold, and then:
 //     greedy rows   -> the lowest index of the maximum, from registers;
-//     no filter     -> an id-order draw over the group sums;
+//     no filter     -> an id-order draw over the double weights (round,
+//                      wave, lane, element), from registers;
 //     any filter    -> a bound below which nothing is kept (the min-p
 //                      threshold, or a histogram of the threads' largest
 //                      group maxima for top-k / top-p), the elements above it
@@ -534,12 +535,6 @@ __device__ __forceinline__ float f32_block_max(float v, float* slots) {
   for (int w = 1; w < kFW; ++w) m = max2f(m, slots[w]);
   return m;
 }
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
 // Block sum over the kFT threads of an fp32 row (every thread gets it).
 __device__ __forceinline__ uint64_t f32_block_sum_u64(uint64_t v, uint64_t* slots) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -557,6 +552,18 @@ __device__ __forceinline__ uint64_t f32_block_sum_u64(uint64_t v, uint64_t* slot
 // q * kFW + wave (every lane of the wave calls it).
 __device__ __forceinline__ void f32_round_sum(double* W, int q, float gs) {
   const double s = dpp_wave_sum_f64((double)gs);
+  if ((threadIdx.x & (kWave - 1)) == 0) W[q * kFW + threadIdx.x / kWave] = s;
+}
+// Rows without filters: the group's weights 2^(z c - O) in double precision
+// (fp32 weights carry relative errors near 1e-7, which on rows with heavy
+// tokens ahead of long tails of tiny ones moves many CDF boundaries by more
+// than the tail tokens' widths).  Pass 1 and the draw both call this.
+__device__ __forceinline__ void f32_weights_f64(const float (&z)[4], double c, float negO, double (&w)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = exp2_f64(__builtin_fma((double)z[e], c, (double)negO));
+}
+__device__ __forceinline__ void f32_round_sum_f64(double* W, int q, double gs) {
+  const double s = dpp_wave_sum_f64(gs);
   if ((threadIdx.x & (kWave - 1)) == 0) W[q * kFW + threadIdx.x / kWave] = s;
 }
 // The sum of the kFS slot totals, the same in every wave.
@@ -623,12 +630,13 @@ enum F32Mode : int32_t { kF32Fallback = 0, kF32NoFilter = 1, kF32Thresh = 2, kF3
 // bstar is a candidate (weight from fixed point), one in a bin above it (or
 // any kept element when bstar < 0) weighs its fp32 weight; eb / ec are the
 // edges E(bstar) / E(bstar + 1): above eb a bin above bstar, in (ec, eb]
-// bin bstar.  Returns the id,
+// bin bstar.  With `w64` (rows without filters) every weight is the
+// double-precision 2^(z c - O) of pass 1.  Returns the id,
 // or -1 (uniformly) when the kept mass is not positive.
 __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const double* W, const uint64_t* Wfix,
                                             double u, const KeepCut& cut, int bstar, float eb, float ec, float chi,
-                                            float clo, float negO, float cscale, double fscale, Shared& sh,
-                                            double& S_K) {
+                                            float clo, float negO, float cscale, double fscale, bool w64, double c,
+                                            Shared& sh, double& S_K) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   double vs[8];
   double ls = 0.0;
@@ -669,25 +677,30 @@ __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const 
     const int g = qs * kFT + ws * kWave + lane;
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     uint64_t fx[4] = {0ull, 0ull, 0ull, 0ull};
+    double s64[4] = {0.0, 0.0, 0.0, 0.0};
     if (g < ngroups) {
       const u32x4 dd = rv[g];
       float z[4];
       unpack4(dd, z);
+      if (w64) {
+        f32_weights_f64(z, c, negO, s64);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t idx = (int64_t)g * 4 + e;
-        const float w = wexp(z[e], chi, clo, negO);
-        if (bstar < 0) {
-          s[e] = keep_cut(z[e], idx, cut) ? w : 0.0f;
-        } else {
-          s[e] = z[e] > eb ? w : 0.0f;
-          fx[e] = (z[e] > ec && !(z[e] > eb) && keep_cut(z[e], idx, cut)) ? to_fix50(w * cscale) : 0ull;
+        for (int e = 0; e < 4; ++e) {
+          const int64_t idx = (int64_t)g * 4 + e;
+          const float w = wexp(z[e], chi, clo, negO);
+          if (bstar < 0) {
+            s[e] = keep_cut(z[e], idx, cut) ? w : 0.0f;
+          } else {
+            s[e] = z[e] > eb ? w : 0.0f;
+            fx[e] = (z[e] > ec && !(z[e] > eb) && keep_cut(z[e], idx, cut)) ? to_fix50(w * cscale) : 0ull;
+          }
         }
       }
     }
     const float gs = (s[0] + s[1]) + (s[2] + s[3]);
     const uint64_t cf = (fx[0] + fx[1]) + (fx[2] + fx[3]);
-    const double v = (double)gs + (double)cf * fscale;
+    const double v = w64 ? ((s64[0] + s64[1]) + (s64[2] + s64[3])) : (double)gs + (double)cf * fscale;
     const double vin = dpp_wave_incl_scan_f64(v);
     const uint64_t lc = __ballot(base + vin > t && v > 0.0);
     const uint64_t lp = __ballot(v > 0.0);
@@ -698,7 +711,7 @@ __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const 
       int64_t id = -1, last = -1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double we = s[e] > 0.0f ? (double)s[e] : (double)fx[e] * fscale;
+        const double we = w64 ? s64[e] : (s[e] > 0.0f ? (double)s[e] : (double)fx[e] * fscale);
         if (we > 0.0 && id < 0) {
           a2 += we;
           last = (int64_t)g * 4 + e;
@@ -716,16 +729,31 @@ __device__ __forceinline__ int64_t f32_draw(const u32x4* rv, int ngroups, const 
 // chunk 1 (in flight in d1) and the chunks after them.  Per group of 4:
 // the maximum, the fp32 weights and their sum (each wave's round total into
 // W1), and with HC / HM the histogram counts / masses (exc: the weight
-// above bin 0's per-element limit).
-template <bool HC, bool HM>
+// above bin 0's per-element limit).  F64 (rows without filters, no
+// histogram): the weights in double precision, f32_weights_f64.
+template <bool HC, bool HM, bool F64 = false>
 __device__ __forceinline__ void f32_pass1(const u32x4* rv, int ngroups, u32x4 (&d0)[kFC], u32x4 (&d1)[kFC],
                                           float chi, float clo, float negO, float ncR, float OR, uint32_t* hc,
-                                          uint32_t* hm, double* W1, float& tmax, float& exc) {
+                                          uint32_t* hm, double* W1, float& tmax, float& exc, double c = 0.0) {
+  static_assert(!F64 || (!HC && !HM), "double weights only for rows without filters");
   const int tid = threadIdx.x;
   auto weigh = [&](const u32x4 (&d)[kFC], int ch) {
 #pragma unroll
     for (int r = 0; r < kFC; ++r) {
       const int q = ch * kFC + r;
+      if (F64) {
+        double g64 = 0.0;
+        if (tid < ngroups - q * kFT) {
+          float z[4];
+          unpack4(d[r], z);
+          tmax = max3f(tmax, max2f(z[0], z[1]), max2f(z[2], z[3]));
+          double w[4];
+          f32_weights_f64(z, c, negO, w);
+          g64 = (w[0] + w[1]) + (w[2] + w[3]);
+        }
+        f32_round_sum_f64(W1, q, g64);
+        continue;
+      }
       float gs = 0.0f;
       if (tid < ngroups - q * kFT) {
         float z[4];
@@ -864,6 +892,7 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   if (hcount && hmass) f32_pass1<true, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
   else if (hcount) f32_pass1<true, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
   else if (hmass) f32_pass1<false, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
+  else if (nofilter) f32_pass1<false, false, true>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc, c);
   else f32_pass1<false, false>(rv, ngroups, d0, d1, chi, clo, negO, ncR, OR, hc, hm, W1, tmax, exc);
   if (kwin && tid < ngroups) atomicAdd(&hc[f32_bin(tmax, ncR, OR)], 1u);
   if (hmass) {
@@ -873,6 +902,8 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   const float m = f32_block_max(tmax, sh.w_max);
   const double S = f32_slot_total(W1);
   if (!(m > -__builtin_inff() && m < __builtin_inff()) || !(S > 0.0 && S < 1e300)) return false;
+  // double weights: the maximum's within the exponent range (no loss to subnormals)
+  if (nofilter && !((double)m * c - Od < 960.0)) return false;
   const float tm = wexp(m, chi, clo, negO);  // the maximum's weight (> 1/2 unless m lies above O)
   if (!(tm > 0.0f && tm < 1e30f)) return false;
   int ex = 0;
@@ -1079,7 +1110,8 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   }
   double S_K = 0.0;
   const int64_t id = f32_draw(rv, ngroups, mode == kF32NoFilter ? W1 : W2, mode == kF32Cand ? Wfix : nullptr, u,
-                              cut, mode == kF32Cand ? bstar : -1, eb, ec, chi, clo, negO, cscale, fscale, sh, S_K);
+                              cut, mode == kF32Cand ? bstar : -1, eb, ec, chi, clo, negO, cscale, fscale,
+                              mode == kF32NoFilter, c, sh, S_K);
   if (id < 0) return false;
   if (tid == 0) {
     a.out_ids[row] = (int32_t)id;

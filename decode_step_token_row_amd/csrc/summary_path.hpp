@@ -37,9 +37,20 @@ __device__ __forceinline__ void issue_row_loads(const u32x4* rv, int ngroups, u3
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Inverse-CDF draw in id order over sm.tsum (group j's weight at j).  With
-// `thread_frames`, group j's value is in the frame 2^-K_t of the thread t
-// that owns it (kref[t] = -K_t); otherwise in the row frame K*.
+// The 16 bytes of round bq of this thread's groups, by a static scan of the
+// registers (branch-free: a few selects per round, no loop over rounds).
+__device__ __forceinline__ u32x4 select_round(const u32x4 (&d)[kSQ], int bq) {
+  u32x4 v = d[0];
+#pragma unroll
+  for (int q = 1; q < kSQ; ++q) {
+    v.x = q == bq ? d[q].x : v.x; v.y = q == bq ? d[q].y : v.y;
+    v.z = q == bq ? d[q].z : v.z; v.w = q == bq ? d[q].w : v.w;
+  }
+  return v;
+}
+
+// Inverse-CDF draw in id order over sm.tsum (group j's weight at j, in the
+// row frame 2^-K*).
 // Wave w takes the groups w*64G .. w*64G + 64G - 1 (G = kSQ groups per
 // thread), its lane l the G consecutive groups from w*64G + Gl (owned by the
 // threads (Gl + i) mod kSNT): the wave totals locate the wave, a wave scan
@@ -51,23 +62,20 @@ __device__ __forceinline__ void issue_row_loads(const u32x4* rv, int ngroups, u3
 // than the drawing one return at once.
 template <bool PEN>
 __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, const u32x4* rv, const PenCtx& pc,
-                                          const Smem& sm, Shared& sh, bool thread_frames, KeepCut cut, float chi,
+                                          const Smem& sm, Shared& sh, KeepCut cut, float chi,
                                           float clo, float negks, double u, bool sync, double& S) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   constexpr int G = kSQ;  // groups per lane
   static_assert(kSNT % G == 0, "a lane's groups have consecutive owners");
   double v[G];
   const float4* src = (const float4*)(sm.tsum + wid * kWave * G + lane * G);
-  const float4* kr = (const float4*)(sm.kref + ((lane * G) & (kSNT - 1)));
 #pragma unroll
   for (int i = 0; i < G / 4; ++i) {
     const float4 f = src[i];
-    float4 k = {negks, negks, negks, negks};
-    if (thread_frames) k = kr[i];
-    v[4 * i] = __builtin_ldexp((double)f.x, (int)(negks - k.x));
-    v[4 * i + 1] = __builtin_ldexp((double)f.y, (int)(negks - k.y));
-    v[4 * i + 2] = __builtin_ldexp((double)f.z, (int)(negks - k.z));
-    v[4 * i + 3] = __builtin_ldexp((double)f.w, (int)(negks - k.w));
+    v[4 * i] = (double)f.x;
+    v[4 * i + 1] = (double)f.y;
+    v[4 * i + 2] = (double)f.z;
+    v[4 * i + 3] = (double)f.w;
   }
   double part = 0.0;
 #pragma unroll
@@ -110,27 +118,118 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
         bl += w;
       }
       if (is < 0) { is = ilast; bsel = blast; }
-      const int owner = (lane * G + is) & (kSNT - 1);  // the thread that owns the group
       const int j = wid * kWave * G + lane * G + is;
-      // the group's weights as the owner computed them: the running sum
+      // the group's weights as its owner computed them: the running sum
       // ends at exactly the group's value
-      const float nk = thread_frames ? sm.kref[owner] : negks;
-      const int dsh = (int)(negks - nk);
       float z[8];
       load_z8<PEN>(rv[j], j, pc, z);
       float acc = 0.0f, prev = 0.0f;
       int pe = -1, last_e = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float w = keep_cut(z[e], (int64_t)j * 8 + e, cut) ? wexp(z[e], chi, clo, nk) : 0.0f;
+        const float w = keep_cut(z[e], (int64_t)j * 8 + e, cut) ? wexp(z[e], chi, clo, negks) : 0.0f;
         acc = (e == 0) ? w : acc + w;
         const bool pos = acc > prev;
         if (pos) last_e = e;
-        if (pe < 0 && pos && bsel + __builtin_ldexp((double)acc, dsh) > t) pe = e;
+        if (pe < 0 && pos && bsel + (double)acc > t) pe = e;
         prev = acc;
       }
       if (pe < 0) pe = last_e;
       const int32_t id = j * 8 + pe;
+      a.out_ids[row] = id;
+      if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+      sh.u64[10] = (uint64_t)id;
+    }
+  }
+  if (sync) __syncthreads();
+  return true;
+}
+
+// Rows without filters weigh every element in double precision: fp32
+// weights carry relative errors near 1e-7, and on rows whose heavy tokens
+// precede long tails of tiny ones that moves many CDF boundaries by more
+// than the tail tokens' widths.  w = 2^(z c) with c = log2(e) / T and no
+// frame (the row maximum keeps |m c| <= kF64Span, else the general path).
+// The group's weights are summed in id order; both the pass and the draw
+// call this, so the draw sees the pass's values exactly.
+constexpr double kF64Span = 960.0;
+__device__ __forceinline__ double group_weights_f64(const float (&z)[8], bool valid, double c, double (&w)[8]) {
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    w[e] = valid ? exp2_f64((double)z[e] * c) : 0.0;
+    s += w[e];
+  }
+  return s;
+}
+
+// The draw for rows without filters over the pass's double weights.  Round
+// q's groups are q * kSNT + tid, so id order is (round, wave, lane,
+// element): the pass left each wave's total of each round (the last lane of
+// an inclusive wave scan) in rw[q * kSNW + w].  Every wave sums the round
+// totals and locates the round and then the wave; that wave repeats the
+// round's scan from its registers and locates the lane, whose running sum
+// locates the element.  Returns false (uniformly) when the total is zero or
+// not finite, else S, the total (no frame).  With `sync` the id is left in
+// sh.u64[10] for the whole block.
+template <bool PEN>
+__device__ __forceinline__ bool nofilter_draw(const SampleArgs& a, int64_t row, const u32x4 (&d)[kSQ], int ngroups,
+                                              const PenCtx& pc, const Smem& sm, Shared& sh, double c, double u,
+                                              bool sync, double& S) {
+  static_assert(kSQ <= kWave, "one lane per round");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const double* rw = (const double*)sm.tsum;
+  double rt = 0.0;
+  if (lane < kSQ) {
+#pragma unroll
+    for (int w = 0; w < kSNW; ++w) rt += rw[lane * kSNW + w];
+  }
+  const double rincl = dpp_wave_incl_scan_f64(rt);
+  S = readlane63_f64(rincl);
+  if (!(S > 0.0) || !(S < 1e300)) return false;
+  const double t = u * S;
+  const uint64_t nzq = __ballot(rt > 0.0);
+  const uint64_t hitq = __ballot(rt > 0.0 && rincl > t);
+  const int qs = hitq ? __builtin_ctzll(hitq) : 63 - __builtin_clzll(nzq);  // rounding: the last round with weight
+  double cum = qs > 0 ? readlane_f64(rincl, qs - 1) : 0.0;
+  int ws = -1, wlast = 0;
+  double bw = 0.0, bwlast = 0.0;
+  for (int w = 0; w < kSNW; ++w) {
+    const double r = rw[qs * kSNW + w];
+    if (r > 0.0) {
+      if (ws < 0 && cum + r > t) { ws = w; bw = cum; }
+      wlast = w;
+      bwlast = cum;
+    }
+    cum += r;
+  }
+  if (ws < 0) { ws = wlast; bw = bwlast; }
+  if (wid == ws) {
+    const bool valid = tid < ngroups - qs * kSNT;
+    float z[8];
+    unpack8(select_round(d, qs), z);
+    if (PEN && pc.on && valid) penalize8(z, (int64_t)(qs * kSNT + tid) * 8, pc);
+    double w8[8];
+    const double g = group_weights_f64(z, valid, c, w8);
+    const double incl = dpp_wave_incl_scan_f64(g);
+    const double prev = __shfl_up(incl, 1);
+    const uint64_t hit = __ballot(g > 0.0 && bw + incl > t);
+    const uint64_t nz = __ballot(g > 0.0);
+    const int ls = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
+    if (lane == ls) {
+      const double bsel = bw + (lane > 0 ? prev : 0.0);
+      double acc = 0.0;
+      int pe = -1, last_e = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc += w8[e];
+        if (w8[e] > 0.0) {
+          if (pe < 0 && bsel + acc > t) pe = e;
+          last_e = e;
+        }
+      }
+      if (pe < 0) pe = last_e;
+      const int32_t id = (qs * kSNT + tid) * 8 + pe;
       a.out_ids[row] = id;
       if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
       sh.u64[10] = (uint64_t)id;
@@ -640,13 +739,14 @@ __device__ __forceinline__ double exact_row_mass(const u32x4 (&dd)[kSQ], const P
 //          without filters).
 // Filter rows keep each group's maximum (-inf for groups past the row's end)
 // in registers, gm[q], or with penalties (whose arithmetic needs the
-// registers) in LDS at sm.tsum[q * kSNT + tid]; NOFILTER rows store each
-// group's weight sum in sm.tsum instead (in the thread's frame, kept per
-// thread in sm.kref).
+// registers) in LDS at sm.tsum[q * kSNT + tid].  NOFILTER rows (W == 3)
+// weigh every element in double precision instead and leave each wave's
+// total of each round in LDS (as doubles at sm.tsum, [q * kSNW + wave]).
 template <bool PEN, int W, bool NOFILTER>
 __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, const PenCtx& pc, const Smem& sm,
                                          float chi, float clo, PassOut& o, float (&gm)[kSQ]) {
   const int tid = threadIdx.x;
+  const double c64 = (double)chi + (double)clo;
   float best = -__builtin_inff();
   int bq = -1;
   double lsum = 0.0;
@@ -676,6 +776,13 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
     }
     best = max2f(best, g);
     if (W == 0) continue;
+    if (W == 3) {
+      double w8[8];
+      const double gw = group_weights_f64(z, valid, c64, w8);
+      const double incl = dpp_wave_incl_scan_f64(gw);
+      if ((tid & (kWave - 1)) == kWave - 1) ((double*)sm.tsum)[q * kSNW + tid / kWave] = incl;
+      continue;
+    }
     const float x = g * chi;
     if (x > kfr + 64.0f) {
       // the first finite group, or one far above the frame: (re)set it
@@ -684,30 +791,14 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
       if (kfr > -__builtin_inff()) {
         const int sh_ = (int)(kfr - nk);
         lsum = __builtin_ldexp(lsum, sh_);
-        if (NOFILTER) {
-          for (int p = 0; p < q; ++p) sm.tsum[p * kSNT + tid] = __builtin_ldexpf(sm.tsum[p * kSNT + tid], sh_);
-        }
       }
       kfr = nk;
       negk = -nk;
     }
     const float s = W == 1 ? wexp(g, chi, clo, negk) : group_weight(z, chi, clo, negk);
-    if (NOFILTER) sm.tsum[q * kSNT + tid] = valid ? s : 0.0f;
-    else lsum += valid ? (double)s : 0.0;
+    lsum += valid ? (double)s : 0.0;
   }
   o.best = best; o.bq = bq; o.lsum = lsum; o.kfr = kfr; o.negk = negk; o.bad = bad; o.special = special;
-}
-
-// The 16 bytes of round bq of this thread's groups, by a static scan of the
-// registers (branch-free: a few selects per round, no loop over rounds).
-__device__ __forceinline__ u32x4 select_round(const u32x4 (&d)[kSQ], int bq) {
-  u32x4 v = d[0];
-#pragma unroll
-  for (int q = 1; q < kSQ; ++q) {
-    v.x = q == bq ? d[q].x : v.x; v.y = q == bq ? d[q].y : v.y;
-    v.z = q == bq ? d[q].z : v.z; v.w = q == bq ? d[q].w : v.w;
-  }
-  return v;
 }
 
 // The lowest index of the maximum wm in the thread's group bq (the first of
@@ -873,7 +964,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   const bool kon = !greedy && P.top_k >= 1 && (int64_t)P.top_k < V;
   const bool pon = !greedy && P.top_p < 1.0f;
   const bool mon = !greedy && P.min_p > 0.0f;
-  const bool weights = nofilter || pon;  // weights needed during the pass
+  const bool weights = pon;  // fp32 weights needed during the pass
   // top-p with top-k: the pass weighs only each group's maximum, which bounds
   // the row's mass from below; a top-k prefix whose mass stays under top_p
   // times that bound is not cut by top-p, and only when it is not is the
@@ -892,7 +983,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // (greedy rows take the group-maxima pass and find the element afterwards)
   PassOut po;
   float gm[kSQ];  // filter rows: the maximum of each of the thread's groups
-  if (nofilter) row_pass<PEN, 2, true>(d, ngroups, pc, sm, chi, clo, po, gm);
+  if (nofilter) row_pass<PEN, 3, true>(d, ngroups, pc, sm, chi, clo, po, gm);
   else if (lazy) row_pass<PEN, 1, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   else if (weights) row_pass<PEN, 2, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   else row_pass<PEN, 0, false>(d, ngroups, pc, sm, chi, clo, po, gm);
@@ -906,8 +997,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   {
     const float wm = dpp_wave_max_f32(best);
     const float kw = wm > -__builtin_inff() && weights ? __builtin_floorf(wm * chi) : 0.0f;  // K_w >= K_t
-    if (nofilter) sm.kref[tid] = negk;
-    if (weights && !nofilter) lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
+    if (weights) lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
     const double ws = pon ? dpp_wave_sum_f64(lsum) : 0.0;
     uint32_t warg = 0xFFFFFFFFu;
     if (greedy) warg = dpp_wave_min_u32(first_index_of<PEN>(d, bq, wm, best == wm && wm > -__builtin_inff(), pc));
@@ -944,7 +1034,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
       negks = -__builtin_floorf(m * chi);
       if (nofilter) {
-        mode = kModeNoFilter;
+        const double mc = (double)m * ((double)chi + (double)clo);
+        mode = mc > -kF64Span && mc < kF64Span ? kModeNoFilter : kModeFallback;
       } else {
         bool ok = true;
         if (pon) {
@@ -1015,9 +1106,9 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
 
   if (mode == kModeNoFilter) {
     path |= ARCS_PATH_SORT_SKIP;
-    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, true, KeepCut{0u, INT64_MAX}, chi, clo, negks, u, debug, S))
-      return false;
+    if (!nofilter_draw<PEN>(a, row, d, ngroups, pc, sm, sh, (double)chi + (double)clo, u, debug, S)) return false;
     if (!debug) return true;
+    S = __builtin_ldexp(S, (int)negks);  // into the row frame 2^-K* of the other modes
     S_K = S;
     id = (int64_t)sh.u64[10];
   } else if (mode == kModeMinpStream) {
@@ -1040,7 +1131,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       }
     }
     __syncthreads();
-    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, false, KeepCut{ord_key(zt), INT64_MAX}, chi, clo, negks, u, debug,
+    if (!tsum_draw<PEN>(a, row, rv, pc, sm, sh, KeepCut{ord_key(zt), INT64_MAX}, chi, clo, negks, u, debug,
                         S_K))
       return false;
     if (!debug) return true;

@@ -75,7 +75,7 @@ enum {
 /* Codes arcs_commit_tokens latches into its fault word (the first one stays). */
 enum {
   ARCS_FAULT_NONE = 0,
-  ARCS_FAULT_TOKEN_RANGE = 1,        /* a token outside [0, V)                          */
+  ARCS_FAULT_TOKEN_RANGE = 1,        /* a token outside [0, V) other than -1            */
   ARCS_FAULT_RING_OVERRUN = 2        /* the ring slot still holds a step not drained yet */
 };
 
@@ -222,7 +222,6 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
                       size_t workspace_bytes, const double* uniforms, float* out_probs,
                       arcs_row_stats* out_stats, void* stream);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
 /*
  * arcs_top_logprobs: the n most probable tokens of each row with their
  * log-probabilities, next to the draw (Arc PR #222, section 3(c): the host
@@ -259,7 +258,9 @@ int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64
  * anything and latches a code into a pinned fault word).  One launch:
  *   p = *position;
  *   refused, with *fault set to the code if it was ARCS_FAULT_NONE, when a
- *   token is outside [0, V) (ARCS_FAULT_TOKEN_RANGE) or the slot p % capacity
+ *   token is outside [0, V) and is not -1 (ARCS_FAULT_TOKEN_RANGE; -1 is the
+ *   sampler's mark for a row it refused, published as it is so that one
+ *   request's invalid parameters do not stop the batch), or the slot p % capacity
  *   still holds a step the host has not drained, p - *drained >= capacity
  *   (ARCS_FAULT_RING_OVERRUN); also refused, silently, while *fault is set
  *   (a latched fault stops publication until the host clears it); nothing
@@ -282,6 +283,7 @@ int arcs_commit_tokens(const int32_t* ids, int64_t B, int64_t V, int32_t* next_i
                        int32_t* ring, uint64_t capacity, uint64_t* published, const uint64_t* drained,
                        uint32_t* fault, void* stream);
 
+/* Library version, major * 10000 + minor * 100 + patch. */
 int arcs_version(void);
 
 #ifdef __cplusplus

@@ -3,4 +3,4 @@
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
 """
-from . import sampler  # noqa: F401
+from . import commit, sampler  # noqa: F401

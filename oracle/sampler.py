@@ -199,14 +199,24 @@ class Cutoff:
     S: float
     margin_p: float   # |top_p*S - nearest bracketing cumulative| / S (inf if off)
     margin_m: float   # min |w - min_p| / min_p (inf if off)
+    near_p: int = 0   # cut positions whose cumulative lies within band_p * S of top_p*S
+    near_m: int = 0   # ids whose weight lies within band_m * min_p of min_p
 
 
-def cutoff(z: np.ndarray, w: np.ndarray, top_k: int, top_p: float, min_p: float) -> Cutoff:
+def cutoff(z: np.ndarray, w: np.ndarray, top_k: int, top_p: float, min_p: float,
+           band_p: float = 0.0, band_m: float = 0.0) -> Cutoff:
+    """Step 6.  The margins say how far the two threshold decisions are from
+    flipping: margin_p is the distance of top_p*S from the nearer of the two
+    cumulative sums around the crossing, over S; margin_m the distance of the
+    nearest weight from min_p, over min_p.  near_p / near_m count the cut
+    positions (ids) that lie within band_p * S (band_m * min_p) of the
+    threshold: the number of places where a computation with that much error
+    could put the cut instead."""
     V = len(z)
     S = math.fsum(w.tolist())
     order = total_order(z)
     L_k = top_k if 1 <= top_k < V else V
-    L_p, margin_p = V, math.inf
+    L_p, margin_p, near_p = V, math.inf, 0
     if top_p < 1.0:
         cum = np.cumsum(w[order].astype(np.longdouble))
         target = np.longdouble(top_p) * np.longdouble(S)
@@ -215,12 +225,16 @@ def cutoff(z: np.ndarray, w: np.ndarray, top_k: int, top_p: float, min_p: float)
         hi = float(cum[L_p - 1] - target)
         lo = float(target - cum[L_p - 2]) if L_p >= 2 else float(target)
         margin_p = min(abs(hi), abs(lo)) / S
-    L_m, margin_m = V, math.inf
+        if band_p > 0.0:
+            near_p = int(np.count_nonzero(np.abs(cum - target) <= np.longdouble(band_p * S)))
+    L_m, margin_m, near_m = V, math.inf, 0
     if min_p > 0.0:
         L_m = int(np.count_nonzero(w >= float(min_p)))
         margin_m = float(np.min(np.abs(w - float(min_p)))) / float(min_p)
+        if band_m > 0.0:
+            near_m = int(np.count_nonzero(np.abs(w - float(min_p)) <= band_m * float(min_p)))
     L = max(1, min(L_k, L_p, L_m))
-    return Cutoff(order, L, L_k, L_p, L_m, S, margin_p, margin_m)
+    return Cutoff(order, L, L_k, L_p, L_m, S, margin_p, margin_m, near_p, near_m)
 
 
 # --------------------------------------------------------------------------
@@ -253,6 +267,7 @@ class RowResult:
     id: int
     greedy: bool = False
     argmax: int = -1
+    max_logit: float = math.nan   # the penalised logit at argmax
     L: int = 0
     cut_value: float = math.nan
     cut_index: int = -1
@@ -262,11 +277,15 @@ class RowResult:
     margin_id: float = math.inf
     margin_p: float = math.inf
     margin_m: float = math.inf
+    near_p: int = 0
+    near_m: int = 0
     L_k: int = 0
     L_p: int = 0
     L_m: int = 0
     kept: Optional[np.ndarray] = None     # kept ids, increasing
     probs: Optional[np.ndarray] = None    # q over the full vocabulary (float64)
+    order: Optional[np.ndarray] = None    # the cutoff order (with probs), for kept sets of another size
+    weights: Optional[np.ndarray] = None  # unnormalised weights w over the vocabulary (with probs)
 
 
 def validate(p) -> int:
@@ -289,7 +308,7 @@ def validate(p) -> int:
 
 def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], seed: int,
                row: int, step: int, u_override: Optional[float] = None,
-               want_probs: bool = False) -> RowResult:
+               want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0) -> RowResult:
     st = validate(p)
     if st != ROW_OK:
         return RowResult(status=st, id=-1)
@@ -299,30 +318,33 @@ def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], s
     T = float(p["temperature"])
     top_k = int(p["top_k"])
     if T == 0.0 or top_k == 1 or z[am] == -np.inf:
-        return RowResult(status=ROW_OK, id=am, greedy=True, argmax=am)
+        return RowResult(status=ROW_OK, id=am, greedy=True, argmax=am, max_logit=float(z[am]))
     _, w = weights(z, T)
-    c = cutoff(z, w, top_k, float(p["top_p"]), float(p["min_p"]))
+    c = cutoff(z, w, top_k, float(p["top_p"]), float(p["min_p"]), band_p, band_m)
     kept = np.sort(c.order[: c.L])
     wk = w[kept]
     S_K = math.fsum(wk.tolist())
     u = uniform(seed, row, step) if u_override is None else float(u_override)
     ids, margins = draw(kept, wk, u)
     last = int(c.order[c.L - 1])
-    res = RowResult(status=ROW_OK, id=int(ids[0]), argmax=am, L=c.L, cut_value=float(z[last]),
+    res = RowResult(status=ROW_OK, id=int(ids[0]), argmax=am, max_logit=float(z[am]), L=c.L,
+                    cut_value=float(z[last]),
                     cut_index=last, S=c.S, S_K=S_K, u=u, margin_id=float(margins[0]),
                     margin_p=c.margin_p, margin_m=c.margin_m, L_k=c.L_k, L_p=c.L_p, L_m=c.L_m,
-                    kept=kept)
+                    kept=kept, near_p=c.near_p, near_m=c.near_m)
     if want_probs:
         q = np.zeros(len(z), dtype=np.float64)
         q[kept] = wk / S_K
         res.probs = q
+        res.order = c.order
+        res.weights = w
     return res
 
 
 def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optional[np.ndarray],
            hist_offsets: Optional[np.ndarray], seed: int, step: int,
            rows: Optional[Sequence[int]] = None, uniforms: Optional[Sequence[float]] = None,
-           want_probs: bool = False) -> List[RowResult]:
+           want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0) -> List[RowResult]:
     """Oracle over a batch.  ``rows`` are the batch indices that key the RNG."""
     n = logits.shape[0]
     rows = list(range(n)) if rows is None else [int(r) for r in rows]
@@ -332,7 +354,8 @@ def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optiona
         if hist_ids is not None and hist_offsets is not None:
             hist = hist_ids[int(hist_offsets[i]): int(hist_offsets[i + 1])]
         u = None if uniforms is None else float(uniforms[i])
-        out.append(sample_row(logits[i], dtype, params[i], hist, seed, rows[i], step, u, want_probs))
+        out.append(sample_row(logits[i], dtype, params[i], hist, seed, rows[i], step, u, want_probs,
+                              band_p, band_m))
     return out
 
 

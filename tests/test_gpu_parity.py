@@ -43,8 +43,16 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def _compare_rows(ids, stats, refs, where, allow_near=True):
-    """Returns the number of excused id mismatches."""
+def _compare_rows(ids, stats, refs, where, allow_near=True, max_excused=None):
+    """Compares one launch with the oracle (called with near-boundary bands, see
+    _oracle); returns the number of excused id mismatches, which must stay
+    within max(1, 1e-4 * rows) unless the caller bounds them itself.
+
+    Rows whose top-p or min-p decision lies within its margin ("near set") may
+    keep a different prefix, but only by positions inside the band: the kept
+    size differs by at most the oracle's count of cut positions (ids) whose
+    cumulative sum (weight) lies within the band, and an equal size means an
+    equal cut."""
     excused = 0
     for b, r in enumerate(refs):
         st = stats[b] if stats is not None else None
@@ -54,18 +62,29 @@ def _compare_rows(ids, stats, refs, where, allow_near=True):
             continue
         if st is not None:
             assert st["argmax"] == r.argmax, (where, b, st["argmax"], r.argmax)
+            # the maximum the kernel's own pass found (the argmax above comes
+            # from the debug re-read of the row)
+            if math.isfinite(r.max_logit):
+                assert st["max_logit"] == np.float32(r.max_logit), (where, b, st["max_logit"], r.max_logit)
         if r.greedy:
             assert ids[b] == r.id, (where, b, ids[b], r.id)
             continue
         near_set = r.margin_p < MARGIN_P or r.margin_m < MARGIN_M
-        if st is not None and not near_set:
-            assert st["kept"] == r.L, (where, b, st["kept"], r.L, r.L_k, r.L_p, r.L_m)
-            assert st["cut_index"] == r.cut_index, (where, b, st["cut_index"], r.cut_index)
-            assert st["cut_value"] == np.float32(r.cut_value), (where, b)
+        if st is not None:
+            if not near_set or st["kept"] == r.L:
+                assert st["kept"] == r.L, (where, b, st["kept"], r.L, r.L_k, r.L_p, r.L_m)
+                assert st["cut_index"] == r.cut_index, (where, b, st["cut_index"], r.cut_index)
+                assert st["cut_value"] == np.float32(r.cut_value), (where, b)
+            else:
+                slack = r.near_p + r.near_m
+                assert 1 <= slack and abs(int(st["kept"]) - r.L) <= slack, \
+                    (where, b, int(st["kept"]), r.L, r.near_p, r.near_m)
         if ids[b] != r.id:
             assert allow_near and (r.margin_id < MARGIN_ID or near_set), \
                 (where, b, int(ids[b]), r.id, r.margin_id, r.margin_p, r.margin_m)
             excused += 1
+    cap = max(1, int(1e-4 * len(refs))) if max_excused is None else max_excused
+    assert excused <= cap, (where, excused, len(refs))
     return excused
 
 
@@ -81,7 +100,7 @@ def _run_debug(arcs, w, uniforms=None, want_probs=False, stride=None):
 
 def _oracle(w, uniforms=None, want_probs=False):
     return oracle.sample(w.logits, w.dtype, w.params, w.hist_ids, w.hist_offsets, w.seed, w.step,
-                         rows=w.rows, uniforms=uniforms, want_probs=want_probs)
+                         rows=w.rows, uniforms=uniforms, want_probs=want_probs, band_p=MARGIN_P, band_m=MARGIN_M)
 
 
 # --------------------------------------------------------------------------

@@ -457,14 +457,160 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as m:
         real_cut = o.cutoff
 
-        def renorm(z, w, k, p, mp):
-            c = real_cut(z, w, k, 1.0, mp)
+        def renorm(z, w, k, p, mp, *bands):
+            c = real_cut(z, w, k, 1.0, mp, *bands)
             kept = c.order[: c.L]
             c2 = real_cut(z[kept], w[kept], -1, p, 0.0)
             c.L = min(c.L, c2.L)
             return c
         m.setattr(o, "cutoff", renorm)
         assert _red(test_combined_filters_take_the_shortest_prefix_without_renormalising)
+    # a draw margin of zero (every mismatch would be excused)
+    with monkeypatch.context() as m:
+        real = o.draw
+        m.setattr(o, "draw", lambda kept, wk, u: (real(kept, wk, u)[0], np.zeros(np.atleast_1d(u).shape)))
+        assert _red(test_margin_id_closed_form)
+        assert _red(test_margin_id_is_the_distance_to_a_flip)
+    # top-p and min-p margins of zero, or measured against the wrong quantity
+    for field, bad in (("margin_p", lambda c: 0.0), ("margin_m", lambda c: 0.0),
+                       ("margin_p", lambda c: c.margin_p * c.S), ("margin_m", lambda c: c.margin_m * 10.0)):
+        with monkeypatch.context() as m:
+            real_cut = o.cutoff
+
+            def planted(*args, _f=field, _b=bad, _r=real_cut):
+                c = _r(*args)
+                if math.isfinite(getattr(c, _f)):
+                    setattr(c, _f, _b(c))
+                return c
+            m.setattr(o, "cutoff", planted)
+            pin = test_margin_p_is_the_distance_to_a_flip if field == "margin_p" else test_margin_m_is_the_distance_to_a_flip
+            closed = test_margin_p_closed_form if field == "margin_p" else test_margin_m_closed_form
+            assert _red(pin) or _red(closed), field
+
+
+# --------------------------------------------------------------------------
+# the margins the parity tests use to excuse a decision near its threshold
+# --------------------------------------------------------------------------
+def test_margin_id_closed_form():
+    # four equal weights (S_K = 4, CDF boundaries at 1, 2, 3): u = 0.25 + d puts
+    # t = 1 + 4d inside id 1's interval [1, 2), at 4d from its lower edge
+    z = np.zeros(4, dtype=np.float32)
+    p = _p(temperature=1.0)
+    for d in (0.125, 2.0 ** -10, 2.0 ** -20, 2.0 ** -30):
+        r = o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.25 + d)
+        assert r.id == 1 and math.isclose(r.margin_id, d, rel_tol=1e-9), (d, r.margin_id)
+        r = o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.75 - d)
+        assert r.id == 2 and math.isclose(r.margin_id, d, rel_tol=1e-9), (d, r.margin_id)
+    # exactly on a boundary the margin is zero
+    assert o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=0.5).margin_id == 0.0
+
+
+def test_margin_id_is_the_distance_to_a_flip():
+    # moving u by less than the margin keeps the id; by a little more, one way
+    # or the other, changes it
+    rng = np.random.default_rng(31)
+    checked = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 12))
+        z = o.widen(rng.normal(0, 1.5, V).astype(np.float32), "f32")
+        p = _p(temperature=float(rng.uniform(0.5, 2.0)))
+        u = float(rng.uniform(0.0, 1.0))
+        r = o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=u)
+        mg = r.margin_id
+        if not (1e-9 < mg < 0.2) or u - 1.1 * mg < 0 or u + 1.1 * mg >= 1:
+            continue
+        same = [o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=u + s * 0.9 * mg).id for s in (-1, 1)]
+        moved = [o.sample_row(z, "f32", p, None, 0, 0, 0, u_override=u + s * 1.1 * mg).id for s in (-1, 1)]
+        assert same == [r.id, r.id], (u, mg)
+        assert moved[0] != r.id or moved[1] != r.id, (u, mg)
+        checked += 1
+    assert checked > 200
+
+
+def test_margin_p_closed_form():
+    # eight equal weights, cumulative sums 1..8 (S = 8); top_p = 3/8 - d puts the
+    # target 8d below the cumulative sum 3: L_p = 3 and margin_p = d
+    z = np.zeros(8, dtype=np.float32)
+    for d in (2.0 ** -6, 2.0 ** -10, 2.0 ** -16):
+        tp = 0.375 - d
+        assert float(np.float32(tp)) == tp
+        r = o.sample_row(z, "f32", _p(temperature=1.0, top_p=tp), None, 0, 0, 0)
+        assert r.L_p == 3 and math.isclose(r.margin_p, d, rel_tol=1e-12), (d, r.margin_p)
+        tp = 0.375 + d  # now just past the sum 3: L_p = 4, margin d again
+        r = o.sample_row(z, "f32", _p(temperature=1.0, top_p=tp), None, 0, 0, 0)
+        assert r.L_p == 4 and math.isclose(r.margin_p, d, rel_tol=1e-12), (d, r.margin_p)
+
+
+def test_margin_p_is_the_distance_to_a_flip():
+    rng = np.random.default_rng(32)
+    checked = 0
+    for _ in range(300):
+        V = int(rng.integers(3, 40))
+        z = o.widen(rng.normal(0, 1.5, V).astype(np.float32), "f32")
+        T = float(rng.uniform(0.5, 2.0))
+        tp = float(rng.uniform(0.1, 0.95))
+        _, w = o.weights(z, T)
+        c = o.cutoff(z, w, -1, tp, 0.0)
+        mg = c.margin_p
+        if not (1e-9 < mg < 0.05):
+            continue
+        near = [o.cutoff(z, w, -1, tp + s * 0.9 * mg, 0.0).L_p for s in (-1, 1)]
+        far = [o.cutoff(z, w, -1, tp + s * 1.1 * mg, 0.0).L_p for s in (-1, 1)]
+        assert near == [c.L_p, c.L_p], (tp, mg)
+        assert far[0] != c.L_p or far[1] != c.L_p, (tp, mg)
+        checked += 1
+    assert checked > 150
+
+
+def test_margin_m_closed_form():
+    # at T = 1/ln 2 (rounded to binary32) the weights are powers of two to
+    # within 1e-7, so a min_p of 2^-4 (1 + d) sits d above the weight of the
+    # value 4 below the maximum: margin_m = d / (1 + d)
+    T = float(np.float32(1.0 / math.log(2.0)))
+    z = np.array([0.0, -4.0, -9.0, -20.0], dtype=np.float32)
+    for d in (2.0 ** -6, 2.0 ** -10, 2.0 ** -14):
+        mp = 2.0 ** -4 * (1.0 + d)
+        assert float(np.float32(mp)) == mp
+        r = o.sample_row(z, "f32", _p(temperature=T, min_p=mp), None, 0, 0, 0)
+        assert r.L_m == 1 and abs(r.margin_m - d / (1 + d)) < 1e-6, (d, r.margin_m)
+        mp = 2.0 ** -4 * (1.0 - d)  # now just below that weight: it is kept
+        r = o.sample_row(z, "f32", _p(temperature=T, min_p=mp), None, 0, 0, 0)
+        assert r.L_m == 2 and abs(r.margin_m - d / (1 - d)) < 1e-6, (d, r.margin_m)
+
+
+def test_margin_m_is_the_distance_to_a_flip():
+    rng = np.random.default_rng(33)
+    checked = 0
+    for _ in range(300):
+        V = int(rng.integers(3, 40))
+        z = o.widen(rng.normal(0, 1.5, V).astype(np.float32), "f32")
+        T = float(rng.uniform(0.5, 2.0))
+        mp = float(rng.uniform(0.01, 0.9))
+        _, w = o.weights(z, T)
+        c = o.cutoff(z, w, -1, 1.0, mp)
+        mg = c.margin_m
+        if not (1e-9 < mg < 0.2):
+            continue
+        near = [o.cutoff(z, w, -1, 1.0, mp * (1 + s * 0.9 * mg)).L_m for s in (-1, 1)]
+        far = [o.cutoff(z, w, -1, 1.0, mp * (1 + s * 1.1 * mg)).L_m for s in (-1, 1)]
+        assert near == [c.L_m, c.L_m], (mp, mg)
+        assert far[0] != c.L_m or far[1] != c.L_m, (mp, mg)
+        checked += 1
+    assert checked > 150
+
+
+def test_near_counts():
+    # equal weights: every cut position is its own cumulative sum k; with
+    # top_p * S on one of them only that position is within a small band, and
+    # with min_p = 1 every id sits on the threshold
+    z = np.zeros(10, dtype=np.float32)
+    r = o.sample_row(z, "f32", _p(temperature=1.0, top_p=0.5), None, 0, 0, 0, band_p=1e-7, band_m=1e-6)
+    assert r.L_p == 5 and r.near_p == 1 and r.margin_p == 0.0
+    r = o.sample_row(z, "f32", _p(temperature=1.0, min_p=1.0), None, 0, 0, 0, band_p=1e-7, band_m=1e-6)
+    assert r.L_m == 10 and r.near_m == 10
+    # a band wider than the spacing of the sums takes in the neighbours
+    r = o.sample_row(z, "f32", _p(temperature=1.0, top_p=0.5), None, 0, 0, 0, band_p=0.15)
+    assert r.near_p == 3
 
 
 # --------------------------------------------------------------------------
