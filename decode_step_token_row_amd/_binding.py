@@ -23,6 +23,17 @@ DTYPE_F32 = 1
 
 # C enum values of include/arcs.h
 OK = 0
+ERR_NULL_POINTER = -1
+ERR_BAD_BATCH = -2
+ERR_BAD_VOCAB = -3
+ERR_BAD_STRIDE = -4
+ERR_BAD_DTYPE = -5
+ERR_WORKSPACE_TOO_SMALL = -6
+ERR_LAUNCH = -7
+ERR_MISALIGNED = -8
+ERR_BAD_HISTORY = -9
+ERR_BAD_TOP_N = -10
+ERR_BAD_CAPACITY = -11
 ROW_OK = 0
 ROW_BAD_TEMPERATURE = 1
 ROW_BAD_TOP_P = 2

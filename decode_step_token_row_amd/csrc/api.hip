@@ -51,8 +51,10 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   if (st != ARCS_OK) return st;
   if (params == nullptr) return ARCS_ERR_NULL_POINTER;
   if ((hist_ids == nullptr) != (hist_offsets == nullptr)) return ARCS_ERR_BAD_HISTORY;
-  if (workspace_bytes < arcs_sample_workspace_bytes(B, V, dtype)) return ARCS_ERR_WORKSPACE_TOO_SMALL;
-  (void)workspace;
+  const size_t ws_need = arcs_sample_workspace_bytes(B, V, dtype);
+  if (workspace_bytes < ws_need) return ARCS_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_need > 0 && workspace == nullptr) return ARCS_ERR_NULL_POINTER;
+  if (ws_need > 0 && ((uintptr_t)workspace & 15u) != 0) return ARCS_ERR_MISALIGNED;
   arcs::SampleArgs a;
   a.logits = logits;
   a.V = V;
@@ -73,8 +75,14 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   a.pen_tables = (hist_ids != nullptr && V <= ARCS_MAX_PENALTY_VOCAB) ? 1 : 0;
   a.bitmap_words = a.pen_tables ? (uint32_t)((V + 31) / 32) : 0u;
   a.deferred_only = 0;
-  hipError_t e = arcs::launch_sample(a, dtype, B, rows_16b_aligned(logits, dtype, row_stride),
-                                     (hipStream_t)stream);
+  const bool vec = rows_16b_aligned(logits, dtype, row_stride);
+  // small batches: greedy rows and rows without filters are read by many
+  // workgroups per row (not with debug outputs, which read the row whole)
+  const bool split = ws_need > 0 && arcs::split_shape(B, V, dtype) && vec && !a.pen_tables &&
+                     out_stats == nullptr && out_probs == nullptr;
+  a.split_parts = split ? (arcs::SplitPart*)workspace : nullptr;
+  a.split_P = split ? arcs::split_slices(B) : 0;
+  hipError_t e = arcs::launch_sample(a, dtype, B, vec, (hipStream_t)stream);
   return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
 }
 
@@ -148,10 +156,8 @@ int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64
 }
 
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype) {
-  (void)B;
-  (void)V;
-  (void)dtype;
-  return 0;
+  if (!arcs::split_shape(B, V, dtype)) return 0;
+  return (size_t)B * (size_t)arcs::split_slices(B) * sizeof(arcs::SplitPart);
 }
 
 const char* arcs_status_string(int code) {

@@ -30,7 +30,36 @@ struct SampleArgs {
   int pen_tables;      // LDS penalty tables present in this launch
   uint32_t bitmap_words;
   int deferred_only;   // general kernel: only rows whose out_ids holds kDeferredId
+  struct SplitPart* split_parts;  // split launch: [B][split_P] slice partials, or NULL
+  int split_P;                    // slices per row of a split launch
 };
+
+// Small batches of bf16 rows (B <= kSplitMaxB): greedy rows and rows without
+// filters are read by P slices per row, one workgroup each, whose partials
+// (slice maximum, the lowest index holding it, the slice's weight in double
+// precision) go to the caller's workspace; the row's own workgroup then
+// combines them and draws, reading one slice again.
+struct SplitPart {
+  float m;      // slice maximum (-inf for a slice of -inf values)
+  int32_t arg;  // lowest index of the maximum; -1: the slice holds NaN or +inf, or
+                // its maximum is out of the double weights' exponent range
+  double s;     // sum over the slice of 2^(z c), c = log2(e) / T (rows without filters)
+};
+static_assert(sizeof(SplitPart) == 16, "split partial record");
+constexpr int64_t kSplitMaxB = 64;     // batches up to this many rows are split
+constexpr int64_t kSplitMinV = 8192;   // and rows of at least this many tokens
+constexpr int kSplitMaxP = 128;        // slices per row
+constexpr int kSplitThreads = 256;     // threads per slice workgroup
+// P = 512 / B slices (at least 8, at most kSplitMaxP): about 512 workgroups
+inline int split_slices(int64_t B) {
+  const int64_t p = (512 + B - 1) / B;
+  return (int)(p < 8 ? 8 : (p > kSplitMaxP ? kSplitMaxP : p));
+}
+// Whether a launch of this shape and element type takes the split path (the
+// kernel also needs 16-byte aligned rows, no history and no debug outputs).
+inline bool split_shape(int64_t B, int64_t V, int dtype) {
+  return dtype == ARCS_DTYPE_BF16 && B >= 1 && B <= kSplitMaxB && V >= kSplitMinV && V <= 131072 && V % 8 == 0;
+}
 
 // out_ids value the fp32 kernel leaves for a row it hands to the general
 // kernel launched after it on the same stream (never a valid id or status).

@@ -313,18 +313,24 @@ struct RowConsts {
   double tdl, u;
   bool ok;
 };
+// c = log2(e) / T as chi + clo (chi rounded down, clo > 0, so weights and
+// bins never decrease with z); false when c is out of range.
+__device__ __forceinline__ bool temp_coeffs(float T, float& chi, float& clo) {
+  const double c = 1.4426950408889634 / (double)T;
+  if (!(c >= 1e-30 && c <= 1e30)) return false;
+  chi = (float)c;
+  if ((double)chi >= c) chi = key_value(ord_key(chi) - 1u);
+  clo = (float)(c - (double)chi);
+  if (!(clo > 0.0f)) clo = 1e-30f;
+  chi = uniform_f32(chi);
+  clo = uniform_f32(clo);
+  return true;
+}
 __device__ __forceinline__ RowConsts row_consts(const arcs_row_params& P, const RowRng& rng, int64_t row) {
   RowConsts r;
   r.chi = 0.0f; r.clo = 0.0f; r.tdl = 0.0; r.u = 0.0; r.ok = true;
   if (P.temperature == 0.0f || P.top_k == 1) return r;
-  const double c = 1.4426950408889634 / (double)P.temperature;
-  if (!(c >= 1e-30 && c <= 1e30)) { r.ok = false; return r; }
-  float chi = (float)c;
-  if ((double)chi >= c) chi = key_value(ord_key(chi) - 1u);
-  float clo = (float)(c - (double)chi);
-  if (!(clo > 0.0f)) clo = 1e-30f;
-  r.chi = uniform_f32(chi);
-  r.clo = uniform_f32(clo);
+  if (!temp_coeffs(P.temperature, r.chi, r.clo)) { r.ok = false; return r; }
   if (P.min_p > 0.0f) r.tdl = uniform_f64((double)P.temperature * log((double)P.min_p));
   double u;
   if (rng.override_on) {
@@ -341,6 +347,101 @@ __device__ __forceinline__ RowConsts row_consts(const arcs_row_params& P, const 
 // of its row in registers, loaded just before the row's own loads: waiting for
 // them then leaves the row's loads in flight (loads complete in issue order).
 constexpr int kHistRegs = 4;
+
+// Rows without filters weigh every element in double precision: fp32
+// weights carry relative errors near 1e-7, and on rows whose heavy tokens
+// precede long tails of tiny ones that moves many CDF boundaries by more
+// than the tail tokens' widths.  w = 2^(z c) with c = log2(e) / T and no
+// frame (the row maximum keeps |m c| <= kF64Span, else the general path).
+// The group's weights are summed in id order; both the pass and the draw
+// call this, so the draw sees the pass's values exactly.
+constexpr double kF64Span = 960.0;
+__device__ __forceinline__ double group_weights_f64(const float (&z)[8], bool valid, double c, double (&w)[8]) {
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    w[e] = valid ? exp2_f64((double)z[e] * c) : 0.0;
+    s += w[e];
+  }
+  return s;
+}
+
+
+// ---------------------------------------------------------------------------
+// split rows, first half: slice partials.  Grid (P, B), kSplitThreads
+// threads; workgroup (s, row) reads groups [s GS, (s + 1) GS) of its row
+// (GS = ceil(V / 8 / P)) and writes that slice's maximum, the lowest index
+// holding it and, for rows without filters, its double-precision weight
+// sum 2^(z c) (no frame).  Rows with filters or bad parameters are left to
+// the row's own workgroup (nothing is written for them).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSplitThreads) void split_partial_kernel(SampleArgs a) {
+  constexpr int NW = kSplitThreads / kWave;
+  __shared__ float s_m[NW];
+  __shared__ uint32_t s_arg[NW], s_bad[NW];
+  __shared__ double s_sum[NW];
+  const int64_t row = blockIdx.y;
+  const int sl = blockIdx.x, Pn = a.split_P;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const arcs_row_params P = a.params[row];
+  if (row_param_status(P) != ARCS_ROW_OK) return;
+  const bool greedy = P.temperature == 0.0f || P.top_k == 1;
+  const bool nofilter = !greedy && !(P.top_k >= 1 && (int64_t)P.top_k < a.V) && !(P.top_p < 1.0f) &&
+                        !(P.min_p > 0.0f);
+  if (!greedy && !nofilter) return;
+  float chi = 0.0f, clo = 0.0f;
+  if (nofilter && !temp_coeffs(P.temperature, chi, clo)) return;
+  const double c = (double)chi + (double)clo;
+  const int ngroups = (int)(a.V / 8);
+  const int GS = (ngroups + Pn - 1) / Pn;
+  const int g0 = sl * GS, g1 = g0 + GS < ngroups ? g0 + GS : ngroups;
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
+  float best = -__builtin_inff();
+  uint32_t bidx = 0xFFFFFFFFu;
+  bool bad = false;
+  double sum = 0.0;
+  for (int g = g0 + tid; g < g1; g += kSplitThreads) {
+    float z[8];
+    unpack8(rv[g], z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (z[e] > best) { best = z[e]; bidx = (uint32_t)(g * 8 + e); }  // ids increase: the first wins
+      bad = bad || !(z[e] == z[e]) || z[e] == __builtin_inff();
+    }
+    if (nofilter) {
+      double w8[8];
+      sum += group_weights_f64(z, true, c, w8);
+    }
+  }
+  const float wm = dpp_wave_max_f32(best);
+  const uint32_t wa = dpp_wave_min_u32(best == wm ? bidx : 0xFFFFFFFFu);
+  const double ws = dpp_wave_sum_f64(sum);
+  const uint32_t wb = __ballot(bad) != 0 ? 1u : 0u;
+  if (lane == 0) { s_m[wid] = wm; s_arg[wid] = wa; s_sum[wid] = ws; s_bad[wid] = wb; }
+  __syncthreads();
+  if (tid == 0) {
+    float m = s_m[0];
+    uint32_t anybad = s_bad[0];
+    double tot = s_sum[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      m = max2f(m, s_m[w]);
+      tot += s_sum[w];
+      anybad |= s_bad[w];
+    }
+    // the lowest index among the waves holding the maximum (a wave's rounds
+    // interleave with the others', so any wave may hold the lowest)
+    uint32_t arg = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) arg = (s_m[w] == m && s_arg[w] < arg) ? s_arg[w] : arg;
+    if (nofilter && !((double)m * c < kF64Span)) anybad = 1u;
+    SplitPart r;
+    r.m = m;
+    r.arg = anybad ? -1 : (int32_t)(arg == 0xFFFFFFFFu ? 0u : arg);
+    r.s = tot;
+    a.split_parts[row * Pn + sl] = r;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // summary kernel: 512 threads per row (eight waves, two per SIMD, up to 256
@@ -1223,6 +1324,13 @@ hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hi
   static std::atomic<int> done[10];
   if (dtype == ARCS_DTYPE_BF16 && vec && a.V <= kSummaryMaxV && a.V % 8 == 0) {
     const size_t lds = sample_lds_bytes(true, pen, a.V);
+    if (a.split_parts != nullptr) {
+      if (pen || a.split_P < 1 || a.split_P > kSplitMaxP || B > kSplitMaxB) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(split_partial_kernel, dim3((unsigned)a.split_P, (unsigned)B), dim3(kSplitThreads), 0,
+                         stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     return pen ? launch_one(sum512::sample_summary_kernel<true>, true, sum512::kSNT, a, B, lds, stream, done[0])
                : launch_one(sum512::sample_summary_kernel<false>, true, sum512::kSNT, a, B, lds, stream, done[1]);
   }

@@ -145,24 +145,6 @@ __device__ __forceinline__ bool tsum_draw(const SampleArgs& a, int64_t row, cons
   return true;
 }
 
-// Rows without filters weigh every element in double precision: fp32
-// weights carry relative errors near 1e-7, and on rows whose heavy tokens
-// precede long tails of tiny ones that moves many CDF boundaries by more
-// than the tail tokens' widths.  w = 2^(z c) with c = log2(e) / T and no
-// frame (the row maximum keeps |m c| <= kF64Span, else the general path).
-// The group's weights are summed in id order; both the pass and the draw
-// call this, so the draw sees the pass's values exactly.
-constexpr double kF64Span = 960.0;
-__device__ __forceinline__ double group_weights_f64(const float (&z)[8], bool valid, double c, double (&w)[8]) {
-  double s = 0.0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    w[e] = valid ? exp2_f64((double)z[e] * c) : 0.0;
-    s += w[e];
-  }
-  return s;
-}
-
 // The draw for rows without filters over the pass's double weights.  Round
 // q's groups are q * kSNT + tid, so id order is (round, wave, lane,
 // element): the pass left each wave's total of each round (the last lane of
@@ -1443,6 +1425,125 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
   return true;
 }
 
+
+// Split rows, second half (the row's own workgroup): the partials of the
+// row's P slices give the maximum, the lowest index holding it and the
+// row's weight; the draw finds the slice (slices are in id order), then one
+// read of that slice, with the same double weights, the element.  Returns
+// false (uniformly) when a slice saw NaN or +inf, or the weights' exponent
+// range does not hold the row: the row then takes the whole-row path.
+__device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, const arcs_row_params& P,
+                                             const RowConsts& rc, Shared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int Pn = a.split_P;
+  const int64_t V = a.V;
+  const int ngroups = (int)(V / 8);
+  const int GS = (ngroups + Pn - 1) / Pn;
+  const bool greedy = P.temperature == 0.0f || P.top_k == 1;
+  const double c = (double)rc.chi + (double)rc.clo;
+  if (wid == 0) {
+    // lane l holds slices 2l and 2l + 1 (P <= 128)
+    const SplitPart* parts = a.split_parts + row * Pn;
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+    int32_t a0 = 0x7FFFFFFF, a1 = 0x7FFFFFFF;
+    double s0 = 0.0, s1 = 0.0;
+    if (2 * lane < Pn) { const SplitPart p = parts[2 * lane]; m0 = p.m; a0 = p.arg; s0 = p.s; }
+    if (2 * lane + 1 < Pn) { const SplitPart p = parts[2 * lane + 1]; m1 = p.m; a1 = p.arg; s1 = p.s; }
+    const bool bad = __ballot(a0 < 0 || a1 < 0) != 0;
+    const float M = dpp_wave_max_f32(max2f(m0, m1));
+    const uint32_t c0 = m0 == M ? (uint32_t)a0 : 0xFFFFFFFFu, c1 = m1 == M ? (uint32_t)a1 : 0xFFFFFFFFu;
+    const uint32_t argmax = M > -__builtin_inff() ? dpp_wave_min_u32(c0 < c1 ? c0 : c1) : 0u;
+    int32_t mode = 0;  // 0: whole-row path, 1: done, 2: draw in slice sh.i32[1]
+    int sstar = 0;
+    double base = 0.0, t = 0.0;
+    if (bad) {
+      mode = 0;
+    } else if (greedy) {
+      mode = 1;
+      if (lane == 0) {
+        a.out_ids[row] = (int32_t)argmax;
+        if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+      }
+    } else if (M > -__builtin_inff() && (double)M * c > -kF64Span) {
+      const double ls = s0 + s1;
+      const double incl = dpp_wave_incl_scan_f64(ls);
+      const double S = readlane63_f64(incl);
+      if (S > 0.0 && S < 1e300) {
+        t = rc.u * S;
+        const uint64_t hit = __ballot(ls > 0.0 && incl > t);
+        const uint64_t nz = __ballot(ls > 0.0);
+        const int kl = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nz);  // rounding: the last with weight
+        const double ex = incl - ls;
+        // in that lane: slice 2l if its weight passes t, else 2l + 1
+        const bool first = s0 > 0.0 && (ex + s0 > t || !(s1 > 0.0));
+        sstar = __builtin_amdgcn_readlane(2 * lane + (first ? 0 : 1), kl);
+        base = readlane_f64(first ? ex : ex + s0, kl);
+        mode = 2;
+      }
+    }
+    if (lane == 0) {
+      sh.i32[0] = mode;
+      sh.i32[1] = sstar;
+      sh.f64[0] = base;
+      sh.f64[1] = t;
+      sh.i32[2] = -1;  // the last group with weight seen (rounding fallback)
+      sh.u64[10] = ~0ull;
+    }
+  }
+  __syncthreads();
+  const int32_t mode = sh.i32[0];
+  if (mode != 2) return mode == 1;
+  const int sstar = sh.i32[1];
+  double base = sh.f64[0];
+  const double t = sh.f64[1];
+  const int g0 = sstar * GS, g1 = g0 + GS < ngroups ? g0 + GS : ngroups;
+  const u32x4* rv = (const u32x4*)((const char*)a.logits + row * a.stride * 2);
+  for (int r0 = g0; r0 < g1; r0 += kSNT) {
+    const int g = r0 + tid;
+    const bool valid = g < g1;
+    float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (valid) unpack8(rv[g], z);
+    double w8[8];
+    const double gw = group_weights_f64(z, valid, c, w8);
+    const double incl = dpp_wave_incl_scan_f64(gw);
+    if (lane == kWave - 1) sh.rtot[wid] = incl;
+    if (gw > 0.0) atomicMax(&sh.i32[2], g);
+    __syncthreads();
+    double wb = base;  // the total before this thread's wave
+    for (int w = 0; w < wid; ++w) wb += sh.rtot[w];
+    double rt = base;
+    for (int w = 0; w < kSNW; ++w) rt += sh.rtot[w];
+    const uint64_t hit = __ballot(gw > 0.0 && wb + incl > t);
+    if (hit && lane == __builtin_ctzll(hit)) atomicMin((unsigned long long*)&sh.u64[10], (unsigned long long)g);
+    __syncthreads();
+    const uint64_t gsel = sh.u64[10];
+    if (gsel != ~0ull || r0 + kSNT >= g1) {
+      // the group (or, past every boundary by rounding, the last with weight):
+      // its thread walks its elements
+      const int gg = gsel != ~0ull ? (int)gsel : sh.i32[2];
+      if (g == gg) {
+        double acc = wb + (incl - gw);
+        int pe = -1, last_e = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc += w8[e];
+          if (w8[e] > 0.0) {
+            if (pe < 0 && acc > t) pe = e;
+            last_e = e;
+          }
+        }
+        if (pe < 0) pe = last_e;
+        a.out_ids[row] = g * 8 + pe;
+        if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+      }
+      return true;
+    }
+    base = rt;
+    __syncthreads();  // sh.rtot is written again by the next round
+  }
+  return true;
+}
+
 template <bool PEN>
 __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -1459,6 +1560,19 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
     // waits for a load, and the record returns first
     u32x4 p0, p1;
     issue_params_load(a.params + row, p0, p1);
+    if (a.split_parts != nullptr) {
+      // split launch: greedy rows and rows without filters finish from the
+      // slice partials (this waits for the parameter record first)
+      const arcs_row_params P = params_from(p0, p1);
+      const bool greedy = P.temperature == 0.0f || P.top_k == 1;
+      const bool nofilter = !greedy && !(P.top_k >= 1 && (int64_t)P.top_k < a.V) && !(P.top_p < 1.0f) &&
+                            !(P.min_p > 0.0f);
+      if (row_param_status(P) == ARCS_ROW_OK && (greedy || nofilter)) {
+        const RowConsts rc = row_consts(P, load_row_rng(a, row), row);
+        if (rc.ok && split_finish(a, row, P, rc, sh)) return;
+        __syncthreads();
+      }
+    }
     issue_row_loads(rv, ngroups, d);
     arcs_row_params P = params_from(p0, p1);
     const RowRng rng = load_row_rng(a, row);

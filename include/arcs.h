@@ -171,9 +171,19 @@ int arcs_argmax(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
  *   seed, step     RNG key, by value
  *   out_ids        device int32[B]; -1 for rows with invalid parameters
  *   out_status     device int32[B] per-row codes, or NULL
- *   workspace      device scratch of workspace_bytes (may be NULL when
- *                  arcs_sample_workspace_bytes() returns 0)
- * Returns ARCS_OK or a negative arcs_status.
+ *   workspace      device scratch of workspace_bytes, 16-byte aligned, owned by
+ *                  the caller and not read before it is written; may be NULL
+ *                  when arcs_sample_workspace_bytes() returns 0.  Batches of
+ *                  at most 64 bf16 rows with 8192 <= V <= 131072, V % 8 == 0
+ *                  use it: their greedy rows and rows without filters are read
+ *                  by P = clamp(512 / B, 8, 128) workgroups per row, which
+ *                  leave per-slice partials (16 bytes each) there for the
+ *                  row's own workgroup.  Calls that share a workspace must be
+ *                  ordered on one stream.
+ * Returns ARCS_OK or a negative arcs_status (ARCS_ERR_WORKSPACE_TOO_SMALL
+ * when workspace_bytes is below arcs_sample_workspace_bytes(),
+ * ARCS_ERR_NULL_POINTER for a NULL workspace the shape needs,
+ * ARCS_ERR_MISALIGNED for a workspace not 16-byte aligned).
  */
 int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                 const arcs_row_params* params, const int32_t* hist_ids,
@@ -202,7 +212,9 @@ int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64
                       const int64_t* hist_offsets, uint64_t* key, int advance, int32_t* out_ids,
                       int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace arcs_sample needs for this shape (may be 0). */
+/* Bytes of device workspace arcs_sample, arcs_sample_keyed and
+ * arcs_sample_debug need for this shape: B * P * 16 for the split batches
+ * described under arcs_sample, else 0. */
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype);
 
 /* Human-readable text for an arcs_status or ARCS_ROW_* code. */

@@ -69,6 +69,18 @@ def test_host_validation_rejects_before_launch(arcs):
     assert S(p, 0, 4, 10, 10, p, None, p, 0, 0, p, None, None, 0, None) == -9
     assert S(p, 0, 4, 10, 5, p, None, None, 0, 0, p, None, None, 0, None) == -4
     assert S(p, 3, 4, 10, 10, p, None, None, 0, 0, p, None, None, 0, None) == -5
+    # small bf16 batches need the split workspace: B * clamp(512 / B, 8, 128) * 16 bytes
+    W = lib.arcs_sample_workspace_bytes
+    for B in (1, 3, 4, 17, 64):
+        assert W(B, 129_280, 0) == B * min(128, max(8, -(-512 // B))) * 16
+    assert W(65, 129_280, 0) == 0 and W(4, 129_280, 1) == 0 and W(4, 8184, 0) == 0
+    assert W(4, 131_080, 0) == 0 and W(4, 20_004, 0) == 0 and W(4, 8192, 0) == 4 * 128 * 16
+    need = W(4, 129_280, 0)
+    V = 129_280
+    assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, None, 0, None) == -6
+    assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, p, need - 1, None) == -6
+    assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, None, need, None) == -1
+    assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, ctypes.c_void_p(base + 8), need, None) == -8
     # sample with a device key: the key is checked before anything else runs
     K = lib.arcs_sample_keyed
     assert K(p, 0, 4, 10, 10, p, None, None, None, 1, p, None, None, 0, None) == -1
