@@ -34,6 +34,8 @@ ERR_MISALIGNED = -8
 ERR_BAD_HISTORY = -9
 ERR_BAD_TOP_N = -10
 ERR_BAD_CAPACITY = -11
+ERR_SCRATCH_TOO_SMALL = -12
+NOALLOC_SCRATCH_BYTES = 16384
 ROW_OK = 0
 ROW_BAD_TEMPERATURE = 1
 ROW_BAD_TOP_P = 2
@@ -95,6 +97,9 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_debug.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p, c_p, c_p, c_p]
         lib.arcs_sample_debug.restype = c_i
+        lib.arcs_sample_noalloc.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
+                                             c_p, c_p, c_p]
+        lib.arcs_sample_noalloc.restype = c_i
         lib.arcs_sample_keyed.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_i,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p]
         lib.arcs_sample_keyed.restype = c_i
@@ -289,6 +294,28 @@ def sample(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step
                                ws_bytes, _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_sample")
+    return out
+
+
+def sample_noalloc(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step: int = 0,
+                   out=None, out_status=None, stream=None):
+    """arcs_sample_noalloc: as sample, with the library's own device scratch
+    instead of a workspace (the C call allocates nothing; pass `out` to keep
+    this wrapper from allocating it)."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    _check_params(params, B)
+    _check_hist(hist_ids, hist_offsets, B)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_out(out, torch.int32, B, "out")
+    if out_status is not None:
+        _check_out(out_status, torch.int32, B, "out_status")
+    st = library().arcs_sample_noalloc(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),
+                                       _ptr(hist_ids), _ptr(hist_offsets), int(seed) & (2**64 - 1),
+                                       int(step) & (2**64 - 1), _ptr(out), _ptr(out_status), _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample_noalloc")
     return out
 
 

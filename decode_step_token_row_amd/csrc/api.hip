@@ -6,12 +6,38 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "arcs.h"
 #include "launch.hpp"
 
-
+// Device scratch of arcs_sample_noalloc: one copy per GPU, held until the
+// process ends, at its own address on each device.  Host code never uses the
+// symbol itself (on the host it is only a stand-in): the address comes from
+// hipGetSymbolAddress with that device current, cached per device.
+static __device__ __align__(256) unsigned char scratch[ARCS_NOALLOC_SCRATCH_BYTES];
+static_assert(arcs::split_max_workspace() <= ARCS_NOALLOC_SCRATCH_BYTES, "the scratch holds every split workspace");
 
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on the first call there).
+// Two threads racing on a first call store the same address.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ARCS_ERR_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return ARCS_ERR_LAUNCH;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  *out = p;
+  return ARCS_OK;
+}
 
 constexpr int64_t kMaxDim = 2147483647;
 
@@ -109,6 +135,22 @@ int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
                      stream);
 }
 
+int arcs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                        const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                        uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status, void* stream) {
+  int st = check_common(logits, dtype, B, V, row_stride, out_ids);
+  if (st != ARCS_OK) return st;
+  const size_t need = arcs_sample_workspace_bytes(B, V, dtype);
+  if (need > (size_t)ARCS_NOALLOC_SCRATCH_BYTES) return ARCS_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != ARCS_OK) return st;
+  }
+  return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step, nullptr,
+                     out_ids, out_status, ws, need, nullptr, nullptr, nullptr, stream);
+}
+
 int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                       const arcs_row_params* params, const int32_t* hist_ids,
                       const int64_t* hist_offsets, uint64_t* key, int advance, int32_t* out_ids,
@@ -169,6 +211,8 @@ const char* arcs_status_string(int code) {
     case ARCS_ERR_BAD_STRIDE: return "row_stride must be >= V";
     case ARCS_ERR_BAD_DTYPE: return "dtype must be ARCS_DTYPE_BF16 or ARCS_DTYPE_F32";
     case ARCS_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than arcs_sample_workspace_bytes()";
+    case ARCS_ERR_SCRATCH_TOO_SMALL:
+      return "the shape needs more workspace than arcs_sample_noalloc's scratch (ARCS_NOALLOC_SCRATCH_BYTES)";
     case ARCS_ERR_LAUNCH: return "kernel launch failed";
     case ARCS_ERR_MISALIGNED: return "logits pointer not aligned to its element size";
     case ARCS_ERR_BAD_HISTORY: return "hist_ids and hist_offsets must both be NULL or both be set";

@@ -51,9 +51,18 @@ constexpr int64_t kSplitMinV = 8192;   // and rows of at least this many tokens
 constexpr int kSplitMaxP = 128;        // slices per row
 constexpr int kSplitThreads = 256;     // threads per slice workgroup
 // P = 512 / B slices (at least 8, at most kSplitMaxP): about 512 workgroups
-inline int split_slices(int64_t B) {
+constexpr int split_slices(int64_t B) {
   const int64_t p = (512 + B - 1) / B;
   return (int)(p < 8 ? 8 : (p > kSplitMaxP ? kSplitMaxP : p));
+}
+// The largest split workspace of any batch size.
+constexpr size_t split_max_workspace() {
+  size_t m = 0;
+  for (int64_t b = 1; b <= kSplitMaxB; ++b) {
+    const size_t w = (size_t)b * (size_t)split_slices(b) * sizeof(SplitPart);
+    m = w > m ? w : m;
+  }
+  return m;
 }
 // Whether a launch of this shape and element type takes the split path (the
 // kernel also needs 16-byte aligned rows, no history and no debug outputs).

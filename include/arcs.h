@@ -52,7 +52,8 @@ typedef enum arcs_status {
   ARCS_ERR_MISALIGNED = -8,          /* logits not aligned to the element size  */
   ARCS_ERR_BAD_HISTORY = -9,         /* exactly one of hist_ids/hist_offsets is NULL */
   ARCS_ERR_BAD_TOP_N = -10,          /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
-  ARCS_ERR_BAD_CAPACITY = -11        /* arcs_commit_tokens: capacity 0, or capacity * B too large */
+  ARCS_ERR_BAD_CAPACITY = -11,       /* arcs_commit_tokens: capacity 0, or capacity * B too large */
+  ARCS_ERR_SCRATCH_TOO_SMALL = -12   /* arcs_sample_noalloc: the shape needs more than its scratch */
 } arcs_status;
 
 /* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
@@ -211,6 +212,25 @@ int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64
                       const arcs_row_params* params, const int32_t* hist_ids,
                       const int64_t* hist_offsets, uint64_t* key, int advance, int32_t* out_ids,
                       int32_t* out_status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * arcs_sample_noalloc: arcs_sample for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid
+ * allocation).  It takes no workspace: shapes that need one use a device
+ * array inside the library, ARCS_NOALLOC_SCRATCH_BYTES per GPU, allocated
+ * with the library's code object and held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library routine that allocates); the
+ * first call on a device looks up that device's copy of the array.
+ * Every call on one GPU shares that GPU's array: calls on one GPU that may
+ * overlap (other streams, other host threads) race and must be ordered by
+ * the caller.  Shapes needing more than the array (none today: the largest
+ * split workspace is 567 * 16 = 9,072 bytes) get ARCS_ERR_SCRATCH_TOO_SMALL before
+ * any launch.  Arguments, outputs and other errors as arcs_sample.
+ */
+#define ARCS_NOALLOC_SCRATCH_BYTES 16384
+int arcs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                        const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                        uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status, void* stream);
 
 /* Bytes of device workspace arcs_sample, arcs_sample_keyed and
  * arcs_sample_debug need for this shape: B * P * 16 for the split batches

@@ -19,7 +19,7 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
                  "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs",
-                 "arcs_commit_tokens"):
+                 "arcs_commit_tokens", "arcs_sample_noalloc"):
         assert name in fns
 
 
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(arcs):
 
 
 def test_status_strings_and_version(arcs):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, 1, 2, 3, 4, 5, 6, 7]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12, 1, 2, 3, 4, 5, 6, 7]:
         assert arcs.status_string(code) != "unknown status", code
     assert arcs.status_string(12345) == "unknown status"
     assert arcs.version() >= 100
@@ -81,6 +81,15 @@ def test_host_validation_rejects_before_launch(arcs):
     assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, p, need - 1, None) == -6
     assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, None, need, None) == -1
     assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, ctypes.c_void_p(base + 8), need, None) == -8
+    # the no-allocation variant checks its arguments first too
+    N = lib.arcs_sample_noalloc
+    assert N(None, 0, 4, 10, 10, p, None, None, 0, 0, p, None, None) == -1
+    assert N(p, 0, 4, 10, 10, p, None, None, 0, 0, None, None, None) == -1
+    assert N(p, 5, 4, 10, 10, p, None, None, 0, 0, p, None, None) == -5
+    assert N(p, 0, 0, 10, 10, p, None, None, 0, 0, p, None, None) == -2
+    assert N(p, 0, 4, 10, 9, p, None, None, 0, 0, p, None, None) == -4
+    assert N(p, 0, 4, 10, 10, None, None, None, 0, 0, p, None, None) == -1
+    assert N(p, 0, 4, 10, 10, p, p, None, 0, 0, p, None, None) == -9
     # sample with a device key: the key is checked before anything else runs
     K = lib.arcs_sample_keyed
     assert K(p, 0, 4, 10, 10, p, None, None, None, 1, p, None, None, 0, None) == -1
