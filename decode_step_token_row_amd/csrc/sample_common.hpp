@@ -84,6 +84,7 @@ struct PenCtx {
   const uint16_t* wprefix;
   const float* zpen;       // general path: penalised logit per distinct id
   const uint32_t* pcount;  // summary path: occurrence count per distinct id
+  uint32_t hmask;          // summary path: bit q set when this thread's group of round q holds a history id
 };
 
 // Rank of a history id among the row's distinct history ids (id order).

@@ -747,7 +747,7 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
     asm volatile("" : "+v"(dq));
     float z[8];
     unpack8(dq, z);
-    if (PEN && pc.on && valid) penalize8(z, (int64_t)(q * kSNT + tid) * 8, pc);
+    if (PEN && ((pc.hmask >> q) & 1u)) penalize8(z, (int64_t)(q * kSNT + tid) * 8, pc);
     float g = group_max(z);
     special = special || !(g == g);
     g = valid && g == g ? g : -__builtin_inff();
@@ -1388,12 +1388,24 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
                                                    int status, PenCtx& pc, const RowHist& hs, uint32_t& path) {
   const int tid = threadIdx.x;
   pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
+  pc.hmask = 0u;
+  // per thread, the rounds whose group holds a history id (kept in the bound
+  // histogram's area, free until after the pass): the pass looks up the
+  // tables only in those rounds
+  static_assert((size_t)kBins * 8 >= (size_t)kSNT * 4 && kSQ <= 32, "a history round mask per thread");
+  uint32_t* hm = sm.bcnt;
   if (status == ARCS_ROW_OK && pc.on) {
     const uint32_t bw = a.bitmap_words;
     for (uint32_t i = tid; i < bw; i += kSNT) sm.bitmap[i] = 0u;
+    hm[tid] = 0u;
     lds_barrier();
-    for_each_hist_id<false>(a, row, hs, [&](uint32_t id, float) { atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31)); });
+    for_each_hist_id<false>(a, row, hs, [&](uint32_t id, float) {
+      atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31));
+      const uint32_t g = id >> 3;
+      atomicOr(&hm[g & (kSNT - 1)], 1u << (g / kSNT));
+    });
     lds_barrier();
+    pc.hmask = hm[tid];
     const uint32_t per = (bw + kSNT - 1) / kSNT;
     const uint32_t w0 = tid * per, w1 = (w0 + per < bw) ? w0 + per : bw;
     uint32_t c = 0;
