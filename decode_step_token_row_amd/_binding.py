@@ -42,6 +42,7 @@ ROW_BAD_TOP_P = 2
 ROW_BAD_MIN_P = 3
 ROW_BAD_PENALTY = 4
 ROW_BAD_FLAGS = 5
+ROW_TIES_WIDE = 1  # arcs_row_params.flags bit
 ROW_HISTORY_TOO_LONG = 6
 ROW_VOCAB_TOO_LARGE = 7
 MAX_HISTORY = 4096

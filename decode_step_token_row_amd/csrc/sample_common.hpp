@@ -389,7 +389,7 @@ __device__ __forceinline__ int row_param_status(const arcs_row_params& P) {
   if (!(__builtin_isfinite(P.presence) && __builtin_isfinite(P.frequency) && __builtin_isfinite(P.repetition)) ||
       P.repetition < 0.0f)
     return ARCS_ROW_BAD_PENALTY;
-  if (P.flags != 0) return ARCS_ROW_BAD_FLAGS;
+  if ((P.flags & ~ARCS_ROW_TIES_WIDE) != 0) return ARCS_ROW_BAD_FLAGS;
   return ARCS_ROW_OK;
 }
 
@@ -691,6 +691,8 @@ __device__ __forceinline__ void generic_row(const SampleArgs& a, int64_t row, co
         if (rp < 1) rp = 1;
         if (rp < r) r = rp;
       }
+      // the wide tie rule keeps every id tied at the cut value
+      if (P.flags & ARCS_ROW_TIES_WIDE) r = cnt_eq;
       kc.mode = 2;
       kc.theta = theta;
       S_K = mass_above + r * Wt;

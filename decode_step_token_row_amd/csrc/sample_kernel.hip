@@ -936,6 +936,8 @@ __device__ __forceinline__ bool f32_sample_row(const SampleArgs& a, int64_t row,
   const bool pon = P.top_p < 1.0f;
   const bool mon = P.min_p > 0.0f;
   const bool nofilter = !kon && !pon && !mon;
+  // rows under the wide tie rule run on the general pipeline
+  if ((P.flags & ARCS_ROW_TIES_WIDE) && (kon || pon)) return false;
   const bool hist = kon || pon;
   path |= ARCS_PATH_REREAD;
   const Smem sm = carve_f32(smem_raw);

@@ -958,6 +958,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   bool lazy = !PEN && pon && kon;
 
   if (!rc.ok) return false;
+  // rows under the wide tie rule run on the general pipeline
+  if ((P.flags & ARCS_ROW_TIES_WIDE) && (kon || pon)) return false;
   const float chi = rc.chi, clo = rc.clo;
   const double tdl = rc.tdl, u = rc.u;
 

@@ -63,7 +63,7 @@ enum {
   ARCS_ROW_BAD_TOP_P = 2,            /* top_p NaN or <= 0                       */
   ARCS_ROW_BAD_MIN_P = 3,            /* min_p NaN, < 0 or > 1                   */
   ARCS_ROW_BAD_PENALTY = 4,          /* non-finite penalty, or repetition < 0   */
-  ARCS_ROW_BAD_FLAGS = 5,            /* flags != 0                              */
+  ARCS_ROW_BAD_FLAGS = 5,            /* flags has a bit other than ARCS_ROW_TIES_WIDE */
   ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY distinct ids */
   ARCS_ROW_VOCAB_TOO_LARGE = 7       /* penalties active and V > ARCS_MAX_PENALTY_VOCAB */
 };
@@ -101,10 +101,14 @@ enum {
  *   repetition   1 (or 0) => off; z = z > 0 ? z / r : z * r for history ids
  *                (applied first, then frequency, then presence; each an
  *                IEEE binary32 operation without fused multiply-add)
- *   flags        must be 0
+ *   flags        0, or ARCS_ROW_TIES_WIDE: the kept prefix grows to every id
+ *                whose value equals that of its last id (the wider tie rule
+ *                the pages report for their fallback device selector, Arc PR
+ *                #194, squashed commit #130); other bits are a row error
  * The kept set is the shortest of the three prefixes (no renormalisation
  * between filters).
  */
+#define ARCS_ROW_TIES_WIDE 1
 typedef struct arcs_row_params {
   float temperature;
   int32_t top_k;

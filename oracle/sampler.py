@@ -69,6 +69,9 @@ ROW_BAD_MIN_P = 3
 ROW_BAD_PENALTY = 4
 ROW_BAD_FLAGS = 5
 
+# Row flags (arcs_row_params.flags).
+ROW_TIES_WIDE = 1   # keep every id sharing the value of the kept prefix's last id
+
 
 # --------------------------------------------------------------------------
 # step 8: SplitMix64 uniform
@@ -237,6 +240,16 @@ def cutoff(z: np.ndarray, w: np.ndarray, top_k: int, top_p: float, min_p: float,
     return Cutoff(order, L, L_k, L_p, L_m, S, margin_p, margin_m, near_p, near_m)
 
 
+def widen_ties(z: np.ndarray, order: np.ndarray, L: int) -> int:
+    """The wide tie rule, the alternative the pages report for their device
+    fallback selector (Arc PR #194, squashed commit #130, "hybrid nucleus
+    selector": on tied supports it keeps every token sharing the boundary bit
+    pattern, erring wider): the kept prefix of length L grows to every id whose
+    value equals that of its last element, i.e. to all ids with z >= that value."""
+    vb = z[order[L - 1]]
+    return int(np.count_nonzero(z >= vb))
+
+
 # --------------------------------------------------------------------------
 # steps 9-10: inverse-CDF draw in token-id order
 # --------------------------------------------------------------------------
@@ -301,7 +314,7 @@ def validate(p) -> int:
     pres, freq, rep = float(p["presence"]), float(p["frequency"]), float(p["repetition"])
     if not (math.isfinite(pres) and math.isfinite(freq) and math.isfinite(rep)) or rep < 0:
         return ROW_BAD_PENALTY
-    if int(p["flags"]) != 0:
+    if int(p["flags"]) & ~ROW_TIES_WIDE:
         return ROW_BAD_FLAGS
     return ROW_OK
 
@@ -321,6 +334,8 @@ def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], s
         return RowResult(status=ROW_OK, id=am, greedy=True, argmax=am, max_logit=float(z[am]))
     _, w = weights(z, T)
     c = cutoff(z, w, top_k, float(p["top_p"]), float(p["min_p"]), band_p, band_m)
+    if int(p["flags"]) & ROW_TIES_WIDE:
+        c.L = widen_ties(z, c.order, c.L)
     kept = np.sort(c.order[: c.L])
     wk = w[kept]
     S_K = math.fsum(wk.tolist())

@@ -355,6 +355,49 @@ def test_invalid_rows_get_status_and_minus_one(arcs):
     _compare_rows(ids, stats, refs, "invalid")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 129_280), ("f32", 129_280), ("bf16", 20_005)])
+def test_wide_tie_rule_rows(arcs, dtype, V):
+    """Rows with ARCS_ROW_TIES_WIDE: the kept prefix grows to every id tied at
+    its last value.  bf16 rows are full of ties (most values repeat), so top-k
+    and top-p cuts usually fall inside a tie group; the debug stats' kept size
+    and cut must be the oracle's, and the ids must agree, on every kernel the
+    shape would take (the fast kernels hand these rows to the general one)."""
+    B = 32
+    w = make_workload("zipf_b256_bf16_greedy" if dtype == "bf16" else "flat_b1024_f32_t1_p0.95",
+                      B=B, V=V, seed=13, step=2)
+    if dtype == "f32":
+        w.logits = np.round(w.logits * 16.0).astype(np.float32) / 16.0  # coarse grid: ties
+    rng = np.random.default_rng(V)
+    p = make_params(B, temperature=1.0, flags=arcs.ROW_TIES_WIDE)
+    for b in range(B):
+        mode = b % 4
+        p[b]["temperature"] = float(rng.uniform(0.5, 1.3))
+        if mode == 0:
+            p[b]["top_k"] = int(rng.integers(2, 3000))
+        elif mode == 1:
+            p[b]["top_p"] = float(rng.uniform(0.3, 0.95))
+        elif mode == 2:
+            p[b]["top_k"] = int(rng.integers(20, 400))
+            p[b]["top_p"] = float(rng.uniform(0.5, 0.99))
+        else:
+            p[b]["min_p"] = float(rng.uniform(0.01, 0.2))
+            p[b]["top_k"] = int(rng.integers(5, 60))
+    w.params = p
+    ids, status, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    assert np.all(status == 0)
+    _compare_rows(ids, stats, refs, f"wide {dtype} V={V}")
+    # the rule widened most rows here, and the strict rule gives other sets
+    strict = w.params.copy()
+    strict["flags"] = 0
+    refs_strict = oracle.sample(w.logits, w.dtype, strict, None, None, w.seed, w.step)
+    grew = sum(r.L > q.L for r, q in zip(refs, refs_strict))
+    assert grew >= B // 4, grew
+    got = arcs.sample(to_device_logits(w.logits, w.dtype), arcs.params_to_device(w.params),
+                      seed=w.seed, step=w.step).cpu().numpy()
+    assert np.array_equal(got, ids)
+
+
 def test_history_limits(arcs):
     import torch
     V = 5000

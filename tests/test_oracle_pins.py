@@ -252,6 +252,64 @@ def test_topp_set_bruteforce():
     assert checked > 250
 
 
+def _bf_wide(z, strict):
+    """The wide rule by its definition: the strict set plus every id whose
+    value equals the smallest value in it."""
+    vb = min(z[i] for i in strict)
+    return set(strict) | {i for i in range(len(z)) if z[i] == vb}
+
+
+def test_wide_ties_bruteforce():
+    rng = np.random.default_rng(14)
+    grew = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 10))
+        z = o.widen(rng.integers(-2, 3, V).astype(np.float32), "f32")
+        if rng.random() < 0.5:
+            k = int(rng.integers(2, V + 1))
+            kw = dict(temperature=1.0, top_k=k)
+            strict = _bf_topk(z, min(k, V))
+        else:
+            T = float(np.float32(rng.uniform(0.3, 2.0)))
+            pp = float(np.float32(rng.uniform(0.05, 0.99)))
+            kw = dict(temperature=T, top_p=pp)
+            r0 = o.sample_row(z, "f32", _p(**kw), None, 1, 0, 0)
+            if r0.margin_p < 1e-12:
+                continue
+            strict = _bf_topp(z, _softmax_w(z, T), pp)
+        r = o.sample_row(z, "f32", _p(flags=o.ROW_TIES_WIDE, **kw), None, 1, 0, 0)
+        want = _bf_wide(z, strict)
+        assert r.status == 0 and set(r.kept.tolist()) == want, (z, kw, strict, want)
+        grew += len(want) > len(strict)
+    assert grew > 50
+
+
+def test_wide_ties_on_a_tied_diffuse_support():
+    """105 tokens of distinct values, then 11 tied at a lower value; top_p set
+    so that the crossing falls on the 6th tied token: the strict prefix keeps
+    111 tokens, the wide rule 116 (the sizes the pages report for their
+    fallback selector on a tied diffuse support)."""
+    z = np.full(300, -50.0, dtype=np.float32)
+    z[:105] = np.linspace(2.0, 1.0, 105, dtype=np.float32)
+    z[105:116] = 0.5
+    zz = o.widen(z, "f32")
+    _, w = o.weights(zz, 1.0)
+    order = o.total_order(zz)
+    cum = np.cumsum(w[order])
+    p = float(np.float32((cum[109] + 0.5 * w[105]) / cum[-1]))
+    strict = o.sample_row(z, "f32", _p(temperature=1.0, top_p=p), None, 1, 0, 0)
+    wide = o.sample_row(z, "f32", _p(temperature=1.0, top_p=p, flags=o.ROW_TIES_WIDE), None, 1, 0, 0)
+    assert strict.L == 111 and wide.L == 116
+    assert set(wide.kept.tolist()) == set(range(116))
+    # top-k at the same place: k = 111 keeps 111 strictly, 116 wide
+    assert o.sample_row(z, "f32", _p(temperature=1.0, top_k=111, flags=o.ROW_TIES_WIDE), None, 1, 0, 0).L == 116
+    assert o.sample_row(z, "f32", _p(temperature=1.0, top_k=111), None, 1, 0, 0).L == 111
+    # min-p sets are defined by value: the flag changes nothing
+    a = o.sample_row(z, "f32", _p(temperature=1.0, min_p=0.5), None, 1, 0, 0)
+    b = o.sample_row(z, "f32", _p(temperature=1.0, min_p=0.5, flags=o.ROW_TIES_WIDE), None, 1, 0, 0)
+    assert a.L == b.L
+
+
 def test_minp_set_against_softmax_definition():
     rng = np.random.default_rng(6)
     for _ in range(200):
@@ -413,7 +471,7 @@ def test_invalid_params_give_status_and_minus_one():
              (dict(top_p=0.0), o.ROW_BAD_TOP_P), (dict(top_p=np.nan), o.ROW_BAD_TOP_P),
              (dict(min_p=-0.1), o.ROW_BAD_MIN_P), (dict(min_p=1.5), o.ROW_BAD_MIN_P),
              (dict(repetition=-1.0), o.ROW_BAD_PENALTY), (dict(presence=np.inf), o.ROW_BAD_PENALTY),
-             (dict(flags=1), o.ROW_BAD_FLAGS)]
+             (dict(flags=2), o.ROW_BAD_FLAGS), (dict(flags=-1), o.ROW_BAD_FLAGS)]
     for kw, code in cases:
         r = o.sample_row(z, "f32", _p(**kw), None, 0, 0, 0)
         assert r.status == code and r.id == -1
@@ -465,6 +523,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
             return c
         m.setattr(o, "cutoff", renorm)
         assert _red(test_combined_filters_take_the_shortest_prefix_without_renormalising)
+    # the wide rule not applied, or applied without the ties themselves
+    with monkeypatch.context() as m:
+        m.setattr(o, "widen_ties", lambda z, order, L: L)
+        assert _red(test_wide_ties_bruteforce)
+        assert _red(test_wide_ties_on_a_tied_diffuse_support)
+    with monkeypatch.context() as m:
+        m.setattr(o, "widen_ties", lambda z, order, L: max(L, int(np.count_nonzero(z > z[order[L - 1]]))))
+        assert _red(test_wide_ties_bruteforce)
     # a draw margin of zero (every mismatch would be excused)
     with monkeypatch.context() as m:
         real = o.draw
