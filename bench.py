@@ -20,6 +20,11 @@ bubble from the host's enqueue rate); HIP events on the launch stream
 bracket exactly K steps.  The headline is also timed as one HIP graph of
 the K launches.
 
+After them, `nucleus_ab` times nucleus (top-p 0.95) sampling on rows whose
+mass sits on 1 .. 12,928 tokens, arcs_sample against the baseline hybrid
+selector of arcs_sample_hybrid_nucleus (enumeration up to 32 ids, then
+threshold bisection), at B = 1.
+
 Prints ONE JSON line: rows/s (= tokens/s), ms per step, the roofline object
 of the sampling kernel (algorithmic bytes per launch over its average launch
 duration, against MI355X's 8 TB/s HBM peak; counted HBM traffic from the
@@ -356,6 +361,54 @@ def measure(arcs, torch, gate, w, name, steps, warmup, event_launches, graph=Fal
     return rec
 
 
+def nucleus_ab(arcs, torch, gate, widths=(1, 8, 64, 512, 4096, 12928), B=1, V=129_280, launches=20,
+               budget=32):
+    """Nucleus sampling on rows whose mass sits on `width` tokens (the pages'
+    support-width sweep for their device selector): arcs_sample with top_p
+    0.95 against the baseline hybrid selector (enumeration up to `budget` ids,
+    then 32-step bisection), µs per launch of each (HIP events, gated)."""
+    from workloads import f32_to_bf16_bits, make_params
+    rng = np.random.default_rng(7)
+    dev = torch.device("cuda:0")
+    out = []
+    for wdt in widths:
+        z = np.full((B, V), -60.0, dtype=np.float32)
+        for b in range(B):
+            z[b, rng.choice(V, size=wdt, replace=False)] = rng.normal(0.0, 0.5, wdt)
+        logits = torch.from_numpy(f32_to_bf16_bits(z).view(np.int16)).view(torch.bfloat16).to(dev)
+        params = arcs.params_to_device(make_params(B, temperature=1.0, top_p=0.95), dev)
+        T = torch.full((B,), 1.0, dtype=torch.float32, device=dev)
+        P = torch.full((B,), 0.95, dtype=torch.float32, device=dev)
+        ids = torch.empty(B, dtype=torch.int32, device=dev)
+        kept = torch.empty(B, dtype=torch.int32, device=dev)
+        ws = arcs.workspace_bytes(B, V, arcs.DTYPE_BF16)
+        wsb = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        runs = {
+            "arcs_sample_us": lambda i: arcs.sample(logits, params, seed=1, step=i, out=ids, workspace=wsb),
+            "hybrid_us": lambda i: arcs.sample_hybrid_nucleus(logits, T, P, budget, seed=1, step=i, out=ids,
+                                                              out_kept=kept),
+        }
+        rec = {"support_width": wdt, "B": B, "V": V, "top_p": 0.95, "budget": budget}
+        for name, fn in runs.items():
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gate.sleep(500.0 + 40.0 * launches)
+            e0.record()
+            for i in range(launches):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            rec[name] = e0.elapsed_time(e1) / launches * 1e3
+        rec["hybrid_kept"] = int(kept[0].item())
+        rec["hybrid_path"] = "enumeration" if rec["hybrid_kept"] <= budget else "bisection"
+        log(f"[bench] nucleus width {wdt}: arcs_sample {rec['arcs_sample_us']:.1f} us, "
+            f"hybrid {rec['hybrid_us']:.1f} us ({rec['hybrid_path']}, kept {rec['hybrid_kept']})")
+        out.append(rec)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +474,7 @@ def main():
             ws = make_workload(name)
             subs.append(measure(arcs, torch, gate, ws, name, min(args.steps, args.sub_steps),
                                 min(args.warmup, 10), min(args.event_launches, 20)))
+    ab = nucleus_ab(arcs, torch, gate) if not args.only else None
 
     ms_per_step = head["us_per_step"] * 1e-3
     roof = dict(head["roofline"])
@@ -458,6 +512,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "sub_records": subs,
+        "nucleus_ab": ab,
     }
     print(json.dumps(res), flush=True)
 

@@ -35,6 +35,7 @@ ERR_BAD_HISTORY = -9
 ERR_BAD_TOP_N = -10
 ERR_BAD_CAPACITY = -11
 ERR_SCRATCH_TOO_SMALL = -12
+ERR_BAD_BUDGET = -13
 NOALLOC_SCRATCH_BYTES = 16384
 ROW_OK = 0
 ROW_BAD_TEMPERATURE = 1
@@ -98,6 +99,9 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_debug.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p, c_p, c_p, c_p]
         lib.arcs_sample_debug.restype = c_i
+        lib.arcs_sample_hybrid_nucleus.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_i, c_u64, c_u64,
+                                                    c_p, c_p, c_p, c_p]
+        lib.arcs_sample_hybrid_nucleus.restype = c_i
         lib.arcs_sample_noalloc.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
                                              c_p, c_p, c_p]
         lib.arcs_sample_noalloc.restype = c_i
@@ -317,6 +321,29 @@ def sample_noalloc(logits, params, hist_ids=None, hist_offsets=None, seed: int =
                                        int(step) & (2**64 - 1), _ptr(out), _ptr(out_status), _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_sample_noalloc")
+    return out
+
+
+def sample_hybrid_nucleus(logits, temperature, top_p, budget: int = 32, seed: int = 0, step: int = 0,
+                          out=None, out_kept=None, out_status=None, stream=None):
+    """arcs_sample_hybrid_nucleus: the baseline enumeration / bisection nucleus
+    sampler (per-row float32 temperature and top_p on the device)."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    for name, t in (("temperature", temperature), ("top_p", top_p)):
+        _check_out(t, torch.float32, B, name)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_out(out, torch.int32, B, "out")
+    for name, t in (("out_kept", out_kept), ("out_status", out_status)):
+        if t is not None:
+            _check_out(t, torch.int32, B, name)
+    st = library().arcs_sample_hybrid_nucleus(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(temperature),
+                                              _ptr(top_p), int(budget), int(seed) & (2**64 - 1),
+                                              int(step) & (2**64 - 1), _ptr(out), _ptr(out_kept),
+                                              _ptr(out_status), _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample_hybrid_nucleus")
     return out
 
 

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libarcs.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "argmax_kernel.hip", "sample_kernel.hip", "logprobs_kernel.hip", "commit_kernel.hip"]
+SOURCES = ["api.hip", "argmax_kernel.hip", "sample_kernel.hip", "logprobs_kernel.hip", "commit_kernel.hip",
+           "hybrid_kernel.hip"]
 ARCH = os.environ.get("ARCS_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [

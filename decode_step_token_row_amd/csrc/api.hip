@@ -174,6 +174,33 @@ int arcs_sample_debug(const void* logits, int dtype, int64_t B, int64_t V, int64
                      out_stats, stream);
 }
 
+int arcs_sample_hybrid_nucleus(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                               const float* temperature, const float* top_p, int budget, uint64_t seed,
+                               uint64_t step, int32_t* out_ids, int32_t* out_kept, int32_t* out_status,
+                               void* stream) {
+  int st = check_common(logits, dtype, B, V, row_stride, out_ids);
+  if (st != ARCS_OK) return st;
+  if (temperature == nullptr || top_p == nullptr) return ARCS_ERR_NULL_POINTER;
+  if (dtype != ARCS_DTYPE_BF16) return ARCS_ERR_BAD_DTYPE;
+  if (V % 8 != 0 || V > 131072) return ARCS_ERR_BAD_VOCAB;
+  if (!rows_16b_aligned(logits, dtype, row_stride)) return ARCS_ERR_MISALIGNED;
+  if (((uintptr_t)temperature) % 4u != 0 || ((uintptr_t)top_p) % 4u != 0) return ARCS_ERR_MISALIGNED;
+  if (budget < 0 || budget > 4096) return ARCS_ERR_BAD_BUDGET;
+  arcs::HybridArgs a;
+  a.logits = logits;
+  a.V = V;
+  a.stride = row_stride;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.budget = budget;
+  a.seed = seed;
+  a.step = step;
+  a.out_ids = out_ids;
+  a.out_kept = out_kept;
+  a.out_status = out_status;
+  return arcs::launch_hybrid_nucleus(a, B, (hipStream_t)stream) == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
+}
+
 int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                       const float* temperature, int n, int32_t* out_ids, float* out_logprobs,
                       int32_t* out_status, void* stream) {
@@ -211,6 +238,7 @@ const char* arcs_status_string(int code) {
     case ARCS_ERR_BAD_STRIDE: return "row_stride must be >= V";
     case ARCS_ERR_BAD_DTYPE: return "dtype must be ARCS_DTYPE_BF16 or ARCS_DTYPE_F32";
     case ARCS_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than arcs_sample_workspace_bytes()";
+    case ARCS_ERR_BAD_BUDGET: return "budget outside [0, 4096]";
     case ARCS_ERR_SCRATCH_TOO_SMALL:
       return "the shape needs more workspace than arcs_sample_noalloc's scratch (ARCS_NOALLOC_SCRATCH_BYTES)";
     case ARCS_ERR_LAUNCH: return "kernel launch failed";

@@ -74,6 +74,22 @@ inline bool split_shape(int64_t B, int64_t V, int dtype) {
 // kernel launched after it on the same stream (never a valid id or status).
 constexpr int32_t kDeferredId = INT32_MIN;
 
+// One launch of the baseline hybrid nucleus selector (arcs_sample_hybrid_nucleus).
+struct HybridArgs {
+  const void* logits;        // bf16
+  int64_t V;
+  int64_t stride;
+  const float* temperature;  // [B]
+  const float* top_p;        // [B]
+  int budget;                // ids enumerated before bisection takes over
+  uint64_t seed;
+  uint64_t step;
+  int32_t* out_ids;          // [B]
+  int32_t* out_kept;         // [B] or NULL
+  int32_t* out_status;       // [B] or NULL
+};
+hipError_t launch_hybrid_nucleus(const HybridArgs& a, int64_t B, hipStream_t stream);
+
 // One top-logprobs launch (arcs_top_logprobs).
 struct LogprobArgs {
   const void* logits;

@@ -1128,18 +1128,13 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     path |= ARCS_PATH_CUTOFF;
     float zc = zc0;
     if (mode == kModeHist) {
-      // a histogram of the threads' two largest group maxima by weight, 8
-      // bins per unit of log2 weight below the row maximum: counts (top-k)
-      // and weights (top-p, a lower bound of the mass above each bin's edge).
-      // When the bound lies beyond the last bin (a large k at a low
-      // temperature), the histogram is built again with bins 16 times wider.
-      float b1 = -__builtin_inff(), b2 = -__builtin_inff();
-#pragma unroll
-      for (int q = 0; q < kSQ; ++q) {
-        const float g = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
-        b2 = g > b1 ? b1 : (g > b2 ? g : b2);
-        b1 = g > b1 ? g : b1;
-      }
+      // a histogram of every group's maximum by weight, 8 bins per unit of
+      // log2 weight below the row maximum: counts (top-k) and weights (top-p),
+      // each a lower bound of what lies above the bin's edge (one element per
+      // group).  Groups in the last bin (far below the maximum) are left out:
+      // a bound there is no bound.  When the bound lies beyond the last bin (a
+      // large k at a low temperature), the histogram is built again with bins
+      // 16 times wider.
       float c8 = (chi + clo) * 8.0f;
       for (int attempt = 0; attempt < 3; ++attempt, c8 *= 0.0625f) {
         if (attempt > 0) {
@@ -1150,11 +1145,11 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           __syncthreads();
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float v = h == 0 ? b1 : b2;
-          if (v > -__builtin_inff()) {
-            const float x = (m - v) * c8;
-            const int bin = x < (float)(kBins - 1) ? (int)x : kBins - 1;
+        for (int q = 0; q < kSQ; ++q) {
+          const float v = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
+          const float x = (m - v) * c8;
+          if (v > -__builtin_inff() && x < (float)(kBins - 1)) {
+            const int bin = (int)x;
             atomicAdd(&sm.bcnt[bin], 1u);
             if (pon) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
           }

@@ -53,7 +53,8 @@ typedef enum arcs_status {
   ARCS_ERR_BAD_HISTORY = -9,         /* exactly one of hist_ids/hist_offsets is NULL */
   ARCS_ERR_BAD_TOP_N = -10,          /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
   ARCS_ERR_BAD_CAPACITY = -11,       /* arcs_commit_tokens: capacity 0, or capacity * B too large */
-  ARCS_ERR_SCRATCH_TOO_SMALL = -12   /* arcs_sample_noalloc: the shape needs more than its scratch */
+  ARCS_ERR_SCRATCH_TOO_SMALL = -12,  /* arcs_sample_noalloc: the shape needs more than its scratch */
+  ARCS_ERR_BAD_BUDGET = -13          /* arcs_sample_hybrid_nucleus: budget outside [0, 4096] */
 } arcs_status;
 
 /* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
@@ -235,6 +236,34 @@ int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64
 int arcs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                         const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
                         uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status, void* stream);
+
+/*
+ * arcs_sample_hybrid_nucleus: a baseline nucleus (top-p) sampler, for A/B
+ * timing against arcs_sample.  It is the selector the pages report for their
+ * device sampler (Arc PR #194, squashed commit #130, "hybrid nucleus
+ * selector"): per row, the ids of the order (value desc, id asc) are
+ * enumerated one at a time, for at most `budget` ids, until their mass
+ * reaches top_p of the row's mass, and the kept set is that prefix; past the
+ * budget, 32 halvings of the value key find the largest threshold whose mass
+ * reaches top_p, and every id at or above it is kept (ties at the boundary
+ * value all kept: the wider rule).  top_p >= 1 keeps every id.  No penalties,
+ * top-k or min-p.  The draw is arcs_sample's: the first kept id in id order
+ * whose running weight exceeds u * S_K, u the SplitMix64 uniform of counter
+ * step * 2^32 + b under seed.  fp32 weights, fp64 sums.
+ *   logits       device bf16 [B, row_stride], rows 16-byte aligned,
+ *                V % 8 == 0, V <= 131072
+ *   temperature  device float[B], > 0 and finite (else row status 1)
+ *   top_p        device float[B], > 0 (else row status 2)
+ *   budget       ids enumerated before bisection takes over, 0 .. 4096
+ *   out_ids      device int32[B]; out_kept device int32[B] (kept set size) or
+ *                NULL; out_status device int32[B] or NULL
+ * Returns ARCS_OK, ARCS_ERR_BAD_DTYPE (not bf16), ARCS_ERR_BAD_VOCAB,
+ * ARCS_ERR_MISALIGNED, ARCS_ERR_BAD_BUDGET or another negative arcs_status.
+ */
+int arcs_sample_hybrid_nucleus(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                               const float* temperature, const float* top_p, int budget, uint64_t seed,
+                               uint64_t step, int32_t* out_ids, int32_t* out_kept, int32_t* out_status,
+                               void* stream);
 
 /* Bytes of device workspace arcs_sample, arcs_sample_keyed and
  * arcs_sample_debug need for this shape: B * P * 16 for the split batches

@@ -374,6 +374,34 @@ def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optiona
     return out
 
 
+def hybrid_nucleus_row(raw_row: np.ndarray, dtype: str, T: float, top_p: float, budget: int, seed: int,
+                       row: int, step: int, band_p: float = 0.0) -> RowResult:
+    """The pages' baseline nucleus selector (Arc PR #194, squashed commit #130,
+    "hybrid nucleus selector"): enumerating the order until the mass reaches
+    top_p keeps the strict prefix, and does so when that prefix has at most
+    `budget` ids; past the budget, threshold bisection over the values keeps
+    every id at or above the crossing value, i.e. the prefix widened to its
+    ties.  No penalties, top-k or min-p; T must be finite and > 0, top_p > 0."""
+    T = float(T)
+    top_p = float(top_p)
+    if not (T > 0.0 and math.isfinite(T)):
+        return RowResult(status=ROW_BAD_TEMPERATURE, id=-1)
+    if not (top_p > 0.0):
+        return RowResult(status=ROW_BAD_TOP_P, id=-1)
+    z = widen(raw_row, dtype)
+    _, w = weights(z, T)
+    c = cutoff(z, w, -1, top_p, 0.0, band_p)
+    L = c.L
+    if top_p < 1.0 and L > budget:
+        L = widen_ties(z, c.order, L)
+    kept = np.sort(c.order[:L])
+    wk = w[kept]
+    u = uniform(seed, row, step)
+    ids, margins = draw(kept, wk, u)
+    return RowResult(status=ROW_OK, id=int(ids[0]), L=L, S=c.S, S_K=math.fsum(wk.tolist()), u=u,
+                     margin_id=float(margins[0]), margin_p=c.margin_p, near_p=c.near_p, kept=kept)
+
+
 def argmax(logits: np.ndarray, dtype: str) -> np.ndarray:
     """Row-wise argmax of the widened raw logits (no penalties)."""
     return np.array([argmax_first(widen(r, dtype)) for r in logits], dtype=np.int32)

@@ -310,6 +310,35 @@ def test_wide_ties_on_a_tied_diffuse_support():
     assert a.L == b.L
 
 
+def test_hybrid_nucleus_is_the_strict_prefix_within_budget_else_the_wide_one():
+    rng = np.random.default_rng(15)
+    for _ in range(100):
+        V = int(rng.integers(2, 12))
+        z = o.widen(rng.integers(-2, 3, V).astype(np.float32), "f32")
+        T = float(np.float32(rng.uniform(0.3, 2.0)))
+        pp = float(np.float32(rng.uniform(0.05, 0.99)))
+        strict = o.sample_row(z, "f32", _p(temperature=T, top_p=pp), None, 3, 1, 2)
+        wide = o.sample_row(z, "f32", _p(temperature=T, top_p=pp, flags=o.ROW_TIES_WIDE), None, 3, 1, 2)
+        assert o.hybrid_nucleus_row(z, "f32", T, pp, V, 3, 1, 2).L == strict.L
+        assert o.hybrid_nucleus_row(z, "f32", T, pp, strict.L, 3, 1, 2).L == strict.L
+        h0 = o.hybrid_nucleus_row(z, "f32", T, pp, strict.L - 1, 3, 1, 2)
+        assert h0.L == wide.L and set(h0.kept.tolist()) == set(wide.kept.tolist())
+        assert h0.id == wide.id
+    # the tied diffuse support: 111 within a budget of 200, 116 past a budget of 32
+    z = np.full(300, -50.0, dtype=np.float32)
+    z[:105] = np.linspace(2.0, 1.0, 105, dtype=np.float32)
+    z[105:116] = 0.5
+    zz = o.widen(z, "f32")
+    _, w = o.weights(zz, 1.0)
+    cum = np.cumsum(w[o.total_order(zz)])
+    pp = float(np.float32((cum[109] + 0.5 * w[105]) / cum[-1]))
+    assert o.hybrid_nucleus_row(z, "f32", 1.0, pp, 200, 0, 0, 0).L == 111
+    assert o.hybrid_nucleus_row(z, "f32", 1.0, pp, 32, 0, 0, 0).L == 116
+    assert o.hybrid_nucleus_row(z, "f32", 1.0, 1.0, 0, 0, 0, 0).L == 300
+    assert o.hybrid_nucleus_row(z, "f32", 0.0, 0.5, 8, 0, 0, 0).status == o.ROW_BAD_TEMPERATURE
+    assert o.hybrid_nucleus_row(z, "f32", 1.0, 0.0, 8, 0, 0, 0).status == o.ROW_BAD_TOP_P
+
+
 def test_minp_set_against_softmax_definition():
     rng = np.random.default_rng(6)
     for _ in range(200):
