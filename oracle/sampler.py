@@ -168,6 +168,75 @@ def penalize(z: np.ndarray, hist: Optional[np.ndarray], presence: float, frequen
 
 
 # --------------------------------------------------------------------------
+# step 2b: the DRY penalty
+# --------------------------------------------------------------------------
+# The pages name it (DrySamplingParams, apply_dry_penalty, a multiplier whose
+# disabled default 0.0 leaves every logit untouched: Arc PR #222, section
+# 3(a)) but do not define it; this is the published "Don't Repeat Yourself"
+# sampler: a token that would extend a repeat of the context's tail by one
+# more token is penalised, growing exponentially with the repeat's length.
+DRY_MAX_WINDOW = 2048   # history tokens matched at most (the last ones)
+
+
+def dry_validate(d) -> int:
+    mult, base = float(d["multiplier"]), float(d["base"])
+    if not (math.isfinite(mult) and mult >= 0.0 and math.isfinite(base) and base > 0.0) \
+            or int(d["allowed_length"]) < 1 or int(d["range"]) < 0:
+        return ROW_BAD_PENALTY
+    return ROW_OK
+
+
+def dry_match_lengths(seq, breakers=()) -> dict:
+    """For every token t of seq (but its first): the length n of the longest
+    tail of seq that also ends right before an occurrence of t, i.e.
+    seq[j-n:j] == seq[N-n:N] with seq[j] == t; no matched token and no t may be
+    a sequence breaker.  Returns {t: largest n} over the t with n >= 1."""
+    brk = set(int(b) for b in breakers)
+    N = len(seq)
+    best = {}
+    for j in range(1, N):
+        t = int(seq[j])
+        if t in brk:
+            continue
+        n = 0
+        while n < j and int(seq[j - 1 - n]) == int(seq[N - 1 - n]) and int(seq[j - 1 - n]) not in brk:
+            n += 1
+        if n > 0:
+            best[t] = max(best.get(t, 0), n)
+    return best
+
+
+def dry_penalize(z: np.ndarray, hist: Optional[np.ndarray], d, breakers=()) -> np.ndarray:
+    """z[t] -= multiplier * base^(n - allowed_length) for every token t in [0, V)
+    with a repeat length n >= allowed_length over the last min(range, 2048)
+    history tokens (range 0: all of them, up to 2048).  binary32 arithmetic:
+    the power by repeated multiplication, then the product, then the
+    subtraction, each rounded."""
+    z = z.copy()
+    if hist is None or d is None or float(d["multiplier"]) == 0.0:
+        return z
+    h = np.asarray(hist, dtype=np.int64)
+    win = int(d["range"]) if int(d["range"]) > 0 else len(h)
+    win = min(win, DRY_MAX_WINDOW, len(h))
+    seq = h[len(h) - win:]
+    al = int(d["allowed_length"])
+    base = np.float32(d["base"])
+    mult = np.float32(d["multiplier"])
+    V = len(z)
+    for t, n in dry_match_lengths(seq, breakers).items():
+        if n < al or not (0 <= t < V):
+            continue
+        v = np.float32(1.0)
+        for _ in range(n - al):
+            v = np.float32(v * base)
+            if not np.isfinite(v):
+                break
+        pen = np.float32(mult * v)
+        z[t] = np.float64(np.float32(np.float32(z[t]) - pen))
+    return z
+
+
+# --------------------------------------------------------------------------
 # step 3: argmax
 # --------------------------------------------------------------------------
 def argmax_first(z: np.ndarray) -> int:
@@ -321,12 +390,16 @@ def validate(p) -> int:
 
 def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], seed: int,
                row: int, step: int, u_override: Optional[float] = None,
-               want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0) -> RowResult:
+               want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0,
+               dry=None, breakers=()) -> RowResult:
     st = validate(p)
+    if st == ROW_OK and dry is not None:
+        st = dry_validate(dry)
     if st != ROW_OK:
         return RowResult(status=st, id=-1)
     z = widen(raw_row, dtype)
     z = penalize(z, hist, float(p["presence"]), float(p["frequency"]), float(p["repetition"]))
+    z = dry_penalize(z, hist, dry, breakers)
     am = argmax_first(z)
     T = float(p["temperature"])
     top_k = int(p["top_k"])
@@ -359,7 +432,8 @@ def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], s
 def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optional[np.ndarray],
            hist_offsets: Optional[np.ndarray], seed: int, step: int,
            rows: Optional[Sequence[int]] = None, uniforms: Optional[Sequence[float]] = None,
-           want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0) -> List[RowResult]:
+           want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0,
+           dry: Optional[np.ndarray] = None, breakers=()) -> List[RowResult]:
     """Oracle over a batch.  ``rows`` are the batch indices that key the RNG."""
     n = logits.shape[0]
     rows = list(range(n)) if rows is None else [int(r) for r in rows]
@@ -370,7 +444,7 @@ def sample(logits: np.ndarray, dtype: str, params: np.ndarray, hist_ids: Optiona
             hist = hist_ids[int(hist_offsets[i]): int(hist_offsets[i + 1])]
         u = None if uniforms is None else float(uniforms[i])
         out.append(sample_row(logits[i], dtype, params[i], hist, seed, rows[i], step, u, want_probs,
-                              band_p, band_m))
+                              band_p, band_m, None if dry is None else dry[i], breakers))
     return out
 
 

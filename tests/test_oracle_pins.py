@@ -507,6 +507,101 @@ def test_invalid_params_give_status_and_minus_one():
 
 
 # --------------------------------------------------------------------------
+# DRY
+# --------------------------------------------------------------------------
+def _bf_dry(seq, breakers):
+    """Brute force by substring search: for every tail length n (no breaker in
+    it), every earlier occurrence of the tail that is followed by a token t
+    (not a breaker) gives t a repeat of at least n."""
+    brk = set(breakers)
+    N = len(seq)
+    best = {}
+    for n in range(1, N):
+        tail = list(seq[N - n:])
+        if brk & set(tail):
+            break
+        for i in range(0, N - n):
+            if list(seq[i:i + n]) == tail and seq[i + n] not in brk:
+                best[seq[i + n]] = max(best.get(seq[i + n], 0), n)
+    return best
+
+
+def _dry(**kw):
+    from workloads import make_dry
+    return make_dry(1, **kw)[0]
+
+
+def test_dry_match_lengths_hand_cases():
+    assert o.dry_match_lengths([5, 6, 7, 5, 6]) == {7: 2}
+    assert o.dry_match_lengths([1, 2, 3, 4, 1, 2, 3]) == {4: 3}
+    assert o.dry_match_lengths([9, 9, 9, 9]) == {9: 3}
+    assert o.dry_match_lengths([1, 2, 3]) == {}
+    # a breaker inside the repeat stops it; a breaker as the next token is never penalised
+    assert o.dry_match_lengths([1, 0, 2, 3, 1, 0, 2], breakers=[0]) == {3: 1}
+    assert o.dry_match_lengths([4, 0, 5, 4], breakers=[0]) == {}
+
+
+def test_dry_match_lengths_bruteforce():
+    rng = np.random.default_rng(31)
+    for _ in range(400):
+        N = int(rng.integers(1, 24))
+        seq = [int(x) for x in rng.integers(0, 4, N)]
+        brk = [int(x) for x in rng.choice(4, size=int(rng.integers(0, 2)), replace=False)]
+        assert o.dry_match_lengths(seq, brk) == _bf_dry(seq, brk), (seq, brk)
+
+
+def test_dry_penalty_values_and_window():
+    z = np.zeros(10, dtype=np.float32)
+    hist = np.array([1, 2, 3, 4, 1, 2, 3])  # 4 repeats a tail of 3
+    out = o.dry_penalize(o.widen(z, "f32"), hist, _dry(multiplier=0.5, base=2.0, allowed_length=2))
+    want = np.zeros(10)
+    want[4] = -0.5 * 2.0 ** (3 - 2)
+    assert np.array_equal(out, want)
+    # allowed_length above the repeat: nothing
+    out = o.dry_penalize(o.widen(z, "f32"), hist, _dry(multiplier=0.5, base=2.0, allowed_length=4))
+    assert np.array_equal(out, np.zeros(10))
+    # range 3 keeps the last three tokens [1, 2, 3]: no repeat
+    out = o.dry_penalize(o.widen(z, "f32"), hist, _dry(multiplier=0.5, base=2.0, allowed_length=1, range=3))
+    assert np.array_equal(out, np.zeros(10))
+    # binary32 arithmetic: 1.75^3 by repeated multiplication, then the product
+    hist = np.array([7, 1, 2, 3, 4, 5, 7, 1, 2, 3, 4])  # 5 repeats a tail of 4 ([7,1,2,3,4])
+    out = o.dry_penalize(o.widen(np.full(10, 0.3, dtype=np.float32), "f32"), hist,
+                         _dry(multiplier=0.8, base=1.75, allowed_length=1))
+    v = np.float32(1.0)
+    for _ in range(5 - 1):
+        v = np.float32(v * np.float32(1.75))
+    assert out[5] == np.float32(np.float32(0.3) - np.float32(np.float32(0.8) * v))
+    assert np.count_nonzero(out != np.float32(0.3)) == 1
+
+
+def test_disabled_dry_is_a_no_op_and_enabled_dry_is_not():
+    """The pages' invariant: DRY at multiplier 0.0 leaves every logit (and so
+    the token) unchanged; at 0.8 it moves them."""
+    rng = np.random.default_rng(32)
+    V = 64
+    z = rng.normal(0, 1, V).astype(np.float32)
+    hist = np.array([3, 9, 11, 3, 9, 11, 3, 9])  # 11 repeats a tail of 5
+    z[11] = z.max() + 0.5  # 11 is the argmax without DRY
+    p = _p(temperature=0.0)
+    plain = o.sample_row(z, "f32", p, hist, 1, 0, 0)
+    off = o.sample_row(z, "f32", p, hist, 1, 0, 0, dry=_dry(multiplier=0.0))
+    on = o.sample_row(z, "f32", p, hist, 1, 0, 0, dry=_dry(multiplier=0.8))
+    assert np.array_equal(o.dry_penalize(o.widen(z, "f32"), hist, _dry(multiplier=0.0)), o.widen(z, "f32"))
+    assert off.id == plain.id == 11 and off.max_logit == plain.max_logit
+    assert on.id != 11
+
+
+def test_dry_parameter_errors():
+    z = np.zeros(4, dtype=np.float32)
+    for field, bad in (("multiplier", -0.1), ("multiplier", np.inf), ("base", 0.0), ("base", np.nan),
+                       ("allowed_length", 0), ("range", -1)):
+        d = _dry(multiplier=0.5)
+        d[field] = bad
+        r = o.sample_row(z, "f32", _p(), np.array([1, 2]), 0, 0, 0, dry=d)
+        assert r.status == o.ROW_BAD_PENALTY and r.id == -1, (field, bad)
+
+
+# --------------------------------------------------------------------------
 # anti-vacuity: planted mistakes must turn a pin red
 # --------------------------------------------------------------------------
 def _red(test_fn):
@@ -560,6 +655,16 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(o, "widen_ties", lambda z, order, L: max(L, int(np.count_nonzero(z > z[order[L - 1]]))))
         assert _red(test_wide_ties_bruteforce)
+    # DRY: a repeat counted one token too long, or breakers ignored
+    with monkeypatch.context() as m:
+        real_ml = o.dry_match_lengths
+        m.setattr(o, "dry_match_lengths", lambda seq, breakers=(): {t: n + 1 for t, n in real_ml(seq, breakers).items()})
+        assert _red(test_dry_match_lengths_hand_cases)
+        assert _red(test_dry_penalty_values_and_window)
+    with monkeypatch.context() as m:
+        real_ml = o.dry_match_lengths
+        m.setattr(o, "dry_match_lengths", lambda seq, breakers=(): real_ml(seq, ()))
+        assert _red(test_dry_match_lengths_bruteforce)
     # a draw margin of zero (every mismatch would be excused)
     with monkeypatch.context() as m:
         real = o.draw

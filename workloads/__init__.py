@@ -6,7 +6,9 @@ path can consume what it produces without sharing any method code.
 """
 
 from .gen import (  # noqa: F401
+    DRY_DTYPE,
     PARAMS_DTYPE,
+    make_dry,
     V_DEFAULT,
     Workload,
     make_params,

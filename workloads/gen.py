@@ -46,6 +46,20 @@ PARAMS_DTYPE = np.dtype(
 )
 assert PARAMS_DTYPE.itemsize == 32
 
+# Per-row DRY penalty record, 16 bytes (arcs_dry_params).
+DRY_DTYPE = np.dtype([("multiplier", "<f4"), ("base", "<f4"), ("allowed_length", "<i4"), ("range", "<i4")])
+assert DRY_DTYPE.itemsize == 16
+
+
+def make_dry(n: int, multiplier=0.0, base=1.75, allowed_length=2, range=0) -> np.ndarray:
+    """DRY records for ``n`` rows (scalars broadcast)."""
+    d = np.zeros(n, dtype=DRY_DTYPE)
+    d["multiplier"] = multiplier
+    d["base"] = base
+    d["allowed_length"] = allowed_length
+    d["range"] = range
+    return d
+
 _PURPOSE_LOGITS = 0
 _PURPOSE_PARAMS = 1
 _PURPOSE_HISTORY = 2
