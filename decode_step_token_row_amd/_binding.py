@@ -36,6 +36,9 @@ ERR_BAD_TOP_N = -10
 ERR_BAD_CAPACITY = -11
 ERR_SCRATCH_TOO_SMALL = -12
 ERR_BAD_BUDGET = -13
+ERR_BAD_DRY = -14
+DRY_MAX_WINDOW = 2048
+DRY_MAX_BREAKERS = 64
 NOALLOC_SCRATCH_BYTES = 16384
 ROW_OK = 0
 ROW_BAD_TEMPERATURE = 1
@@ -99,6 +102,9 @@ def library() -> ctypes.CDLL:
         lib.arcs_sample_debug.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_u64, c_u64,
                                           c_p, c_p, c_p, ctypes.c_size_t, c_p, c_p, c_p, c_p]
         lib.arcs_sample_debug.restype = c_i
+        lib.arcs_sample_dry.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_i, c_u64,
+                                         c_u64, c_p, c_p, c_p, c_u64, c_p]
+        lib.arcs_sample_dry.restype = c_i
         lib.arcs_sample_hybrid_nucleus.argtypes = [c_p, c_i, c_i64, c_i64, c_i64, c_p, c_p, c_i, c_u64, c_u64,
                                                     c_p, c_p, c_p, c_p]
         lib.arcs_sample_hybrid_nucleus.restype = c_i
@@ -321,6 +327,46 @@ def sample_noalloc(logits, params, hist_ids=None, hist_offsets=None, seed: int =
                                        int(step) & (2**64 - 1), _ptr(out), _ptr(out_status), _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_sample_noalloc")
+    return out
+
+
+def dry_to_device(dry, device="cuda"):
+    """A DRY_DTYPE structured numpy array (workloads.make_dry) as device bytes."""
+    torch = _torch()
+    arr = np.ascontiguousarray(dry).view(np.uint8).reshape(len(dry), 16)
+    return torch.from_numpy(arr.copy()).to(device)
+
+
+def sample_dry(logits, params, hist_ids, hist_offsets, dry, breakers=None, seed: int = 0, step: int = 0,
+               out=None, out_status=None, workspace=None, stream=None):
+    """arcs_sample_dry: arcs_sample with per-row DRY records (device bytes from
+    dry_to_device) and optional device int32 sequence breakers."""
+    torch = _torch()
+    B, V, stride = _check_logits(logits)
+    _check_params(params, B)
+    _check_hist(hist_ids, hist_offsets, B)
+    if dry is not None and (not dry.is_cuda or dry.dtype != torch.uint8 or dry.numel() != 16 * B
+                            or not dry.is_contiguous()):
+        raise ValueError("dry must be contiguous device bytes of B DRY records (dry_to_device)")
+    nb = 0
+    if breakers is not None:
+        nb = breakers.numel()
+        _check_out(breakers, torch.int32, nb, "breakers")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_out(out, torch.int32, B, "out")
+    if out_status is not None:
+        _check_out(out_status, torch.int32, B, "out_status")
+    ws_need = workspace_bytes(B, V, _dtype_code(logits))
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().arcs_sample_dry(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params), _ptr(hist_ids),
+                                   _ptr(hist_offsets), _ptr(dry), _ptr(breakers), nb, int(seed) & (2**64 - 1),
+                                   int(step) & (2**64 - 1), _ptr(out), _ptr(out_status), _ptr(workspace),
+                                   ws_bytes, _stream_ptr(stream))
+    if st != OK:
+        raise ArcsError(st, "arcs_sample_dry")
     return out
 
 

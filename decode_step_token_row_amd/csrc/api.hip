@@ -72,9 +72,13 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
                 const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
                 uint64_t seed, uint64_t step, const uint64_t* key, int32_t* out_ids, int32_t* out_status,
                 void* workspace, size_t workspace_bytes, const double* uniforms, float* out_probs,
-                arcs_row_stats* out_stats, void* stream) {
+                arcs_row_stats* out_stats, void* stream, const arcs_dry_params* dry = nullptr,
+                const int32_t* breakers = nullptr, int n_breakers = 0) {
   int st = check_common(logits, dtype, B, V, row_stride, out_ids);
   if (st != ARCS_OK) return st;
+  if (n_breakers < 0 || n_breakers > ARCS_DRY_MAX_BREAKERS || (n_breakers > 0 && breakers == nullptr))
+    return ARCS_ERR_BAD_DRY;
+  if (((uintptr_t)dry) % 4u != 0 || ((uintptr_t)breakers) % 4u != 0) return ARCS_ERR_MISALIGNED;
   if (params == nullptr) return ARCS_ERR_NULL_POINTER;
   if ((hist_ids == nullptr) != (hist_offsets == nullptr)) return ARCS_ERR_BAD_HISTORY;
   const size_t ws_need = arcs_sample_workspace_bytes(B, V, dtype);
@@ -101,6 +105,9 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   a.pen_tables = (hist_ids != nullptr && V <= ARCS_MAX_PENALTY_VOCAB) ? 1 : 0;
   a.bitmap_words = a.pen_tables ? (uint32_t)((V + 31) / 32) : 0u;
   a.deferred_only = 0;
+  a.dry = dry;
+  a.dry_breakers = breakers;
+  a.n_breakers = n_breakers;
   const bool vec = rows_16b_aligned(logits, dtype, row_stride);
   // small batches: greedy rows and rows without filters are read by many
   // workgroups per row (not with debug outputs, which read the row whole)
@@ -133,6 +140,16 @@ int arcs_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step,
                      nullptr, out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr,
                      stream);
+}
+
+int arcs_sample_dry(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                    const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                    const arcs_dry_params* dry, const int32_t* breakers, int n_breakers, uint64_t seed,
+                    uint64_t step, int32_t* out_ids, int32_t* out_status, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return sample_impl(logits, dtype, B, V, row_stride, params, hist_ids, hist_offsets, seed, step, nullptr,
+                     out_ids, out_status, workspace, workspace_bytes, nullptr, nullptr, nullptr, stream, dry,
+                     breakers, n_breakers);
 }
 
 int arcs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
@@ -239,6 +256,7 @@ const char* arcs_status_string(int code) {
     case ARCS_ERR_BAD_DTYPE: return "dtype must be ARCS_DTYPE_BF16 or ARCS_DTYPE_F32";
     case ARCS_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than arcs_sample_workspace_bytes()";
     case ARCS_ERR_BAD_BUDGET: return "budget outside [0, 4096]";
+    case ARCS_ERR_BAD_DRY: return "DRY breakers: NULL with n_breakers > 0, or n_breakers outside [0, 64]";
     case ARCS_ERR_SCRATCH_TOO_SMALL:
       return "the shape needs more workspace than arcs_sample_noalloc's scratch (ARCS_NOALLOC_SCRATCH_BYTES)";
     case ARCS_ERR_LAUNCH: return "kernel launch failed";

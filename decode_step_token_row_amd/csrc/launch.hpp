@@ -32,6 +32,9 @@ struct SampleArgs {
   int deferred_only;   // general kernel: only rows whose out_ids holds kDeferredId
   struct SplitPart* split_parts;  // split launch: [B][split_P] slice partials, or NULL
   int split_P;                    // slices per row of a split launch
+  const arcs_dry_params* dry;     // [B] DRY records, or NULL
+  const int32_t* dry_breakers;    // [n_breakers]
+  int n_breakers;
 };
 
 // Small batches of bf16 rows (B <= kSplitMaxB): greedy rows and rows without

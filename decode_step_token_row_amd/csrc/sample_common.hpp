@@ -85,6 +85,7 @@ struct PenCtx {
   const float* zpen;       // general path: penalised logit per distinct id
   const uint32_t* pcount;  // summary path: occurrence count per distinct id
   uint32_t hmask;          // summary path: bit q set when this thread's group of round q holds a history id
+  bool dry_on;             // the row's DRY record is active (its rows run on the general pipeline)
 };
 
 // Rank of a history id among the row's distinct history ids (id order).
@@ -393,6 +394,73 @@ __device__ __forceinline__ int row_param_status(const arcs_row_params& P) {
   return ARCS_ROW_OK;
 }
 
+// The row's DRY record (rows with history arrays only): ARCS_ROW_OK or
+// ARCS_ROW_BAD_PENALTY; `on` when its multiplier is not 0.
+__device__ __forceinline__ int dry_status(const SampleArgs& a, int64_t row, bool& on) {
+  on = false;
+  if (a.dry == nullptr || a.hist_ids == nullptr) return ARCS_ROW_OK;
+  const arcs_dry_params D = a.dry[row];
+  if (!(__builtin_isfinite(D.multiplier) && D.multiplier >= 0.0f && __builtin_isfinite(D.base) && D.base > 0.0f) ||
+      D.allowed_length < 1 || D.range < 0)
+    return ARCS_ROW_BAD_PENALTY;
+  on = D.multiplier != 0.0f;
+  return ARCS_ROW_OK;
+}
+
+// The DRY penalty folded into the penalised logits zpen[rank] (built
+// already).  Over the last min(range, ARCS_DRY_MAX_WINDOW) history ids, in
+// `win` (ids outside [0, V) and sequence breakers become a marker that
+// matches nothing), each position j >= 1 extends the window's tail backwards
+// from j - 1 while the ids agree: that length n is a repeat the token at j
+// would continue; per distinct id the longest (LDS atomic max into `len`,
+// kMaxDistinct entries), then zpen -= multiplier * base^(n - allowed_length)
+// for n >= allowed_length.  The power is a product of n - allowed_length
+// binary32 multiplications.  All NT threads call it; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void apply_dry(const SampleArgs& a, int64_t row, int64_t h0, int64_t h1, const Smem& sm,
+                                          uint32_t* win, uint32_t* len) {
+  constexpr uint32_t kBreak = 0xFFFFFFFFu;
+  const int tid = threadIdx.x;
+  const arcs_dry_params D = a.dry[row];
+  int64_t N = h1 - h0;
+  if (D.range > 0 && (int64_t)D.range < N) N = D.range;
+  if (N > ARCS_DRY_MAX_WINDOW) N = ARCS_DRY_MAX_WINDOW;
+  const int64_t s0 = h1 - N;
+  for (int64_t i = tid; i < N; i += NT) {
+    const int32_t id = a.hist_ids[s0 + i];
+    bool brk = id < 0 || (int64_t)id >= a.V;
+    for (int k = 0; k < a.n_breakers && !brk; ++k) brk = a.dry_breakers[k] == id;
+    win[i] = brk ? kBreak : (uint32_t)id;
+  }
+  for (int r = tid; r < kMaxDistinct; r += NT) len[r] = 0u;
+  __syncthreads();
+  for (int64_t j = 1 + tid; j < N; j += NT) {
+    const uint32_t t = win[j];
+    if (t == kBreak) continue;
+    int64_t n = 0;
+    while (n < j) {
+      const uint32_t x = win[j - 1 - n];
+      if (x == kBreak || x != win[N - 1 - n]) break;
+      ++n;
+    }
+    if (n > 0) atomicMax(&len[pen_rank(t, sm.bitmap, sm.wprefix)], (uint32_t)n);
+  }
+  __syncthreads();
+  const float base = D.base, mult = D.multiplier;
+  for (int r = tid; r < kMaxDistinct; r += NT) {
+    const uint32_t n = len[r];
+    if (n >= (uint32_t)D.allowed_length) {
+      float v = 1.0f;
+      for (uint32_t k = (uint32_t)D.allowed_length; k < n; ++k) {
+        v = v * base;
+        if (!__builtin_isfinite(v)) break;
+      }
+      sm.zpen[r] = sm.zpen[r] - mult * v;
+    }
+  }
+  __syncthreads();
+}
+
 // A row whose parameters or history failed: -1, its status, zeroed debug outputs.
 template <int NT>
 __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t row, int status) {
@@ -425,19 +493,22 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   const int64_t V = a.V;
   // ---- 0. parameters (P holds the row's record, loaded by the caller) ------
   int status = row_param_status(P);
+  bool dry_on = false;
+  if (status == ARCS_ROW_OK) status = dry_status(a, row, dry_on);
 
   pc.on = false;
+  pc.dry_on = false;
   pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
   pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
   pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   int64_t h0 = 0, h1 = 0;
   if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
-    const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on;
+    const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on || dry_on;
     h0 = a.hist_offsets[row];
     h1 = a.hist_offsets[row + 1];
     if (active && h1 > h0) {
       if (!PEN) status = ARCS_ROW_VOCAB_TOO_LARGE;
-      else pc.on = true;
+      else { pc.on = true; pc.dry_on = dry_on; }
     }
   }
 
@@ -481,6 +552,11 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
         }
       }
       __syncthreads();
+      // the general pipeline's union area is free until pass A: the window
+      // (2048 ids) and the per-id repeat lengths (4096) fit it
+      static_assert((size_t)kMaxBins * 4 >= (size_t)ARCS_DRY_MAX_WINDOW * 4 &&
+                    (size_t)kMaxBins * 8 >= (size_t)kMaxDistinct * 4, "DRY scratch in the union area");
+      if (pc.dry_on) apply_dry<NT>(a, row, h0, h1, sm, sm.hcnt, (uint32_t*)sm.hmass);
     } else {
       status = ARCS_ROW_HISTORY_TOO_LONG;
       pc.on = false;

@@ -958,8 +958,10 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   bool lazy = !PEN && pon && kon;
 
   if (!rc.ok) return false;
-  // rows under the wide tie rule run on the general pipeline
+  // rows under the wide tie rule, and rows with an active DRY penalty, run on
+  // the general pipeline
   if ((P.flags & ARCS_ROW_TIES_WIDE) && (kon || pon)) return false;
+  if (PEN && pc.dry_on) return false;
   const float chi = rc.chi, clo = rc.clo;
   const double tdl = rc.tdl, u = rc.u;
 
@@ -1334,17 +1336,21 @@ __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row
     h0 = a.hist_offsets[row];
     h1 = a.hist_offsets[row + 1];
   }
-  const int status = row_param_status(P);
+  int status = row_param_status(P);
+  bool dry_on = false;
+  if (status == ARCS_ROW_OK) status = dry_status(a, row, dry_on);
   pc.on = false;
+  pc.dry_on = false;
   pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
   pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
   pc.zpen = nullptr; pc.pcount = nullptr;
   hs.h0 = 0; hs.h1 = 0;
   if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
-    const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on;
+    const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on || dry_on;
     hs.h0 = h0;
     hs.h1 = h1;
     pc.on = active && hs.h1 > hs.h0;
+    pc.dry_on = dry_on && pc.on;
   }
   // branch-free: buffer loads past a resource's size return 0 without a
   // memory access (rows without active penalties get an empty resource; ids
@@ -1619,6 +1625,14 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
           sm.zpen[rk] = penalize(canon_nan(raw), sm.pcount[rk], pc);
         });
         __syncthreads();
+        if (pc.dry_on) {
+          // the window and the repeat lengths after the penalised logits, in
+          // the candidate area (free on this path)
+          uint32_t* win = (uint32_t*)(sm.zpen + kMaxDistinct);
+          static_assert((size_t)kCandCap * 12 >= (size_t)kMaxDistinct * 8 + (size_t)ARCS_DRY_MAX_WINDOW * 4,
+                        "DRY scratch in the candidate area");
+          apply_dry<kSNT>(a, row, hs.h0, hs.h1, sm, win, win + ARCS_DRY_MAX_WINDOW);
+        }
       }
       generic_row<kSNT, true, true>(a, row, P, pc, path, sm, sh);
     }

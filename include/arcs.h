@@ -54,7 +54,8 @@ typedef enum arcs_status {
   ARCS_ERR_BAD_TOP_N = -10,          /* arcs_top_logprobs: n outside [1, ARCS_MAX_TOP_LOGPROBS] */
   ARCS_ERR_BAD_CAPACITY = -11,       /* arcs_commit_tokens: capacity 0, or capacity * B too large */
   ARCS_ERR_SCRATCH_TOO_SMALL = -12,  /* arcs_sample_noalloc: the shape needs more than its scratch */
-  ARCS_ERR_BAD_BUDGET = -13          /* arcs_sample_hybrid_nucleus: budget outside [0, 4096] */
+  ARCS_ERR_BAD_BUDGET = -13,         /* arcs_sample_hybrid_nucleus: budget outside [0, 4096] */
+  ARCS_ERR_BAD_DRY = -14             /* arcs_sample_dry: breakers NULL or n_breakers outside [0, 64] */
 } arcs_status;
 
 /* Per-row status codes written to out_status[b] (out_ids[b] = -1 when != 0). */
@@ -120,6 +121,34 @@ typedef struct arcs_row_params {
   float repetition;
   int32_t flags;
 } arcs_row_params;
+
+/*
+ * Per-row DRY ("don't repeat yourself") penalty, 16 bytes, device array of B
+ * records (arcs_sample_dry).  The pages name the penalty and fix one fact:
+ * at its disabled default, multiplier 0.0, it touches no logit (Arc PR #222,
+ * section 3(a)), so such rows keep the fast path.  Otherwise, over the last
+ * min(range, ARCS_DRY_MAX_WINDOW) history ids (range 0: all, up to the
+ * window), a token t gets n = the length of the longest tail of that window
+ * which also ends right before an earlier occurrence of t (no sequence
+ * breaker, and no id outside [0, V), inside the match or as t), and when
+ * n >= allowed_length its logit loses multiplier * base^(n - allowed_length),
+ * after the presence / frequency / repetition penalties (binary32: the power
+ * by repeated multiplication, the product, the subtraction).
+ *   multiplier      >= 0, finite (0: off)
+ *   base            > 0, finite
+ *   allowed_length  >= 1
+ *   range           >= 0 (0: the whole window)
+ * Invalid records give the row ARCS_ROW_BAD_PENALTY.  DRY needs the row's
+ * history: rows without history arrays ignore the record.
+ */
+typedef struct arcs_dry_params {
+  float multiplier;
+  float base;
+  int32_t allowed_length;
+  int32_t range;
+} arcs_dry_params;
+#define ARCS_DRY_MAX_WINDOW 2048
+#define ARCS_DRY_MAX_BREAKERS 64
 
 /* Per-row diagnostics written by arcs_sample_debug only. */
 typedef struct arcs_row_stats {
@@ -236,6 +265,22 @@ int arcs_sample_keyed(const void* logits, int dtype, int64_t B, int64_t V, int64
 int arcs_sample_noalloc(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
                         const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
                         uint64_t seed, uint64_t step, int32_t* out_ids, int32_t* out_status, void* stream);
+
+/*
+ * arcs_sample_dry: arcs_sample with a DRY penalty record per row (see
+ * arcs_dry_params) and the call's sequence breakers.
+ *   dry          device arcs_dry_params[B], or NULL (= arcs_sample)
+ *   breakers     device int32 ids that break repeats, n_breakers of them
+ *                (0 .. ARCS_DRY_MAX_BREAKERS; NULL when 0)
+ * Rows whose DRY record is active (multiplier != 0, with history) run on the
+ * general pipeline.  Other arguments, outputs and errors as arcs_sample, plus
+ * ARCS_ERR_BAD_DRY.
+ */
+int arcs_sample_dry(const void* logits, int dtype, int64_t B, int64_t V, int64_t row_stride,
+                    const arcs_row_params* params, const int32_t* hist_ids, const int64_t* hist_offsets,
+                    const arcs_dry_params* dry, const int32_t* breakers, int n_breakers, uint64_t seed,
+                    uint64_t step, int32_t* out_ids, int32_t* out_status, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * arcs_sample_hybrid_nucleus: a baseline nucleus (top-p) sampler, for A/B

@@ -19,7 +19,8 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
                  "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs",
-                 "arcs_commit_tokens", "arcs_sample_noalloc", "arcs_sample_hybrid_nucleus"):
+                 "arcs_commit_tokens", "arcs_sample_noalloc", "arcs_sample_hybrid_nucleus",
+                 "arcs_sample_dry"):
         assert name in fns
 
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol(arcs):
 
 
 def test_status_strings_and_version(arcs):
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12, -13, 1, 2, 3, 4, 5, 6, 7]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12, -13, -14, 1, 2, 3, 4, 5, 6, 7]:
         assert arcs.status_string(code) != "unknown status", code
     assert arcs.status_string(12345) == "unknown status"
     assert arcs.version() >= 100
@@ -90,6 +91,13 @@ def test_host_validation_rejects_before_launch(arcs):
     assert N(p, 0, 4, 10, 9, p, None, None, 0, 0, p, None, None) == -4
     assert N(p, 0, 4, 10, 10, None, None, None, 0, 0, p, None, None) == -1
     assert N(p, 0, 4, 10, 10, p, p, None, 0, 0, p, None, None) == -9
+    # DRY: breakers bounded and present when counted, records aligned
+    D = lib.arcs_sample_dry
+    assert D(p, 0, 4, 10, 10, p, None, None, p, None, 1, 0, 0, p, None, None, 0, None) == -14
+    assert D(p, 0, 4, 10, 10, p, None, None, p, p, 65, 0, 0, p, None, None, 0, None) == -14
+    assert D(p, 0, 4, 10, 10, p, None, None, p, p, -1, 0, 0, p, None, None, 0, None) == -14
+    assert D(p, 0, 4, 10, 10, p, None, None, ctypes.c_void_p(base + 2), None, 0, 0, 0, p, None, None, 0, None) == -8
+    assert D(None, 0, 4, 10, 10, p, None, None, p, None, 0, 0, 0, p, None, None, 0, None) == -1
     # the baseline hybrid nucleus sampler: bf16 only, V % 8 == 0 and <= 131072,
     # aligned rows, both parameter arrays, a budget in [0, 4096]
     H = lib.arcs_sample_hybrid_nucleus

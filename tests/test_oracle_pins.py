@@ -572,6 +572,15 @@ def test_dry_penalty_values_and_window():
         v = np.float32(v * np.float32(1.75))
     assert out[5] == np.float32(np.float32(0.3) - np.float32(np.float32(0.8) * v))
     assert np.count_nonzero(out != np.float32(0.3)) == 1
+    # ids outside [0, V) break repeats: [1, 2, -5, 1, 2] -> no repeat of 2 through -5
+    hist = np.array([1, 2, -5, 1, 2])
+    out = o.dry_penalize(o.widen(np.zeros(10, dtype=np.float32), "f32"), hist,
+                         _dry(multiplier=0.5, base=2.0, allowed_length=1))
+    assert np.array_equal(out, np.zeros(10))
+    hist = np.array([1, 2, 6, 1, 2])
+    out = o.dry_penalize(o.widen(np.zeros(10, dtype=np.float32), "f32"), hist,
+                         _dry(multiplier=0.5, base=2.0, allowed_length=1))
+    assert out[6] == -1.0 and np.count_nonzero(out) == 1
 
 
 def test_disabled_dry_is_a_no_op_and_enabled_dry_is_not():
