@@ -209,9 +209,10 @@ def dry_match_lengths(seq, breakers=()) -> dict:
 def dry_penalize(z: np.ndarray, hist: Optional[np.ndarray], d, breakers=()) -> np.ndarray:
     """z[t] -= multiplier * base^(n - allowed_length) for every token t in [0, V)
     with a repeat length n >= allowed_length over the last min(range, 2048)
-    history tokens (range 0: all of them, up to 2048).  binary32 arithmetic:
-    the power by repeated multiplication, then the product, then the
-    subtraction, each rounded."""
+    history tokens (range 0: all of them, up to 2048).  History ids outside
+    [0, V) are not tokens of the vocabulary and break repeats like the
+    sequence breakers.  binary32 arithmetic: the power by repeated
+    multiplication, then the product, then the subtraction, each rounded."""
     z = z.copy()
     if hist is None or d is None or float(d["multiplier"]) == 0.0:
         return z
@@ -223,7 +224,8 @@ def dry_penalize(z: np.ndarray, hist: Optional[np.ndarray], d, breakers=()) -> n
     base = np.float32(d["base"])
     mult = np.float32(d["multiplier"])
     V = len(z)
-    for t, n in dry_match_lengths(seq, breakers).items():
+    brk = set(int(b) for b in breakers) | {int(t) for t in seq if not (0 <= int(t) < len(z))}
+    for t, n in dry_match_lengths(seq, brk).items():
         if n < al or not (0 <= t < V):
             continue
         v = np.float32(1.0)
@@ -393,7 +395,7 @@ def sample_row(raw_row: np.ndarray, dtype: str, p, hist: Optional[np.ndarray], s
                want_probs: bool = False, band_p: float = 0.0, band_m: float = 0.0,
                dry=None, breakers=()) -> RowResult:
     st = validate(p)
-    if st == ROW_OK and dry is not None:
+    if st == ROW_OK and dry is not None and hist is not None:
         st = dry_validate(dry)
     if st != ROW_OK:
         return RowResult(status=st, id=-1)
