@@ -1097,6 +1097,11 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     S = __builtin_ldexp(S, (int)negks);  // into the row frame 2^-K* of the other modes
     S_K = S;
     id = (int64_t)sh.u64[10];
+  } else if (PEN && mode == kModeMinpStream) {
+    // penalised rows with min-p alone over more than 4,096 candidates: the
+    // general pipeline (this loop's registers on top of the penalised row's
+    // spilled loaded values, each spill waiting for every load in flight)
+    return false;
   } else if (mode == kModeMinpStream) {
     // ---- min-p alone over many groups: masked sums and the id-order draw ------------
     path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
@@ -1367,15 +1372,18 @@ __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row
 }
 
 // Visits the row's history ids in [0, V), with their raw logits (read from
-// memory) when WITH_RAW: those held in registers, then any beyond them.
-template <bool WITH_RAW, class Fn>
+// memory) when WITH_RAW: those held in registers, then any beyond them (or,
+// FROM_MEMORY, all of them read again).
+template <bool WITH_RAW, bool FROM_MEMORY = false, class Fn>
 __device__ __forceinline__ void for_each_hist_id(const SampleArgs& a, int64_t row, const RowHist& hs, Fn&& f) {
   const uint16_t* rowp = (const uint16_t*)((const char*)a.logits + row * a.stride * 2);
+  if (!FROM_MEMORY) {
 #pragma unroll
-  for (int k = 0; k < kHistRegs; ++k)
-    if (k * kSNT + (int)threadIdx.x < hs.nreg && hs.id[k] >= 0 && (int64_t)hs.id[k] < a.V)
-      f((uint32_t)hs.id[k], WITH_RAW ? bf16_to_f32(rowp[hs.id[k]]) : 0.0f);
-  for (int64_t i = hs.h0 + (int64_t)kHistRegs * kSNT + threadIdx.x; i < hs.h1; i += kSNT) {
+    for (int k = 0; k < kHistRegs; ++k)
+      if (k * kSNT + (int)threadIdx.x < hs.nreg && hs.id[k] >= 0 && (int64_t)hs.id[k] < a.V)
+        f((uint32_t)hs.id[k], WITH_RAW ? bf16_to_f32(rowp[hs.id[k]]) : 0.0f);
+  }
+  for (int64_t i = hs.h0 + (FROM_MEMORY ? 0 : (int64_t)kHistRegs * kSNT) + threadIdx.x; i < hs.h1; i += kSNT) {
     const int32_t id = a.hist_ids[i];
     if (id >= 0 && (int64_t)id < a.V) f((uint32_t)id, WITH_RAW ? bf16_to_f32(rowp[id]) : 0.0f);
   }
@@ -1620,7 +1628,9 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
         // the general pipeline reads penalised logits per distinct id: built
         // here from the counts and the raw logits (every occurrence of an id
         // writes the same value)
-        for_each_hist_id<true>(a, row, hs, [&](uint32_t id, float raw) {
+        RowHist hm = hs;
+        hm.nreg = 0;  // the ids again from memory: keeping the registers that long spilled the row
+        for_each_hist_id<true, true>(a, row, hm, [&](uint32_t id, float raw) {
           const uint32_t rk = pen_rank(id, sm.bitmap, sm.wprefix);
           sm.zpen[rk] = penalize(canon_nan(raw), sm.pcount[rk], pc);
         });
