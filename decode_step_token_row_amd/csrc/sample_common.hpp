@@ -486,7 +486,10 @@ __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t r
 // each bitmap word (a block scan of popcounts), and per distinct id its count
 // and its penalised logit, computed once here from the raw logit.  Looking
 // up an element is then one popcount and one LDS read.
-template <int NT, bool BF16, bool PEN>
+// NOHIST: a launch without history arrays (the caller guarantees
+// a.hist_ids == NULL, and with it no DRY record is read): nothing here reads
+// device memory, so no wait here can drain row loads already in flight.
+template <int NT, bool BF16, bool PEN, bool NOHIST = false>
 __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, const Smem& sm, Shared& sh,
                                              arcs_row_params& P, PenCtx& pc, uint32_t& path) {
   const int tid = threadIdx.x;
@@ -494,7 +497,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   // ---- 0. parameters (P holds the row's record, loaded by the caller) ------
   int status = row_param_status(P);
   bool dry_on = false;
-  if (status == ARCS_ROW_OK) status = dry_status(a, row, dry_on);
+  if (!NOHIST && status == ARCS_ROW_OK) status = dry_status(a, row, dry_on);
 
   pc.on = false;
   pc.dry_on = false;
@@ -502,7 +505,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
   pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
   pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   int64_t h0 = 0, h1 = 0;
-  if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
+  if (!NOHIST && status == ARCS_ROW_OK && a.hist_ids != nullptr) {
     const bool active = P.presence != 0.0f || P.frequency != 0.0f || pc.rep_on || dry_on;
     h0 = a.hist_offsets[row];
     h1 = a.hist_offsets[row + 1];

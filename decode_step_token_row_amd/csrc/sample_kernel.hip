@@ -304,6 +304,37 @@ __device__ __forceinline__ RowRng load_row_rng(const SampleArgs& a, int64_t row)
   return r;
 }
 
+// The same values through two unconditional vector loads (a missing array
+// reads zeros through an empty buffer resource), issued before the row's
+// loads: with no branch around them, a wait for them counts only the loads
+// issued before them and never drains the row's loads.
+struct RngLoads {
+  u32x4 key;
+  u32x4 ovr;
+};
+__device__ __forceinline__ RngLoads issue_rng_loads(const SampleArgs& a, int64_t row) {
+  RngLoads l;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.key, (short)0, a.key ? 16 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.uniforms ? a.uniforms + row : nullptr), (short)0, a.uniforms ? 8 : 0, 0x00020000);
+  l.key = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 0, 0, 0));
+  l.ovr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, 0, 0, 0));
+  return l;
+}
+__device__ __forceinline__ RowRng rng_from(const SampleArgs& a, const RngLoads& l) {
+  auto u64_of = [](uint32_t lo, uint32_t hi) {
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)lo) |
+           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)hi) << 32);
+  };
+  RowRng r;
+  r.override_on = a.uniforms != nullptr;
+  r.u_override = r.override_on ? __builtin_bit_cast(double, u64_of(l.ovr.x, l.ovr.y)) : 0.0;
+  r.seed = a.key ? u64_of(l.key.x, l.key.y) : a.seed;
+  r.step = a.key ? u64_of(l.key.z, l.key.w) : a.step;
+  return r;
+}
+
 // The row's constants for the summary path: the temperature coefficient
 // c = log2(e) / T = chi + clo (chi rounded down, clo > 0), T ln(min_p) and the
 // uniform.  ok = false for temperatures so extreme that z * c leaves the

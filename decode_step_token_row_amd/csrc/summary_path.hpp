@@ -37,14 +37,43 @@ __device__ __forceinline__ void issue_row_loads(const u32x4* rv, int ngroups, u3
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The 16 bytes of round bq of this thread's groups, by a static scan of the
-// registers (branch-free: a few selects per round, no loop over rounds).
-__device__ __forceinline__ u32x4 select_round(const u32x4 (&d)[kSQ], int bq) {
+// The 16 bytes of round qs when qs is the same in every lane of the wave: a
+// scalar branch to one copy instead of a select over every round (each case
+// opaque, so that the switch is not folded into an indexed read, which would
+// move the row's registers to scratch memory).
+__device__ __forceinline__ u32x4 uniform_round(const u32x4 (&d)[kSQ], int qs) {
+  const int q = __builtin_amdgcn_readfirstlane(qs);
   u32x4 v = d[0];
-#pragma unroll
-  for (int q = 1; q < kSQ; ++q) {
-    v.x = q == bq ? d[q].x : v.x; v.y = q == bq ? d[q].y : v.y;
-    v.z = q == bq ? d[q].z : v.z; v.w = q == bq ? d[q].w : v.w;
+  switch (q) {
+#define ARCS_UROUND_(i)                                       \
+  case i:                                                     \
+    v = d[i < kSQ ? i : 0];                                   \
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); \
+    break;
+    ARCS_UROUND_(1) ARCS_UROUND_(2) ARCS_UROUND_(3) ARCS_UROUND_(4) ARCS_UROUND_(5) ARCS_UROUND_(6)
+    ARCS_UROUND_(7) ARCS_UROUND_(8) ARCS_UROUND_(9) ARCS_UROUND_(10) ARCS_UROUND_(11) ARCS_UROUND_(12)
+    ARCS_UROUND_(13) ARCS_UROUND_(14) ARCS_UROUND_(15) ARCS_UROUND_(16) ARCS_UROUND_(17) ARCS_UROUND_(18)
+    ARCS_UROUND_(19) ARCS_UROUND_(20) ARCS_UROUND_(21) ARCS_UROUND_(22) ARCS_UROUND_(23) ARCS_UROUND_(24)
+    ARCS_UROUND_(25) ARCS_UROUND_(26) ARCS_UROUND_(27) ARCS_UROUND_(28) ARCS_UROUND_(29) ARCS_UROUND_(30)
+    ARCS_UROUND_(31)
+#undef ARCS_UROUND_
+    default: break;
+  }
+  return v;
+}
+
+// The 16 bytes of round bq (lanes with `want`; the others get zeros): one
+// uniform fetch per distinct round among those lanes, so a wave where few
+// lanes want a group pays for few copies.
+__device__ __forceinline__ u32x4 rounds_of(const u32x4 (&d)[kSQ], int bq, bool want) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  for (uint64_t pend = __ballot(want); pend;) {
+    const int qs = __builtin_amdgcn_readlane(bq, __builtin_ctzll(pend));
+    const u32x4 vq = uniform_round(d, qs);
+    const bool take = want && bq == qs;
+    v.x = take ? vq.x : v.x; v.y = take ? vq.y : v.y;
+    v.z = take ? vq.z : v.z; v.w = take ? vq.w : v.w;
+    pend &= ~__ballot(take);
   }
   return v;
 }
@@ -189,7 +218,7 @@ __device__ __forceinline__ bool nofilter_draw(const SampleArgs& a, int64_t row, 
   if (wid == ws) {
     const bool valid = tid < ngroups - qs * kSNT;
     float z[8];
-    unpack8(select_round(d, qs), z);
+    unpack8(uniform_round(d, qs), z);
     if (PEN && pc.on && valid) penalize8(z, (int64_t)(qs * kSNT + tid) * 8, pc);
     double w8[8];
     const double g = group_weights_f64(z, valid, c, w8);
@@ -792,7 +821,7 @@ __device__ __forceinline__ uint32_t first_index_of(const u32x4 (&d)[kSQ], int bq
   const int tid = threadIdx.x;
   uint32_t idx = 0xFFFFFFFFu;
   if (!__ballot(look)) return idx;
-  const u32x4 v = select_round(d, bq < 0 ? 0 : bq);
+  const u32x4 v = rounds_of(d, bq, look);
   if (look) {
     float z[8];
     load_z8<PEN>(v, bq * kSNT + tid, pc, z);
@@ -821,7 +850,7 @@ __device__ __forceinline__ void gather_candidates(const u32x4 (&d)[kSQ], const f
   const bool has = best >= bound;
   if (!__ballot(has)) return;
   // the best group, and a mask of the other rounds at or above the bound
-  const u32x4 v = select_round(d, bq < 0 ? 0 : bq);
+  const u32x4 v = rounds_of(d, bq, has);
   uint32_t extra = 0;
 #pragma unroll
   for (int q = 0; q < kSQ; ++q) {
@@ -843,7 +872,7 @@ __device__ __forceinline__ void gather_candidates(const u32x4 (&d)[kSQ], const f
   if (few) {
     for (uint32_t m = wex; m; m &= m - 1u) {
       const int qs = __builtin_ctz(m);
-      const u32x4 v2 = select_round(d, qs);
+      const u32x4 v2 = uniform_round(d, qs);
       if ((extra >> qs) & 1u) {
         float z[8];
         load_z8<PEN>(v2, qs * kSNT + tid, pc, z);
@@ -887,7 +916,7 @@ __device__ __forceinline__ void gather_candidates(const u32x4 (&d)[kSQ], const f
   if (few) {
     for (uint32_t m = wex; m; m &= m - 1u) {
       const int qs = __builtin_ctz(m);
-      const u32x4 v2 = select_round(d, qs);
+      const u32x4 v2 = uniform_round(d, qs);
       if ((extra >> qs) & 1u) {
         const int j = qs * kSNT + tid;
         float z[8];
@@ -1011,7 +1040,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     float negks = 0.0f, zt = -__builtin_inff(), zc0 = -FLT_MAX;
     double S = 0.0, Pm = 0.0;
     uint32_t argmax = 0u;
-    if (__ballot(rin && sh.w_flags[lane] != 0u)) {
+    if (__builtin_expect(__ballot(rin && sh.w_flags[lane] != 0u) != 0, 0)) {
       mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
     } else if (greedy) {
       mode = kModeGreedy;
@@ -1052,7 +1081,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   double S = sh.r_S;  // a lower bound of the row's mass while `lazy`
   double Pm = sh.r_Pm;
   int32_t mode = sh.r_mode;
-  if (mode == kModeFallback) return false;
+  if (__builtin_expect(mode == kModeFallback, 0)) return false;
 
   if (mode == kModeGreedy) {
     path |= ARCS_PATH_GREEDY;
@@ -1081,7 +1110,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     nc = sh.i32[3];
     // more than the list holds (min-p rows only): masked sums for min-p alone,
     // else a histogram bound above the threshold
-    if (nc > kCandCap) mode = (!kon && !pon) ? kModeMinpStream : kModeHist;
+    if (__builtin_expect(nc > kCandCap, 0)) mode = (!kon && !pon) ? kModeMinpStream : kModeHist;
   }
 
   int64_t id = -1;
@@ -1102,7 +1131,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     // general pipeline (this loop's registers on top of the penalised row's
     // spilled loaded values, each spill waiting for every load in flight)
     return false;
-  } else if (mode == kModeMinpStream) {
+  } else if (__builtin_expect(mode == kModeMinpStream, 0)) {
     // ---- min-p alone over many groups: masked sums and the id-order draw ------------
     path |= ARCS_PATH_CUTOFF | ARCS_PATH_MINP_FLOOR;
     {
@@ -1206,8 +1235,8 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     }
     const bool minp_complete = mon && !(zc > zt);
     if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
-    if (nc > kCandCap || nc <= 0) return false;
-    if (nc <= kSmallSort) {
+    if (__builtin_expect(nc > kCandCap || nc <= 0, 0)) return false;
+    if (__builtin_expect(nc <= kSmallSort, 1)) {
       for (;;) {
         if (wid == 0) {
           const double cap = lazy ? (double)P.top_p * S * (1.0 - 1e-5) : 0.0;
@@ -1221,7 +1250,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
         Pm = (double)P.top_p * S;
         lazy = false;
       }
-      if (sh.i32[6] < 0) return false;
+      if (__builtin_expect(sh.i32[6] < 0, 0)) return false;
       if (!debug) return true;
       id = (int64_t)sh.u64[10];
       L = (int64_t)sh.u64[11];
@@ -1583,6 +1612,7 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
     // waits for a load, and the record returns first
     u32x4 p0, p1;
     issue_params_load(a.params + row, p0, p1);
+    const RngLoads rl = issue_rng_loads(a, row);
     if (a.split_parts != nullptr) {
       // split launch: greedy rows and rows without filters finish from the
       // slice partials (this waits for the parameter record first)
@@ -1598,10 +1628,12 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
     }
     issue_row_loads(rv, ngroups, d);
     arcs_row_params P = params_from(p0, p1);
-    const RowRng rng = load_row_rng(a, row);
-    if (!row_prologue<kSNT, true, false>(a, row, sm, sh, P, pc, path)) return;
+    const RowRng rng = rng_from(a, rl);
+    // this kernel runs only in launches without history arrays (those take
+    // the penalised kernel)
+    if (!row_prologue<kSNT, true, false, true>(a, row, sm, sh, P, pc, path)) return;
     const RowConsts rc = row_consts(P, rng, row);  // while the loads are in flight
-    if (!stream_row<false>(a, row, P, rc, pc, path, sm, sh, d)) {
+    if (__builtin_expect(!stream_row<false>(a, row, P, rc, pc, path, sm, sh, d), 0)) {
       __syncthreads();
       generic_row<kSNT, true, true>(a, row, P, pc, path, sm, sh);
     }
