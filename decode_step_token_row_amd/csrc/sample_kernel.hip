@@ -280,6 +280,7 @@ __device__ __forceinline__ uint64_t to_fix50(float w) { return (uint64_t)((doubl
 struct PassOut {
   float best;         // the thread's largest value (-inf: none)
   int bq;             // the first round whose group holds it (-1: none)
+  float second;       // filter rows: the largest maximum of the thread's other groups
   double lsum;        // top-p rows: the thread's weight total in its frame 2^-kfr
   float kfr, negk;    // the frame exponent (-inf before the first finite group) and -kfr
   bool bad, special;  // a frame out of range; a signalling NaN

@@ -273,57 +273,65 @@ __device__ __forceinline__ int small_cut_draw(const SampleArgs& a, int64_t row, 
   const uint64_t key = in ? sm.ckey[lane] : ~0ull;
   const float w = in ? sm.cw[lane] : 0.0f;
   const uint32_t myid = (uint32_t)key;
-  uint32_t r = 0, nm = 0;
-  double before = 0.0, tot = 0.0;
-  for (int j0 = 0; j0 < nc; j0 += 8) {
-    uint64_t kj[8];
-    float wj[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e < nc ? j0 + e : nc - 1;
-      kj[e] = sm.ckey[j];
-      wj[e] = sm.cw[j];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (j0 + e < nc) {
-        r += kj[e] < key ? 1u : 0u;
-        before += (uint32_t)kj[e] < myid ? (double)wj[e] : 0.0;
-        tot += (double)wj[e];
-        nm += key_value(~(uint32_t)(kj[e] >> 32)) >= zt ? 1u : 0u;
-      }
-    }
-  }
-  const int64_t Lk = (kon && (int64_t)top_k <= nc) ? (int64_t)top_k : INF;
-  if (minp_complete && (int)nm == nc && Lk >= nc) {
-    // every entry is kept unless top-p cuts inside the min-p set
-    bool fast;
-    if (lazy_cap > 0.0) {
-      if (!(tot < lazy_cap)) return 2;
-      fast = true;
-    } else {
-      fast = !pon || tot < Pm;
-    }
+  const int64_t Lk0 = (kon && (int64_t)top_k <= nc) ? (int64_t)top_k : INF;
+  if (minp_complete && Lk0 >= nc && __builtin_popcountll(__ballot(in && key_value(~(uint32_t)(key >> 32)) >= zt)) == nc) {
+    // every entry is kept unless top-p cuts inside the min-p set: the total
+    // by a wave sum, and only the id-order masses by a pass over the list
+    const double tot = dpp_wave_sum_f64(in ? (double)w : 0.0);
+    const bool fast = lazy_cap > 0.0 ? tot < lazy_cap : (!pon || tot < Pm);
+    if (lazy_cap > 0.0 && !fast) return 2;
     if (fast) {
+      // (four partial sums: the weights of a min-p set lie within a factor
+      // 1 / min_p of each other, so for min_p above about 1e-7 every sum of
+      // up to 64 of them is exact in double precision and the order does not
+      // matter; below that the order moves a sum by a double's rounding, far
+      // under the binary32 weights' own error)
+      double b4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int j0 = 0; j0 < nc; j0 += 8) {
+        uint32_t ij[8];
+        float wj[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e < nc ? j0 + e : nc - 1;
+          ij[e] = ((const uint32_t*)sm.ckey)[2 * j];  // the id half of the key
+          wj[e] = sm.cw[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (j0 + e < nc) b4[e & 3] += ij[e] < myid ? (double)wj[e] : 0.0;
+      }
+      const double before = (b4[0] + b4[1]) + (b4[2] + b4[3]);
       const double t = u * tot;
       const bool hit = in && w > 0.0f && before + (double)w > t;
       uint32_t pid = dpp_wave_min_u32(hit ? myid : 0xFFFFFFFFu);
       if (pid == 0xFFFFFFFFu) pid = ~dpp_wave_min_u32(in && w > 0.0f ? ~myid : 0xFFFFFFFFu);  // rounding: the last id with weight
-      const uint64_t lastb = __ballot(in && r == (uint32_t)(nc - 1));
-      const int ll = lastb ? __builtin_ctzll(lastb) : 0;
-      const uint64_t ck = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), ll) << 32) |
-                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, ll);
+      if (lane == 0) {
+        a.out_ids[row] = (int32_t)pid;
+        if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+      }
+      // the debug outputs' values: the largest key is the kept set's last entry
+      const uint32_t khi = ~dpp_wave_min_u32(in ? ~(uint32_t)(key >> 32) : 0xFFFFFFFFu);
+      const uint32_t klo = ~dpp_wave_min_u32(in && (uint32_t)(key >> 32) == khi ? ~(uint32_t)key : 0xFFFFFFFFu);
       if (lane == 0) {
         sh.u64[10] = pid;
         sh.u64[11] = (uint64_t)nc;
         sh.f64[kSNW + 1] = tot;
-        sh.u64[12] = ck;
-        a.out_ids[row] = (int32_t)pid;
-        if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
+        sh.u64[12] = ((uint64_t)khi << 32) | klo;
       }
       return 1;
     }
   }
+  // the rank of each entry among the keys
+  uint32_t r = 0;
+  for (int j0 = 0; j0 < nc; j0 += 8) {
+    uint64_t kj[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kj[e] = sm.ckey[j0 + e < nc ? j0 + e : nc - 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j0 + e < nc) r += kj[e] < key ? 1u : 0u;
+  }
+  const int64_t Lk = Lk0;
   // the entries in key order, the value-order prefix masses
   wave_lds_sync();
   if (in) { sm.skey[r] = key; sm.sw[r] = w; }
@@ -758,9 +766,10 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
                                          float chi, float clo, PassOut& o, float (&gm)[kSQ]) {
   const int tid = threadIdx.x;
   const double c64 = (double)chi + (double)clo;
-  float best = -__builtin_inff();
+  float best = -__builtin_inff(), second = -__builtin_inff();
   int bq = -1;
   double lsum = 0.0;
+  float lsf = 0.0f;  // W == 1: the sum in binary32 (a lower bound; its rounding is far inside the 1e-5 margin of its use)
   float kfr = -__builtin_inff(), negk = 0.0f;
   bool bad = false, special = false;
 #pragma unroll
@@ -784,6 +793,7 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
       if (PEN) sm.tsum[q * kSNT + tid] = g;
       else gm[q] = g;
       bq = g > best ? q : bq;
+      second = max2f(second, g > best ? best : g);
     }
     best = max2f(best, g);
     if (W == 0) continue;
@@ -801,15 +811,21 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
       const float nk = __builtin_floorf(x);
       if (kfr > -__builtin_inff()) {
         const int sh_ = (int)(kfr - nk);
-        lsum = __builtin_ldexp(lsum, sh_);
+        if (W == 1) lsf = __builtin_ldexpf(lsf, sh_);
+        else lsum = __builtin_ldexp(lsum, sh_);
       }
       kfr = nk;
       negk = -nk;
     }
-    const float s = W == 1 ? wexp(g, chi, clo, negk) : group_weight(z, chi, clo, negk);
-    lsum += valid ? (double)s : 0.0;
+    if (W == 1) {
+      lsf += wexp(g, chi, clo, negk);  // g is -inf (weight 0) past the row's end
+    } else {
+      const float s = group_weight(z, chi, clo, negk);
+      lsum += valid ? (double)s : 0.0;
+    }
   }
-  o.best = best; o.bq = bq; o.lsum = lsum; o.kfr = kfr; o.negk = negk; o.bad = bad; o.special = special;
+  if (W == 1) lsum = (double)lsf;
+  o.best = best; o.bq = bq; o.second = second; o.lsum = lsum; o.kfr = kfr; o.negk = negk; o.bad = bad; o.special = special;
 }
 
 // The lowest index of the maximum wm in the thread's group bq (the first of
@@ -843,19 +859,22 @@ __device__ __forceinline__ uint32_t first_index_of(const u32x4 (&d)[kSQ], int bq
 // count sh.i32[3] place them.  A count above kCandCap means the list is
 // incomplete.  Waves with no group at or above the bound return at once.
 template <bool PEN, bool WEIGHTS = true>
-__device__ __forceinline__ void gather_candidates(const u32x4 (&d)[kSQ], const float (&gm)[kSQ], float best, int bq,
+__device__ __forceinline__ void gather_candidates(const u32x4 (&d)[kSQ], const float (&gm)[kSQ], float best, float second, int bq,
                                                   const PenCtx& pc, const Smem& sm, Shared& sh, float bound,
                                                   float chi, float clo, float negks) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const bool has = best >= bound;
   if (!__ballot(has)) return;
   // the best group, and a mask of the other rounds at or above the bound
+  // (looked for only in waves where some thread's second group reaches it)
   const u32x4 v = rounds_of(d, bq, has);
   uint32_t extra = 0;
+  if (__ballot(second >= bound)) {
 #pragma unroll
-  for (int q = 0; q < kSQ; ++q) {
-    const float g = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
-    extra |= (q != bq && g >= bound) ? (1u << q) : 0u;
+    for (int q = 0; q < kSQ; ++q) {
+      const float g = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
+      extra |= (q != bq && g >= bound) ? (1u << q) : 0u;
+    }
   }
   float zb[8];
   load_z8<PEN>(v, bq * kSNT + tid, pc, zb);
@@ -1031,61 +1050,59 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   }
   __syncthreads();
 
-  // ---- wave 0: the row's values and the mode (lane w reads record w) ----------------
-  if (wid == 0) {
-    const bool rin = lane < kSNW;
-    const float rm = rin ? sh.w_max[lane] : -__builtin_inff();
-    const float m = dpp_wave_max_f32(rm);
-    int32_t mode = kModeFallback;
-    float negks = 0.0f, zt = -__builtin_inff(), zc0 = -FLT_MAX;
-    double S = 0.0, Pm = 0.0;
-    uint32_t argmax = 0u;
-    if (__builtin_expect(__ballot(rin && sh.w_flags[lane] != 0u) != 0, 0)) {
-      mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
-    } else if (greedy) {
-      mode = kModeGreedy;
-      argmax = m > -__builtin_inff() ? dpp_wave_min_u32(rin && rm == m ? sh.w_arg[lane] : 0xFFFFFFFFu) : 0u;
-    } else if (m > -__builtin_inff() && m < __builtin_inff() && m * chi > -1048576.0f && m * chi < 1048576.0f) {
-      // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
-      negks = -__builtin_floorf(m * chi);
-      if (nofilter) {
-        const double mc = (double)m * ((double)chi + (double)clo);
-        mode = mc > -kF64Span && mc < kF64Span ? kModeNoFilter : kModeFallback;
-      } else {
-        bool ok = true;
-        if (pon) {
-          const double x = rin ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
-          S = dpp_wave_sum_f64(x);
-          ok = S > 0.0 && S < 1e300;
-          Pm = (double)P.top_p * S;
-        }
-        if (mon) {
-          bool found;
-          zt = minp_threshold(m, tdl, found);
-          ok = ok && found;
-          zc0 = zt > -FLT_MAX ? zt : -FLT_MAX;
-        }
-        // min-p rows gather at the exact threshold; small rows take every
-        // element; the others first bound the cut with a histogram
-        if (!ok) mode = kModeFallback;
-        else mode = (mon || ngroups <= kCandCap / 8) ? kModeCand : kModeHist;
+  // ---- the row's values and the mode, in every wave (lane w reads record w) ---------
+  // (the same records and the same wave operations give the same values in
+  // every wave, so no second barrier broadcasts them)
+  const bool rin = lane < kSNW;
+  const float rm = rin ? sh.w_max[lane] : -__builtin_inff();
+  static_assert(kSNW <= 8, "one record per lane of the first half-row");
+  const float m0 = dpp_octet_max_f32(rm);
+  int32_t mode = kModeFallback;
+  float negks = 0.0f, zt = -__builtin_inff(), zc0 = -FLT_MAX;
+  double S = 0.0;  // a lower bound of the row's mass while `lazy`
+  double Pm = 0.0;
+  uint32_t argmax = 0u;
+  if (__builtin_expect(__ballot(rin && sh.w_flags[lane] != 0u) != 0, 0)) {
+    mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
+  } else if (greedy) {
+    mode = kModeGreedy;
+    argmax = m0 > -__builtin_inff() ? dpp_octet_min_u32(rin && rm == m0 ? sh.w_arg[lane] : 0xFFFFFFFFu) : 0u;
+  } else if (m0 > -__builtin_inff() && m0 < __builtin_inff() && m0 * chi > -1048576.0f && m0 * chi < 1048576.0f) {
+    // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
+    negks = -__builtin_floorf(m0 * chi);
+    if (nofilter) {
+      const double mc = (double)m0 * ((double)chi + (double)clo);
+      mode = mc > -kF64Span && mc < kF64Span ? kModeNoFilter : kModeFallback;
+    } else {
+      bool ok = true;
+      if (pon) {
+        const double x = rin ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
+        S = dpp_octet_sum_f64(x);
+        ok = S > 0.0 && S < 1e300;
+        Pm = (double)P.top_p * S;
       }
-    }
-    if (lane == 0) {
-      sh.r_m = m; sh.r_negks = negks; sh.r_zt = zt; sh.r_zc = zc0;
-      sh.r_S = S; sh.r_Pm = Pm; sh.r_mode = mode; sh.r_arg = argmax;
+      if (mon) {
+        bool found;
+        zt = minp_threshold(m0, tdl, found);
+        ok = ok && found;
+        zc0 = zt > -FLT_MAX ? zt : -FLT_MAX;
+      }
+      // min-p rows gather at the exact threshold; small rows take every
+      // element; the others first bound the cut with a histogram
+      if (!ok) mode = kModeFallback;
+      else mode = (mon || ngroups <= kCandCap / 8) ? kModeCand : kModeHist;
     }
   }
-  __syncthreads();
-  const float m = sh.r_m, negks = sh.r_negks, zt = sh.r_zt, zc0 = sh.r_zc;
-  double S = sh.r_S;  // a lower bound of the row's mass while `lazy`
-  double Pm = sh.r_Pm;
-  int32_t mode = sh.r_mode;
+  // wave-uniform: scalar registers, leaving the vector ones to the row
+  mode = __builtin_amdgcn_readfirstlane(mode);
+  argmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)argmax);
+  const float m = uniform_f32(m0);
+  negks = uniform_f32(negks); zt = uniform_f32(zt); zc0 = uniform_f32(zc0);
+  S = uniform_f64(S); Pm = uniform_f64(Pm);
   if (__builtin_expect(mode == kModeFallback, 0)) return false;
 
   if (mode == kModeGreedy) {
     path |= ARCS_PATH_GREEDY;
-    const uint32_t argmax = sh.r_arg;
     if (tid == 0) {
       a.out_ids[row] = (int32_t)argmax;
       if (a.out_status) a.out_status[row] = ARCS_ROW_OK;
@@ -1105,7 +1122,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // ---- the candidates z >= zc0 from the registers (min-p rows, small rows) ----------
   int nc = -1;
   if (mode == kModeCand) {
-    gather_candidates<PEN>(d, gm, best, bq, pc, sm, sh, zc0, chi, clo, negks);
+    gather_candidates<PEN>(d, gm, best, po.second, bq, pc, sm, sh, zc0, chi, clo, negks);
     __syncthreads();
     nc = sh.i32[3];
     // more than the list holds (min-p rows only): masked sums for min-p alone,
@@ -1170,7 +1187,12 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       // group).  Groups in the last bin (far below the maximum) are left out:
       // a bound there is no bound.  When the bound lies beyond the last bin (a
       // large k at a low temperature), the histogram is built again with bins
-      // 16 times wider.
+      // 16 times wider.  Rows that need only a count, for a k of at most half
+      // the thread count, histogram the thread maxima alone (also one element
+      // each): the k-th largest of them lies close to the k-th largest
+      // element, and one update per thread replaces one per group.
+      const bool hmass = pon && !lazy;
+      const bool thr = !hmass && kon && P.top_k <= kSNT / 2;
       float c8 = (chi + clo) * 8.0f;
       for (int attempt = 0; attempt < 3; ++attempt, c8 *= 0.0625f) {
         if (attempt > 0) {
@@ -1180,14 +1202,20 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           }
           __syncthreads();
         }
+        if (thr) {
+          const float x = (m - best) * c8;
+          if (best > -__builtin_inff() && x < (float)(kBins - 1)) atomicAdd(&sm.bcnt[(int)x], 1u);
+        } else {
 #pragma unroll
-        for (int q = 0; q < kSQ; ++q) {
-          const float v = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
-          const float x = (m - v) * c8;
-          if (v > -__builtin_inff() && x < (float)(kBins - 1)) {
-            const int bin = (int)x;
-            atomicAdd(&sm.bcnt[bin], 1u);
-            if (pon) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
+          for (int q = 0; q < kSQ; ++q) {
+            float v = PEN ? sm.tsum[q * kSNT + tid] : gm[q];
+            asm volatile("" : "+v"(v));  // round by round: no weights computed ahead and held
+            const float x = (m - v) * c8;
+            if (v > -__builtin_inff() && x < (float)(kBins - 1)) {
+              const int bin = (int)x;
+              atomicAdd(&sm.bcnt[bin], 1u);
+              if (hmass) atomicAdd(&sm.bmass[bin], wexp(v, chi, clo, negks));
+            }
           }
         }
         __syncthreads();
@@ -1202,7 +1230,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
           const uint32_t cex = dpp_wave_incl_scan_u32(ctot) - ctot;
           const double mex = dpp_wave_incl_scan_f64(mtot) - mtot;
           const uint32_t k_need = kon ? (uint32_t)P.top_k : 0xFFFFFFFFu;
-          const double p_need = (pon && !lazy) ? Pm * (1.0 + 1e-4) : __builtin_inf();
+          const double p_need = hmass ? Pm * (1.0 + 1e-4) : __builtin_inf();
           int fb = 4;
           uint32_t cc = cex;
           double mc = mex;
@@ -1229,7 +1257,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       zc = sh.r_zc;
       if (!(zc > -__builtin_inff())) return false;
       // ---- gather the candidates z >= zc -------------------------------------------
-      gather_candidates<PEN>(d, gm, best, bq, pc, sm, sh, zc, chi, clo, negks);
+      gather_candidates<PEN>(d, gm, best, po.second, bq, pc, sm, sh, zc, chi, clo, negks);
       __syncthreads();
       nc = sh.i32[3];
     }
