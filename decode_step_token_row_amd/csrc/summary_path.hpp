@@ -751,16 +751,43 @@ __device__ __forceinline__ double exact_row_mass(const u32x4 (&dd)[kSQ], const P
 // The pass over a row whose loads are in flight, one instantiation per kind
 // of row so that the unrolled loop carries no per-group branches on the
 // row's parameters:
-//   W = 0  group maxima only (greedy, min-p and top-k rows);
-//   W = 1  plus the weight of each group's maximum (top-p with top-k: a lower
-//          bound of the row's mass);
-//   W = 2  plus every element's weight (top-p rows without top-k, and rows
-//          without filters).
+//   W = 0  group maxima only (greedy, min-p and top-k rows, and top-p with
+//          top-k, whose mass is bounded from the group maxima afterwards);
+//   W = 2  plus every element's weight (top-p rows without top-k).
 // Filter rows keep each group's maximum (-inf for groups past the row's end)
 // in registers, gm[q], or with penalties (whose arithmetic needs the
 // registers) in LDS at sm.tsum[q * kSNT + tid].  NOFILTER rows (W == 3)
 // weigh every element in double precision instead and leave each wave's
 // total of each round in LDS (as doubles at sm.tsum, [q * kSNW + wave]).
+// A lower bound of the row's mass (frame 2^-K*) from every group's maximum,
+// for rows whose top-p test the two largest group maxima per thread did not
+// settle: the maxima again from the registers (keeping them from the pass
+// would hold 32 more registers through the whole tail), binary32 sums of 32
+// terms per thread (rounding far inside the 1e-5 margin of the test).
+__device__ __forceinline__ double group_max_mass(const u32x4 (&dd)[kSQ], int ngroups, float chi, float clo,
+                                                 float negks, Shared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kSQ; ++q) {
+    int lim = ngroups - q * kSNT;
+    asm volatile("" : "+s"(lim));
+    u32x4 dq = dd[q];
+    asm volatile("" : "+v"(dq));  // weighed here, not ahead in the caller
+    float z[8];
+    unpack8(dq, z);
+    const float g = group_max(z);
+    s += tid < lim && g == g ? wexp(g, chi, clo, negks) : 0.0f;
+  }
+  const double ws = dpp_wave_sum_f64((double)s);
+  __syncthreads();
+  if (lane == 0) sh.rtot[wid] = ws;
+  __syncthreads();
+  double S = 0.0;
+  for (int w = 0; w < kSNW; ++w) S += sh.rtot[w];
+  return S;
+}
+
 template <bool PEN, int W, bool NOFILTER>
 __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, const PenCtx& pc, const Smem& sm,
                                          float chi, float clo, PassOut& o, float (&gm)[kSQ]) {
@@ -769,7 +796,6 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
   float best = -__builtin_inff(), second = -__builtin_inff();
   int bq = -1;
   double lsum = 0.0;
-  float lsf = 0.0f;  // W == 1: the sum in binary32 (a lower bound; its rounding is far inside the 1e-5 margin of its use)
   float kfr = -__builtin_inff(), negk = 0.0f;
   bool bad = false, special = false;
 #pragma unroll
@@ -811,20 +837,14 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
       const float nk = __builtin_floorf(x);
       if (kfr > -__builtin_inff()) {
         const int sh_ = (int)(kfr - nk);
-        if (W == 1) lsf = __builtin_ldexpf(lsf, sh_);
-        else lsum = __builtin_ldexp(lsum, sh_);
+        lsum = __builtin_ldexp(lsum, sh_);
       }
       kfr = nk;
       negk = -nk;
     }
-    if (W == 1) {
-      lsf += wexp(g, chi, clo, negk);  // g is -inf (weight 0) past the row's end
-    } else {
-      const float s = group_weight(z, chi, clo, negk);
-      lsum += valid ? (double)s : 0.0;
-    }
+    const float s = group_weight(z, chi, clo, negk);
+    lsum += valid ? (double)s : 0.0;
   }
-  if (W == 1) lsum = (double)lsf;
   o.best = best; o.bq = bq; o.second = second; o.lsum = lsum; o.kfr = kfr; o.negk = negk; o.bad = bad; o.special = special;
 }
 
@@ -994,16 +1014,19 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   const bool kon = !greedy && P.top_k >= 1 && (int64_t)P.top_k < V;
   const bool pon = !greedy && P.top_p < 1.0f;
   const bool mon = !greedy && P.min_p > 0.0f;
-  const bool weights = pon;  // fp32 weights needed during the pass
-  // top-p with top-k: the pass weighs only each group's maximum, which bounds
-  // the row's mass from below; a top-k prefix whose mass stays under top_p
-  // times that bound is not cut by top-p, and only when it is not is the
-  // exact mass computed (a second read of the row).  A prefix of at most k
-  // tokens rarely reaches top_p of the mass; a min-p set without top-k holds
-  // most of it on exactly the peaked rows where top-p cuts, so those rows
-  // weigh every element in the pass.  The penalised kernel always weighs every
-  // element: there the second-read code measured slower than what it saves.
-  bool lazy = !PEN && pon && kon;
+  const bool weights = pon;  // a mass in the wave records (from every weight in the pass, unless lazy)
+  // top-p with top-k and min-p: the pass weighs nothing; the weights of each
+  // thread's two largest group maxima bound the row's mass from below, and a
+  // kept prefix whose mass stays under top_p times that bound is not cut by
+  // top-p.  Only when it is not are all group maxima weighed (a tighter
+  // bound), and then the exact mass computed (a second pass over the
+  // registers).  A prefix cut by both top-k and min-p rarely reaches top_p of
+  // the mass; the top-k prefix alone often does (top-p then cuts inside it),
+  // and a min-p set without top-k holds most of the mass on exactly the
+  // peaked rows where top-p cuts, so those rows weigh every element in the
+  // pass.  The penalised kernel always weighs every element: there the
+  // second-pass code measured slower than what it saves.
+  bool lazy = !PEN && pon && kon && mon;
 
   if (!rc.ok) return false;
   // rows under the wide tie rule, and rows with an active DRY penalty, run on
@@ -1018,8 +1041,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   PassOut po;
   float gm[kSQ];  // filter rows: the maximum of each of the thread's groups
   if (nofilter) row_pass<PEN, 3, true>(d, ngroups, pc, sm, chi, clo, po, gm);
-  else if (lazy) row_pass<PEN, 1, false>(d, ngroups, pc, sm, chi, clo, po, gm);
-  else if (weights) row_pass<PEN, 2, false>(d, ngroups, pc, sm, chi, clo, po, gm);
+  else if (weights && !lazy) row_pass<PEN, 2, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   else row_pass<PEN, 0, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   const float best = po.best;
   const int bq = po.bq;
@@ -1031,7 +1053,13 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   {
     const float wm = dpp_wave_max_f32(best);
     const float kw = wm > -__builtin_inff() && weights ? __builtin_floorf(wm * chi) : 0.0f;  // K_w >= K_t
-    if (weights) lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
+    if (lazy) {
+      // the weights of each thread's two largest group maxima, in the wave's
+      // frame: a lower bound of the row's mass
+      lsum = (double)wexp(best, chi, clo, -kw) + (double)wexp(po.second, chi, clo, -kw);
+    } else if (weights) {
+      lsum = __builtin_ldexp(lsum, kfr > -__builtin_inff() ? (int)(kfr - kw) : 0);
+    }
     const double ws = pon ? dpp_wave_sum_f64(lsum) : 0.0;
     uint32_t warg = 0xFFFFFFFFu;
     if (greedy) warg = dpp_wave_min_u32(first_index_of<PEN>(d, bq, wm, best == wm && wm > -__builtin_inff(), pc));
@@ -1187,12 +1215,13 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       // group).  Groups in the last bin (far below the maximum) are left out:
       // a bound there is no bound.  When the bound lies beyond the last bin (a
       // large k at a low temperature), the histogram is built again with bins
-      // 16 times wider.  Rows that need only a count, for a k of at most half
-      // the thread count, histogram the thread maxima alone (also one element
-      // each): the k-th largest of them lies close to the k-th largest
-      // element, and one update per thread replaces one per group.
-      const bool hmass = pon && !lazy;
-      const bool thr = !hmass && kon && P.top_k <= kSNT / 2;
+      // 16 times wider.  Rows with a k of at most half the thread count
+      // histogram the thread maxima alone, counts only (also one element
+      // each; the kept set lies within the top k, so the count bound is enough
+      // whatever top-p does): the k-th largest of them lies close to the k-th
+      // largest element, and one update per thread replaces one per group.
+      const bool thr = kon && P.top_k <= kSNT / 2;
+      const bool hmass = pon && !lazy && !thr;
       float c8 = (chi + clo) * 8.0f;
       for (int attempt = 0; attempt < 3; ++attempt, c8 *= 0.0625f) {
         if (attempt > 0) {
@@ -1265,6 +1294,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     if (minp_complete) path |= ARCS_PATH_MINP_FLOOR;
     if (__builtin_expect(nc > kCandCap || nc <= 0, 0)) return false;
     if (__builtin_expect(nc <= kSmallSort, 1)) {
+      bool wider_bound = false;
       for (;;) {
         if (wid == 0) {
           const double cap = lazy ? (double)P.top_p * S * (1.0 - 1e-5) : 0.0;
@@ -1273,7 +1303,13 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
         }
         __syncthreads();
         if (!lazy || sh.i32[6] != 1) break;
-        // top-p may cut inside the prefix: the exact mass, then the cut again
+        // top-p may cut inside the prefix: a tighter bound (every group's
+        // maximum), then the exact mass, each followed by the cut again
+        if (!wider_bound) {
+          wider_bound = true;
+          S = group_max_mass(d, ngroups, chi, clo, negks, sh);
+          continue;
+        }
         S = exact_row_mass<PEN>(d, pc, ngroups, chi, clo, negks, sh);
         Pm = (double)P.top_p * S;
         lazy = false;
@@ -1295,12 +1331,17 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
                             pon))
         return false;
       if (lazy && !(kept_mass < (double)P.top_p * S * (1.0 - 1e-5))) {
-        // top-p may cut inside the prefix: the exact mass, then the cut again
-        S = exact_row_mass<PEN>(d, pc, ngroups, chi, clo, negks, sh);
-        Pm = (double)P.top_p * S;
-        lazy = false;
-        if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, true, Pm, minp_complete, zt, cut, L, kept_mass, true))
-          return false;
+        // top-p may cut inside the prefix: a tighter bound (every group's
+        // maximum), then the exact mass and the cut again
+        S = group_max_mass(d, ngroups, chi, clo, negks, sh);
+        if (!(kept_mass < (double)P.top_p * S * (1.0 - 1e-5))) {
+          S = exact_row_mass<PEN>(d, pc, ngroups, chi, clo, negks, sh);
+          Pm = (double)P.top_p * S;
+          lazy = false;
+          if (!large_cut_select(sm, sh, nc, lowbit, kon, P.top_k, true, Pm, minp_complete, zt, cut, L, kept_mass,
+                                true))
+            return false;
+        }
       }
       const double ux = u * 0x1p64;  // the uniform as a 64-bit fraction
       const uint64_t uf = ux >= 0x1p64 ? ~0ull : (ux <= 0.0 ? 0ull : (uint64_t)ux);

@@ -529,6 +529,32 @@ def test_top_p_with_other_filters_binding_or_not(arcs):
     assert np.array_equal(got, ids)
 
 
+def test_top_k_top_p_min_p_mass_bounds(arcs):
+    """Rows with top-k, top-p and min-p and no history settle top-p from a
+    lower bound of the mass: the two largest group maxima per thread, then
+    every group maximum, then the exact mass.  The parameter sets are chosen
+    (on these zipf rows) so that each of the three settles some rows, on small
+    (<= 64) and larger candidate sets."""
+    B = 32
+    w = make_workload("zipf_b256_bf16_t0.7_k50_p0.9_minp0.05", B=B)
+    p = make_params(B, temperature=0.7)
+    cfg = [(0.7, 50, 0.9, 0.05), (1.0, 60, 0.6, 0.01), (0.7, 50, 0.85, 0.01), (0.7, 200, 0.8, 0.005)]
+    for b in range(B):
+        T, k, tp, mp = cfg[b % 4]
+        p[b]["temperature"], p[b]["top_k"], p[b]["top_p"], p[b]["min_p"] = T, k, tp, mp
+    w.params = p
+    ids, _, stats, _ = _run_debug(arcs, w)
+    refs = _oracle(w)
+    _compare_rows(ids, stats, refs, "mass bounds")
+    for b, r in enumerate(refs):
+        assert abs(stats[b]["mass_total"] - r.S) <= 1e-5 * r.S, (b, stats[b]["mass_total"], r.S)
+    logits = to_device_logits(w.logits, w.dtype)
+    for step in (0, 3):
+        got = arcs.sample(logits, arcs.params_to_device(w.params), seed=w.seed, step=step).cpu().numpy()
+        w.step = step
+        _compare_rows(got, None, _oracle(w), f"mass bounds step {step}")
+
+
 def test_minp_rows_with_crowded_threads(arcs):
     """min-p rows whose large values crowd a few 16-byte groups 8,192 tokens
     apart (one thread's share of the row on the single-pass kernel): several
