@@ -120,6 +120,8 @@ def library() -> ctypes.CDLL:
         lib.arcs_commit_tokens.restype = c_i
         lib.arcs_sample_workspace_bytes.argtypes = [c_i64, c_i64, c_i]
         lib.arcs_sample_workspace_bytes.restype = ctypes.c_size_t
+        lib.arcs_long_history_workspace_bytes.argtypes = [c_i64, c_i64]
+        lib.arcs_long_history_workspace_bytes.restype = ctypes.c_size_t
         lib.arcs_status_string.argtypes = [c_i]
         lib.arcs_status_string.restype = ctypes.c_char_p
         lib.arcs_version.argtypes = []
@@ -138,6 +140,10 @@ def version() -> int:
 
 def workspace_bytes(B: int, V: int, dtype: int) -> int:
     return int(library().arcs_sample_workspace_bytes(int(B), int(V), int(dtype)))
+
+
+def long_history_workspace_bytes(B: int, V: int) -> int:
+    return int(library().arcs_long_history_workspace_bytes(int(B), int(V)))
 
 
 # --------------------------------------------------------------------------
@@ -434,7 +440,7 @@ def sample_keyed(logits, params, key, hist_ids=None, hist_offsets=None, advance:
 
 
 def sample_debug(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0, step: int = 0,
-                 uniforms=None, want_probs: bool = False, stream=None):
+                 uniforms=None, want_probs: bool = False, workspace=None, stream=None):
     """arcs_sample_debug: returns (ids, status, stats[B] numpy structured, probs or None)."""
     torch = _torch()
     B, V, stride = _check_logits(logits)
@@ -448,11 +454,16 @@ def sample_debug(logits, params, hist_ids=None, hist_offsets=None, seed: int = 0
     if uniforms is not None:
         _check_out(uniforms, torch.float64, B, "uniforms")
     ws_need = workspace_bytes(B, V, _dtype_code(logits))
-    workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev) if ws_need else None
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        ws_bytes = ws_need
     st = library().arcs_sample_debug(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(params),
                                      _ptr(hist_ids), _ptr(hist_offsets), int(seed) & (2**64 - 1),
                                      int(step) & (2**64 - 1), _ptr(out), _ptr(status), _ptr(workspace),
-                                     ws_need, _ptr(uniforms), _ptr(probs), _ptr(stats), _stream_ptr(stream))
+                                     ws_bytes, _ptr(uniforms), _ptr(probs), _ptr(stats), _stream_ptr(stream))
     if st != OK:
         raise ArcsError(st, "arcs_sample_debug")
     torch.cuda.synchronize(dev)

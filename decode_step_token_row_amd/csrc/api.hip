@@ -108,6 +108,13 @@ int sample_impl(const void* logits, int dtype, int64_t B, int64_t V, int64_t row
   a.dry = dry;
   a.dry_breakers = breakers;
   a.n_breakers = n_breakers;
+  // penalised launches: a workspace of arcs_long_history_workspace_bytes()
+  // takes the rows whose penalties the LDS tables cannot hold
+  const size_t long_need = arcs_long_history_workspace_bytes(B, V);
+  a.long_ws = (hist_ids != nullptr && workspace != nullptr && workspace_bytes >= long_need &&
+               ((uintptr_t)workspace & 15u) == 0)
+                  ? (float*)workspace
+                  : nullptr;
   const bool vec = rows_16b_aligned(logits, dtype, row_stride);
   // small batches: greedy rows and rows without filters are read by many
   // workgroups per row (not with debug outputs, which read the row whole)
@@ -239,6 +246,12 @@ int arcs_top_logprobs(const void* logits, int dtype, int64_t B, int64_t V, int64
   hipError_t e = arcs::launch_top_logprobs(a, dtype, B, rows_16b_aligned(logits, dtype, row_stride),
                                            (hipStream_t)stream);
   return e == hipSuccess ? ARCS_OK : ARCS_ERR_LAUNCH;
+}
+
+size_t arcs_long_history_workspace_bytes(int64_t B, int64_t V) {
+  if (B <= 0 || V <= 0) return 0;
+  const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)V * 4u;
+  return n > (unsigned __int128)SIZE_MAX ? SIZE_MAX : (size_t)n;
 }
 
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype) {

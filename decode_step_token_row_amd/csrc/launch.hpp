@@ -33,6 +33,8 @@ struct SampleArgs {
   struct SplitPart* split_parts;  // split launch: [B][split_P] slice partials, or NULL
   int split_P;                    // slices per row of a split launch
   const arcs_dry_params* dry;     // [B] DRY records, or NULL
+  float* long_ws;                 // [B][V] binary32: penalised copies of rows whose penalties the LDS
+                                  // tables cannot hold (caller workspace), or NULL
   const int32_t* dry_breakers;    // [n_breakers]
   int n_breakers;
 };

@@ -461,6 +461,12 @@ __device__ __forceinline__ void apply_dry(const SampleArgs& a, int64_t row, int6
   __syncthreads();
 }
 
+// A row whose active penalties the LDS tables cannot hold (more distinct
+// history ids than kMaxDistinct, or V above the penalty vocabulary) in a
+// launch with a long-history workspace: handed to the workspace path (its
+// out_ids entry marked, nothing else written), never stored as a status.
+constexpr int kStatusDeferLong = -100;
+
 // A row whose parameters or history failed: -1, its status, zeroed debug outputs.
 template <int NT>
 __device__ __forceinline__ void write_row_failure(const SampleArgs& a, int64_t row, int status) {
@@ -510,7 +516,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
     h0 = a.hist_offsets[row];
     h1 = a.hist_offsets[row + 1];
     if (active && h1 > h0) {
-      if (!PEN) status = ARCS_ROW_VOCAB_TOO_LARGE;
+      if (!PEN) status = a.long_ws != nullptr ? kStatusDeferLong : ARCS_ROW_VOCAB_TOO_LARGE;
       else { pc.on = true; pc.dry_on = dry_on; }
     }
   }
@@ -561,11 +567,15 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
                     (size_t)kMaxBins * 8 >= (size_t)kMaxDistinct * 4, "DRY scratch in the union area");
       if (pc.dry_on) apply_dry<NT>(a, row, h0, h1, sm, sm.hcnt, (uint32_t*)sm.hmass);
     } else {
-      status = ARCS_ROW_HISTORY_TOO_LONG;
+      status = a.long_ws != nullptr ? kStatusDeferLong : ARCS_ROW_HISTORY_TOO_LONG;
       pc.on = false;
     }
   }
 
+  if (status == kStatusDeferLong) {
+    if (tid == 0) a.out_ids[row] = kDeferredId;
+    return false;
+  }
   if (status != ARCS_ROW_OK) {
     write_row_failure<NT>(a, row, status);
     return false;

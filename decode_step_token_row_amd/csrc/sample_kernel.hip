@@ -1353,7 +1353,127 @@ hipError_t launch_one(Kern kernel, bool summary, int threads, const SampleArgs& 
   return hipGetLastError();
 }
 
+// Rows the sampling kernel handed over (out_ids marked) in a launch with a
+// long-history workspace: their penalties in binary32 in the row's slice of
+// the workspace, for the general kernel to sample with no penalties.  The
+// slice first counts each id's occurrences in the history (atomics in device
+// memory), then every element becomes its penalised value (the same binary32
+// sequence as the tables' path) or keeps its raw value; an active DRY record
+// then lowers the ids its repeat lengths reach, the lengths gathered per id
+// in an LDS hash of the window's ids (at most ARCS_DRY_MAX_WINDOW of them, in
+// twice as many slots).  Other rows exit at once.
+constexpr int kLongNT = 512;
+constexpr int kDryHashSlots = 2 * ARCS_DRY_MAX_WINDOW;
+static_assert((kDryHashSlots & (kDryHashSlots - 1)) == 0, "hash slots: a power of two");
+template <bool BF16>
+__global__ __launch_bounds__(kLongNT) void long_history_prep_kernel(SampleArgs a) {
+  __shared__ uint32_t win[ARCS_DRY_MAX_WINDOW];
+  __shared__ uint32_t hkey[kDryHashSlots];
+  __shared__ uint32_t hlen[kDryHashSlots];
+  constexpr uint32_t kEmpty = 0xFFFFFFFFu, kBreak = 0xFFFFFFFFu;
+  const int64_t row = blockIdx.x;
+  if (a.out_ids[row] != kDeferredId) return;
+  const int tid = threadIdx.x;
+  const int64_t V = a.V;
+  uint32_t* cnt = (uint32_t*)(a.long_ws + row * V);
+  float* zc = a.long_ws + row * V;
+  const arcs_row_params P = a.params[row];
+  PenCtx pc;
+  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
+  pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  const int64_t h0 = a.hist_offsets[row], h1 = a.hist_offsets[row + 1];
+  for (int64_t i = tid; i < V; i += kLongNT) cnt[i] = 0u;
+  __syncthreads();
+  for (int64_t i = h0 + tid; i < h1; i += kLongNT) {
+    const int32_t id = a.hist_ids[i];
+    if (id >= 0 && (int64_t)id < V) atomicAdd(&cnt[id], 1u);
+  }
+  __syncthreads();
+  const char* rowp = (const char*)a.logits + row * a.stride * (BF16 ? 2 : 4);
+  for (int64_t i = tid; i < V; i += kLongNT) {
+    const uint32_t c = cnt[i];
+    const float raw = BF16 ? bf16_to_f32(((const uint16_t*)rowp)[i]) : ((const float*)rowp)[i];
+    zc[i] = c != 0u ? penalize(canon_nan(raw), c, pc) : raw;
+  }
+  bool dry_on = false;
+  (void)dry_status(a, row, dry_on);  // (the record was validated by the sampling kernel)
+  if (!dry_on) return;
+  const arcs_dry_params D = a.dry[row];
+  int64_t N = h1 - h0;
+  if (D.range > 0 && (int64_t)D.range < N) N = D.range;
+  if (N > ARCS_DRY_MAX_WINDOW) N = ARCS_DRY_MAX_WINDOW;
+  const int64_t s0 = h1 - N;
+  for (int64_t i = tid; i < N; i += kLongNT) {
+    const int32_t id = a.hist_ids[s0 + i];
+    bool brk = id < 0 || (int64_t)id >= V;
+    for (int k = 0; k < a.n_breakers && !brk; ++k) brk = a.dry_breakers[k] == id;
+    win[i] = brk ? kBreak : (uint32_t)id;
+  }
+  for (int k = tid; k < kDryHashSlots; k += kLongNT) { hkey[k] = kEmpty; hlen[k] = 0u; }
+  __syncthreads();  // also orders the penalised values above before the DRY updates below
+  for (int64_t j = 1 + tid; j < N; j += kLongNT) {
+    const uint32_t t = win[j];
+    if (t == kBreak) continue;
+    int64_t n = 0;
+    while (n < j) {
+      const uint32_t x = win[j - 1 - n];
+      if (x == kBreak || x != win[N - 1 - n]) break;
+      ++n;
+    }
+    if (n == 0) continue;
+    uint32_t h = (t * 2654435761u) >> 20 & (kDryHashSlots - 1);  // Knuth's multiplicative hash
+    for (;;) {
+      const uint32_t old = atomicCAS(&hkey[h], kEmpty, t);
+      if (old == kEmpty || old == t) {
+        atomicMax(&hlen[h], (uint32_t)n);
+        break;
+      }
+      h = (h + 1u) & (kDryHashSlots - 1);
+    }
+  }
+  __syncthreads();
+  const float base = D.base, mult = D.multiplier;
+  for (int k = tid; k < kDryHashSlots; k += kLongNT) {
+    const uint32_t t = hkey[k], n = hlen[k];
+    if (t == kEmpty || n < (uint32_t)D.allowed_length) continue;
+    float v = 1.0f;
+    for (uint32_t i = (uint32_t)D.allowed_length; i < n; ++i) {
+      v = v * base;
+      if (!__builtin_isfinite(v)) break;
+    }
+    zc[t] = zc[t] - mult * v;
+  }
+}
+
+hipError_t launch_sample_rows(const SampleArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream);
+
 hipError_t launch_sample(const SampleArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream) {
+  hipError_t e = launch_sample_rows(a, dtype, B, vec, stream);
+  if (e != hipSuccess || a.long_ws == nullptr) return e;
+  if (dtype == ARCS_DTYPE_BF16) hipLaunchKernelGGL(long_history_prep_kernel<true>, dim3((unsigned)B), dim3(kLongNT), 0, stream, a);
+  else hipLaunchKernelGGL(long_history_prep_kernel<false>, dim3((unsigned)B), dim3(kLongNT), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the handed-over rows from their binary32 copies, penalties done
+  SampleArgs g = a;
+  g.logits = a.long_ws;
+  g.stride = a.V;
+  g.hist_ids = nullptr;
+  g.hist_offsets = nullptr;
+  g.dry = nullptr;
+  g.pen_tables = 0;
+  g.bitmap_words = 0;
+  g.split_parts = nullptr;
+  g.split_P = 0;
+  g.long_ws = nullptr;
+  g.deferred_only = 1;
+  static std::atomic<int> done[2];
+  const size_t lds = sample_lds_bytes(false, false, a.V);
+  return a.V % 4 == 0 ? launch_one(sample_kernel<false, true, false>, false, kNT, g, B, lds, stream, done[0])
+                      : launch_one(sample_kernel<false, false, false>, false, kNT, g, B, lds, stream, done[1]);
+}
+
+hipError_t launch_sample_rows(const SampleArgs& a, int dtype, int64_t B, bool vec, hipStream_t stream) {
   const bool pen = a.pen_tables != 0;
   static std::atomic<int> done[10];
   if (dtype == ARCS_DTYPE_BF16 && vec && a.V <= kSummaryMaxV && a.V % 8 == 0) {

@@ -1534,9 +1534,13 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
       });
       lds_barrier();
     } else {
-      status = ARCS_ROW_HISTORY_TOO_LONG;
+      status = a.long_ws != nullptr ? kStatusDeferLong : ARCS_ROW_HISTORY_TOO_LONG;
       pc.on = false;
     }
+  }
+  if (status == kStatusDeferLong) {
+    if (tid == 0) a.out_ids[row] = kDeferredId;
+    return false;
   }
   if (status != ARCS_ROW_OK) {
     write_row_failure<kSNT>(a, row, status);

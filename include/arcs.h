@@ -66,12 +66,17 @@ enum {
   ARCS_ROW_BAD_MIN_P = 3,            /* min_p NaN, < 0 or > 1                   */
   ARCS_ROW_BAD_PENALTY = 4,          /* non-finite penalty, or repetition < 0   */
   ARCS_ROW_BAD_FLAGS = 5,            /* flags has a bit other than ARCS_ROW_TIES_WIDE */
-  ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY distinct ids */
-  ARCS_ROW_VOCAB_TOO_LARGE = 7       /* penalties active and V > ARCS_MAX_PENALTY_VOCAB */
+  ARCS_ROW_HISTORY_TOO_LONG = 6,     /* penalties active, > ARCS_MAX_HISTORY distinct ids,
+                                        and no long-history workspace */
+  ARCS_ROW_VOCAB_TOO_LARGE = 7       /* penalties active, V > ARCS_MAX_PENALTY_VOCAB,
+                                        and no long-history workspace */
 };
 
 /* Limits of the penalty tables kept in LDS (per row): distinct history ids
- * in [0, V) (the number of history entries itself is not limited) and V. */
+ * in [0, V) (the number of history entries itself is not limited) and V.
+ * Beyond them a penalised call needs a long-history workspace (see
+ * arcs_long_history_workspace_bytes); without one such rows get the status
+ * codes above. */
 #define ARCS_MAX_HISTORY 4096
 #define ARCS_MAX_PENALTY_VOCAB 262144
 
@@ -314,6 +319,24 @@ int arcs_sample_hybrid_nucleus(const void* logits, int dtype, int64_t B, int64_t
  * arcs_sample_debug need for this shape: B * P * 16 for the split batches
  * described under arcs_sample, else 0. */
 size_t arcs_sample_workspace_bytes(int64_t B, int64_t V, int dtype);
+
+/*
+ * arcs_long_history_workspace_bytes: B * V * 4 (saturating).  A call with
+ * history arrays (arcs_sample, arcs_sample_keyed, arcs_sample_debug,
+ * arcs_sample_dry) whose workspace is at least this large and 16-byte aligned
+ * samples rows whose active penalties the LDS tables cannot hold (more than
+ * ARCS_MAX_HISTORY distinct history ids, or V > ARCS_MAX_PENALTY_VOCAB)
+ * instead of failing them: such a row's penalised logits (repetition,
+ * frequency and presence, Arc PR #222 page, section 3(a); and the
+ * DRY record if active) are written in binary32 to the row's slice of the
+ * workspace (offset row * V * 4) and the general pipeline samples that copy,
+ * in two more launches on the same stream that other rows leave at once.
+ * The results equal the table path's.  The workspace is owned by the caller,
+ * not read before it is written, and shared only by calls ordered on one
+ * stream; smaller workspaces (or none) keep the status codes
+ * ARCS_ROW_HISTORY_TOO_LONG / ARCS_ROW_VOCAB_TOO_LARGE.
+ */
+size_t arcs_long_history_workspace_bytes(int64_t B, int64_t V);
 
 /* Human-readable text for an arcs_status or ARCS_ROW_* code. */
 const char* arcs_status_string(int code);

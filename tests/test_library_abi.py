@@ -20,7 +20,7 @@ def test_header_declares_the_boundary():
     for name in ("arcs_argmax", "arcs_sample", "arcs_sample_keyed", "arcs_sample_workspace_bytes",
                  "arcs_status_string", "arcs_sample_debug", "arcs_version", "arcs_top_logprobs",
                  "arcs_commit_tokens", "arcs_sample_noalloc", "arcs_sample_hybrid_nucleus",
-                 "arcs_sample_dry"):
+                 "arcs_sample_dry", "arcs_long_history_workspace_bytes"):
         assert name in fns
 
 
@@ -76,6 +76,10 @@ def test_host_validation_rejects_before_launch(arcs):
         assert W(B, 129_280, 0) == B * min(128, max(8, -(-512 // B))) * 16
     assert W(65, 129_280, 0) == 0 and W(4, 129_280, 1) == 0 and W(4, 8184, 0) == 0
     assert W(4, 131_080, 0) == 0 and W(4, 20_004, 0) == 0 and W(4, 8192, 0) == 4 * 128 * 16
+    # the long-history workspace: one binary32 copy of a row per row, saturating
+    L = lib.arcs_long_history_workspace_bytes
+    assert L(4, 129_280) == 4 * 129_280 * 4 and L(1, 1) == 4 and L(0, 10) == 0 and L(3, 0) == 0
+    assert L(2**31 - 1, 2**31 - 1) == (2**31 - 1) ** 2 * 4 and L(2**62, 2**31 - 1) == 2**64 - 1
     need = W(4, 129_280, 0)
     V = 129_280
     assert S(p, 0, 4, V, V, p, None, None, 0, 0, p, None, None, 0, None) == -6
