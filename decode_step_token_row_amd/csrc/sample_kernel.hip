@@ -102,6 +102,16 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
 // tables: one pass of the loop per history id in the group (groups without
 // one cost a bitmap read), rather than a branch per element.  The operations
 // are those of the general path's table (the same binary32 sequence).
+// Element e of the group (e differs from lane to lane) replaced by its
+// penalised value for an id seen cnt times.
+__device__ __forceinline__ void penalize_elem(float (&z)[8], int e, uint32_t cnt, const PenCtx& pc) {
+  float ze = z[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) ze = e == k ? z[k] : ze;
+  const float pz = penalize(canon_nan(ze), cnt, pc);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) z[k] = e == k ? pz : z[k];
+}
 __device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCtx& pc) {
   const uint32_t w = (uint32_t)(g0 >> 5), s5 = (uint32_t)(g0 & 31);
   const uint32_t word = pc.bitmap[w];
@@ -111,13 +121,7 @@ __device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCt
   do {
     const int e = __builtin_ctz(bits);
     bits &= bits - 1u;
-    const uint32_t cnt = pc.pcount[r++];
-    float ze = z[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) ze = e == k ? z[k] : ze;
-    const float pz = penalize(canon_nan(ze), cnt, pc);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) z[k] = e == k ? pz : z[k];
+    penalize_elem(z, e, pc.pcount[r++], pc);
   } while (bits);
 }
 

@@ -798,6 +798,10 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
   double lsum = 0.0;
   float kfr = -__builtin_inff(), negk = 0.0f;
   bool bad = false, special = false;
+  // the penalty values in vector registers: the pass's scalar registers are
+  // all taken, and scalar copies would be spilled and reloaded every round
+  PenCtx pv = pc;
+  if (PEN) asm volatile("" : "+v"(pv.pres), "+v"(pv.freq), "+v"(pv.rep));
 #pragma unroll
   for (int q = 0; q < kSQ; ++q) {
     // the round's bound is formed here, not hoisted out of the unrolled
@@ -811,7 +815,7 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
     asm volatile("" : "+v"(dq));
     float z[8];
     unpack8(dq, z);
-    if (PEN && ((pc.hmask >> q) & 1u)) penalize8(z, (int64_t)(q * kSNT + tid) * 8, pc);
+    if (PEN && ((pc.hmask >> q) & 1u)) penalize8(z, (int64_t)(q * kSNT + tid) * 8, pv);
     float g = group_max(z);
     special = special || !(g == g);
     g = valid && g == g ? g : -__builtin_inff();
