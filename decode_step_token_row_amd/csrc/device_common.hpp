@@ -233,6 +233,22 @@ __device__ __forceinline__ double exp2_f64(double t) {
   p = __builtin_fma(p, f, 1.0);
   return __builtin_ldexp(p, (int)n);
 }
+// 2^t in double precision from a table T64[j] = 2^(j/64) (j = 0..63, filled
+// by exp2_f64): t = n + j/64 + r with 64 n + j = rint(64 t) and |r| <= 1/128,
+// 2^r from its Taylor series to degree 3 (relative error below 4e-11), the
+// product scaled by 2^n.  t below -1100, and -inf, give 0; t above 1023
+// gives +inf.  Three multiply-adds and one table read in place of ten.
+__device__ __forceinline__ double exp2_f64_tab(double t, const double* T64) {
+  t = t > -1100.0 ? t : -1100.0;
+  const double s = __builtin_rint(t * 64.0);
+  const double r = __builtin_fma(s, -0.015625, t);  // t - s / 64, exact
+  const int si = (int)s;
+  double p = __builtin_fma(0x1.c6b08d704a0c0p-5, r, 0x1.ebfbdff82c58fp-3);
+  p = __builtin_fma(p, r, 0x1.62e42fefa39efp-1);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(T64[si & 63] * p, si >> 6);
+}
+
 // inclusive prefix sums across the wave (lane order)
 __device__ __forceinline__ double dpp_wave_incl_scan_f64(double v) {
   v += dpp_f64<0x111>(0.0, v);

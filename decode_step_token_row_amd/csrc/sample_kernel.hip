@@ -390,16 +390,25 @@ constexpr int kHistRegs = 4;
 // than the tail tokens' widths.  w = 2^(z c) with c = log2(e) / T and no
 // frame (the row maximum keeps |m c| <= kF64Span, else the general path).
 // The group's weights are summed in id order; both the pass and the draw
-// call this, so the draw sees the pass's values exactly.
+// call this, so the draw sees the pass's values exactly.  The powers come
+// from exp2_f64_tab, its table in LDS (fill_exp2_table first).
 constexpr double kF64Span = 960.0;
-__device__ __forceinline__ double group_weights_f64(const float (&z)[8], bool valid, double c, double (&w)[8]) {
+__device__ __forceinline__ double group_weights_f64(const float (&z)[8], bool valid, double c, double (&w)[8],
+                                                    const double* T64) {
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    w[e] = valid ? exp2_f64((double)z[e] * c) : 0.0;
+    w[e] = valid ? exp2_f64_tab((double)z[e] * c, T64) : 0.0;
     s += w[e];
   }
   return s;
+}
+// exp2_f64_tab's table, written by every wave that uses it (the same values
+// everywhere, so no workgroup barrier: each wave reads its own writes).
+__device__ __forceinline__ void fill_exp2_table(double* T64) {
+  const int lane = threadIdx.x & (kWave - 1);
+  T64[lane] = exp2_f64((double)lane * 0.015625);
+  wave_lds_sync();
 }
 
 
@@ -419,12 +428,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_partial_kernel(SampleArgs
   const int64_t row = blockIdx.y;
   const int sl = blockIdx.x, Pn = a.split_P;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  __shared__ double s_exp2[kWave];
   const arcs_row_params P = a.params[row];
   if (row_param_status(P) != ARCS_ROW_OK) return;
   const bool greedy = P.temperature == 0.0f || P.top_k == 1;
   const bool nofilter = !greedy && !(P.top_k >= 1 && (int64_t)P.top_k < a.V) && !(P.top_p < 1.0f) &&
                         !(P.min_p > 0.0f);
   if (!greedy && !nofilter) return;
+  if (nofilter) fill_exp2_table(s_exp2);
   float chi = 0.0f, clo = 0.0f;
   if (nofilter && !temp_coeffs(P.temperature, chi, clo)) return;
   const double c = (double)chi + (double)clo;
@@ -446,7 +457,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_partial_kernel(SampleArgs
     }
     if (nofilter) {
       double w8[8];
-      sum += group_weights_f64(z, true, c, w8);
+      sum += group_weights_f64(z, true, c, w8, s_exp2);
     }
   }
   const float wm = dpp_wave_max_f32(best);

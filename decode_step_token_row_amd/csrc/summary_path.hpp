@@ -221,7 +221,7 @@ __device__ __forceinline__ bool nofilter_draw(const SampleArgs& a, int64_t row, 
     unpack8(uniform_round(d, qs), z);
     if (PEN && pc.on && valid) penalize8(z, (int64_t)(qs * kSNT + tid) * 8, pc);
     double w8[8];
-    const double g = group_weights_f64(z, valid, c, w8);
+    const double g = group_weights_f64(z, valid, c, w8, (const double*)sm.skey);
     const double incl = dpp_wave_incl_scan_f64(g);
     const double prev = __shfl_up(incl, 1);
     const uint64_t hit = __ballot(g > 0.0 && bw + incl > t);
@@ -829,7 +829,7 @@ __device__ __forceinline__ void row_pass(const u32x4 (&d)[kSQ], int ngroups, con
     if (W == 0) continue;
     if (W == 3) {
       double w8[8];
-      const double gw = group_weights_f64(z, valid, c64, w8);
+      const double gw = group_weights_f64(z, valid, c64, w8, (const double*)sm.skey);
       const double incl = dpp_wave_incl_scan_f64(gw);
       if ((tid & (kWave - 1)) == kWave - 1) ((double*)sm.tsum)[q * kSNW + tid / kWave] = incl;
       continue;
@@ -1044,7 +1044,13 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // (greedy rows take the group-maxima pass and find the element afterwards)
   PassOut po;
   float gm[kSQ];  // filter rows: the maximum of each of the thread's groups
-  if (nofilter) row_pass<PEN, 3, true>(d, ngroups, pc, sm, chi, clo, po, gm);
+  if (nofilter) {
+    // the power table of the double weights in the small-sort area (unused by
+    // rows without filters)
+    static_assert((size_t)kSmallSort * 8 >= (size_t)kWave * 8, "the power table fits the small-sort keys");
+    fill_exp2_table((double*)sm.skey);
+    row_pass<PEN, 3, true>(d, ngroups, pc, sm, chi, clo, po, gm);
+  }
   else if (weights && !lazy) row_pass<PEN, 2, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   else row_pass<PEN, 0, false>(d, ngroups, pc, sm, chi, clo, po, gm);
   const float best = po.best;
@@ -1562,7 +1568,7 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
 // false (uniformly) when a slice saw NaN or +inf, or the weights' exponent
 // range does not hold the row: the row then takes the whole-row path.
 __device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, const arcs_row_params& P,
-                                             const RowConsts& rc, Shared& sh) {
+                                             const RowConsts& rc, const Smem& sm, Shared& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int Pn = a.split_P;
   const int64_t V = a.V;
@@ -1622,6 +1628,7 @@ __device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, c
   __syncthreads();
   const int32_t mode = sh.i32[0];
   if (mode != 2) return mode == 1;
+  fill_exp2_table((double*)sm.skey);  // the slice's double weights, as in the slice kernel
   const int sstar = sh.i32[1];
   double base = sh.f64[0];
   const double t = sh.f64[1];
@@ -1633,7 +1640,7 @@ __device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, c
     float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if (valid) unpack8(rv[g], z);
     double w8[8];
-    const double gw = group_weights_f64(z, valid, c, w8);
+    const double gw = group_weights_f64(z, valid, c, w8, (const double*)sm.skey);
     const double incl = dpp_wave_incl_scan_f64(gw);
     if (lane == kWave - 1) sh.rtot[wid] = incl;
     if (gw > 0.0) atomicMax(&sh.i32[2], g);
@@ -1699,7 +1706,7 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
                             !(P.min_p > 0.0f);
       if (row_param_status(P) == ARCS_ROW_OK && (greedy || nofilter)) {
         const RowConsts rc = row_consts(P, load_row_rng(a, row), row);
-        if (rc.ok && split_finish(a, row, P, rc, sh)) return;
+        if (rc.ok && split_finish(a, row, P, rc, sm, sh)) return;
         __syncthreads();
       }
     }
