@@ -109,7 +109,10 @@ def kernel_name(w) -> str:
     if w.greedy_only:
         return "argmax_fast_kernel" if fits else "argmax_kernel"
     if fits:
-        return "sample_summary_kernel"
+        # small batches without history arrays read their greedy and
+        # unfiltered rows split over many workgroups first
+        split = w.B <= 64 and 8192 <= w.V and w.hist_ids is None
+        return "split_partial_kernel + sample_summary_kernel" if split else "sample_summary_kernel"
     if w.dtype == "f32" and w.V % 4 == 0 and w.V <= 131072 and w.hist_ids is None:
         return "sample_f32_kernel (+ sample_kernel for deferred rows)"
     return "sample_kernel"
