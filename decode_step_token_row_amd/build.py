@@ -1,9 +1,12 @@
 """Compile libarcs.so (HIP kernels + C ABI) for gfx950, in-tree.
 
 Flags: -O3, no fused multiply-add contraction (the penalty arithmetic is an
-exact sequence of binary32 operations), and packed-FP32 instruction
-selection disabled.  hipcc's host pass warns that it does not know the
-packed-fp32 feature; the warning is harmless.
+exact sequence of binary32 operations), packed-FP32 instruction selection
+disabled, and a higher size limit for loops marked `#pragma unroll`: the
+register-resident row is indexed by round number, so a round loop that is
+only partly unrolled indexes it at run time and moves it to scratch memory.
+hipcc's host pass warns that it does not know the packed-fp32 feature; the
+warning is harmless.
 """
 
 from __future__ import annotations
@@ -32,6 +35,7 @@ COMMON = [
     "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=100000",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}",
     f"-I{CSRC}",

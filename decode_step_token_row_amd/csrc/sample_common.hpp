@@ -79,7 +79,7 @@ inline size_t sample_lds_bytes(bool summary, bool pen_tables, int64_t V) {
 struct PenCtx {
   bool on;
   bool rep_on;
-  float pres, freq, rep;
+  float pres, freq, rep;   // a factor or term that is off holds its neutral value (set_penalty_values)
   const uint32_t* bitmap;
   const uint16_t* wprefix;
   const float* zpen;       // general path: penalised logit per distinct id
@@ -94,10 +94,25 @@ __device__ __forceinline__ uint32_t pen_rank(uint32_t id, const uint32_t* bitmap
   return (uint32_t)wprefix[w] + (uint32_t)__builtin_popcount(bitmap[w] & ((1u << (id & 31)) - 1u));
 }
 
+// The row's penalty values.  One that is off is stored as its neutral value:
+// a repetition factor of 1 (z / 1 and z * 1 are z), frequency and presence
+// terms of +0 (z - (+0) is z for every binary32 z, -0 and the infinities
+// included).  The penalty then runs the same three steps on every row, with
+// no branch, and gives the values of the steps it would otherwise skip.
+__device__ __forceinline__ void set_penalty_values(PenCtx& pc, const arcs_row_params& P) {
+  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
+  pc.rep = pc.rep_on ? P.repetition : 1.0f;
+  pc.freq = P.frequency != 0.0f ? P.frequency : 0.0f;
+  pc.pres = P.presence != 0.0f ? P.presence : 0.0f;
+}
+
+// Penalised logit of an id seen c times (z already canonical: no NaN):
+// repetition (divide positive logits, multiply the others), then frequency,
+// then presence, each an exact binary32 operation (no FMA).
 __device__ __forceinline__ float penalize(float z, uint32_t c, const PenCtx& pc) {
-  if (pc.rep_on) z = (z > 0.0f) ? z / pc.rep : z * pc.rep;
-  if (pc.freq != 0.0f) z = z - pc.freq * (float)c;
-  if (pc.pres != 0.0f) z = z - pc.pres;
+  z = (z > 0.0f) ? z / pc.rep : z * pc.rep;
+  z = z - pc.freq * (float)c;
+  z = z - pc.pres;
   return z;
 }
 
@@ -507,8 +522,7 @@ __device__ __forceinline__ bool row_prologue(const SampleArgs& a, int64_t row, c
 
   pc.on = false;
   pc.dry_on = false;
-  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
-  pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  set_penalty_values(pc, P);
   pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   int64_t h0 = 0, h1 = 0;
   if (!NOHIST && status == ARCS_ROW_OK && a.hist_ids != nullptr) {

@@ -97,11 +97,6 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&z)[8]) {
 }
 
 
-// The history ids among the 8 elements of the group at g0 (a multiple of 8)
-// are penalised from their own logit and their occurrence count in the LDS
-// tables: one pass of the loop per history id in the group (groups without
-// one cost a bitmap read), rather than a branch per element.  The operations
-// are those of the general path's table (the same binary32 sequence).
 // Element e of the group (e differs from lane to lane) replaced by its
 // penalised value for an id seen cnt times.
 __device__ __forceinline__ void penalize_elem(float (&z)[8], int e, uint32_t cnt, const PenCtx& pc) {
@@ -112,6 +107,12 @@ __device__ __forceinline__ void penalize_elem(float (&z)[8], int e, uint32_t cnt
 #pragma unroll
   for (int k = 0; k < 8; ++k) z[k] = e == k ? pz : z[k];
 }
+
+// The history ids among the 8 elements of the group at g0 (a multiple of 8)
+// replaced by their penalised values, from their own logit and their
+// occurrence count in the LDS tables (the general path's binary32 sequence):
+// one pass of the loop per history id in the group (groups without one cost
+// a bitmap read).
 __device__ __forceinline__ void penalize8(float (&z)[8], int64_t g0, const PenCtx& pc) {
   const uint32_t w = (uint32_t)(g0 >> 5), s5 = (uint32_t)(g0 & 31);
   const uint32_t word = pc.bitmap[w];
@@ -1394,8 +1395,7 @@ __global__ __launch_bounds__(kLongNT) void long_history_prep_kernel(SampleArgs a
   float* zc = a.long_ws + row * V;
   const arcs_row_params P = a.params[row];
   PenCtx pc;
-  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
-  pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  set_penalty_values(pc, P);
   const int64_t h0 = a.hist_offsets[row], h1 = a.hist_offsets[row + 1];
   for (int64_t i = tid; i < V; i += kLongNT) cnt[i] = 0u;
   __syncthreads();

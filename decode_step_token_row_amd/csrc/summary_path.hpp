@@ -1454,8 +1454,7 @@ __device__ __forceinline__ int load_row_history(const SampleArgs& a, int64_t row
   if (status == ARCS_ROW_OK) status = dry_status(a, row, dry_on);
   pc.on = false;
   pc.dry_on = false;
-  pc.rep_on = !(P.repetition == 1.0f || P.repetition == 0.0f);
-  pc.pres = P.presence; pc.freq = P.frequency; pc.rep = P.repetition;
+  set_penalty_values(pc, P);
   pc.zpen = nullptr; pc.pcount = nullptr;
   hs.h0 = 0; hs.h1 = 0;
   if (status == ARCS_ROW_OK && a.hist_ids != nullptr) {
