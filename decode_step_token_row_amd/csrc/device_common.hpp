@@ -191,26 +191,37 @@ __device__ __forceinline__ float dpp_wave_max_f32(float v) {
 // workgroup; the other lanes hold the identity): three butterfly steps inside
 // the first half-row, the result read from lane 0.  Same pairing as the first
 // three steps of the whole-wave versions, so sums come out identical.
+// N = 16: a fourth step over the row of 16 lanes (row_mirror: lane i reads
+// lane 15 - i, which after the first three holds the other octet's result).
+template <int N = 8>
 __device__ __forceinline__ float dpp_octet_max_f32(float v) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
   const float ni = -__builtin_inff();
   float t;
   t = dpp_f32<0xB1>(ni, v); v = v > t ? v : t;
   t = dpp_f32<0x4E>(ni, v); v = v > t ? v : t;
   t = dpp_f32<0x141>(ni, v); v = v > t ? v : t;
+  if constexpr (N == 16) { t = dpp_f32<0x140>(ni, v); v = v > t ? v : t; }
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
 }
+template <int N = 8>
 __device__ __forceinline__ double dpp_octet_sum_f64(double v) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
   v += dpp_f64<0xB1>(0.0, v);
   v += dpp_f64<0x4E>(0.0, v);
   v += dpp_f64<0x141>(0.0, v);
+  if constexpr (N == 16) v += dpp_f64<0x140>(0.0, v);
   return readlane_f64(v, 0);
 }
+template <int N = 8>
 __device__ __forceinline__ uint32_t dpp_octet_min_u32(uint32_t v) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
   const uint32_t id = 0xFFFFFFFFu;
   uint32_t t;
   t = dpp_u32<0xB1>(id, v); v = v < t ? v : t;
   t = dpp_u32<0x4E>(id, v); v = v < t ? v : t;
   t = dpp_u32<0x141>(id, v); v = v < t ? v : t;
+  if constexpr (N == 16) { t = dpp_u32<0x140>(id, v); v = v < t ? v : t; }
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
 }
 // 2^t in double precision: t = n + f with n = rint(t) and |f| <= 1/2, 2^f

@@ -501,6 +501,13 @@ namespace sum512 {
 constexpr int kSNT = 512;
 #include "summary_path.hpp"
 }  // namespace sum512
+// Rows with active penalties: 1024 threads of 16 rounds each.  Their row is
+// latency-bound (history ids, tables, the per-round lookups, the cut), and
+// twice the waves halve each thread's share of those steps.
+namespace sum1024 {
+constexpr int kSNT = 1024;
+#include "summary_path.hpp"
+}  // namespace sum1024
 
 // ---------------------------------------------------------------------------
 // fp32 kernel
@@ -1500,7 +1507,7 @@ hipError_t launch_sample_rows(const SampleArgs& a, int dtype, int64_t B, bool ve
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    return pen ? launch_one(sum512::sample_summary_kernel<true>, true, sum512::kSNT, a, B, lds, stream, done[0])
+    return pen ? launch_one(sum1024::sample_summary_kernel<true>, true, sum1024::kSNT, a, B, lds, stream, done[0])
                : launch_one(sum512::sample_summary_kernel<false>, true, sum512::kSNT, a, B, lds, stream, done[1]);
   }
   if (dtype == ARCS_DTYPE_F32 && vec && !pen && a.V <= kF32MaxV && a.V % 4 == 0) {

@@ -1093,8 +1093,9 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
   // every wave, so no second barrier broadcasts them)
   const bool rin = lane < kSNW;
   const float rm = rin ? sh.w_max[lane] : -__builtin_inff();
-  static_assert(kSNW <= 8, "one record per lane of the first half-row");
-  const float m0 = dpp_octet_max_f32(rm);
+  static_assert(kSNW <= 16, "one record per lane of the first row of 16 lanes");
+  constexpr int kRecLanes = kSNW <= 8 ? 8 : 16;
+  const float m0 = dpp_octet_max_f32<kRecLanes>(rm);
   int32_t mode = kModeFallback;
   float negks = 0.0f, zt = -__builtin_inff(), zc0 = -FLT_MAX;
   double S = 0.0;  // a lower bound of the row's mass while `lazy`
@@ -1104,7 +1105,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
     mode = kModeFallback;  // a signalling NaN or an out-of-range exponent frame
   } else if (greedy) {
     mode = kModeGreedy;
-    argmax = m0 > -__builtin_inff() ? dpp_octet_min_u32(rin && rm == m0 ? sh.w_arg[lane] : 0xFFFFFFFFu) : 0u;
+    argmax = m0 > -__builtin_inff() ? dpp_octet_min_u32<kRecLanes>(rin && rm == m0 ? sh.w_arg[lane] : 0xFFFFFFFFu) : 0u;
   } else if (m0 > -__builtin_inff() && m0 < __builtin_inff() && m0 * chi > -1048576.0f && m0 * chi < 1048576.0f) {
     // (all -inf rows, +inf, or a maximum too large for the exponent frame: general path)
     negks = -__builtin_floorf(m0 * chi);
@@ -1115,7 +1116,7 @@ __device__ __forceinline__ bool stream_row(const SampleArgs& a, int64_t row, con
       bool ok = true;
       if (pon) {
         const double x = rin ? __builtin_ldexp(sh.w_sum[lane], (int)(negks - sh.w_negk[lane])) : 0.0;
-        S = dpp_octet_sum_f64(x);
+        S = dpp_octet_sum_f64<kRecLanes>(x);
         ok = S > 0.0 && S < 1e300;
         Pm = (double)P.top_p * S;
       }
@@ -1507,11 +1508,12 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
   const int tid = threadIdx.x;
   pc.bitmap = sm.bitmap; pc.wprefix = sm.wprefix; pc.zpen = sm.zpen; pc.pcount = sm.pcount;
   pc.hmask = 0u;
-  // per thread, the rounds whose group holds a history id (kept in the bound
-  // histogram's area, free until after the pass): the pass looks up the
+  // per thread, the rounds whose group holds a history id (kept in the group
+  // value area, where the pass writes each thread's entry of round 0 only
+  // after reading it): the pass looks up the
   // tables only in those rounds
-  static_assert((size_t)kBins * 8 >= (size_t)kSNT * 4 && kSQ <= 32, "a history round mask per thread");
-  uint32_t* hm = sm.bcnt;
+  static_assert((size_t)kMaxGroups >= (size_t)kSNT && kSQ <= 32, "a history round mask per thread");
+  uint32_t* hm = (uint32_t*)sm.tsum;
   if (status == ARCS_ROW_OK && pc.on) {
     const uint32_t bw = a.bitmap_words;
     for (uint32_t i = tid; i < bw; i += kSNT) sm.bitmap[i] = 0u;
