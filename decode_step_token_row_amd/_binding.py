@@ -51,6 +51,7 @@ ROW_HISTORY_TOO_LONG = 6
 ROW_VOCAB_TOO_LARGE = 7
 MAX_HISTORY = 4096
 MAX_PENALTY_VOCAB = 262144
+TOP_LOGPROBS_MAX_VOCAB = 262144  # ARCS_TOP_LOGPROBS_MAX_VOCAB
 
 PATH_GREEDY = 1
 PATH_SORT_SKIP = 2

@@ -30,7 +30,7 @@
 //
 // The units of those n threads are read again (from cache), spread over the
 // whole workgroup, and their elements with coarse key at or above beta are
-// gathered into LDS with their exact keys (at most n * 128); each
+// gathered into LDS with their exact keys (at most n * 256); each
 // candidate's rank among the candidates is its position in the output.
 #include <atomic>
 #include <type_traits>
@@ -42,7 +42,7 @@ namespace arcs {
 
 constexpr int kLpNT = 1024;
 constexpr int kLpNW = kLpNT / kWave;
-constexpr int kLpPerThread = 128;                                  // elements a thread owns at most
+constexpr int kLpPerThread = 256;                                  // elements a thread owns at most
 static_assert((int64_t)kLpNT * kLpPerThread == ARCS_TOP_LOGPROBS_MAX_VOCAB, "vocabulary bound");
 constexpr int kLpCap = ARCS_MAX_TOP_LOGPROBS * kLpPerThread;       // candidates at most
 constexpr int kLpBatch = 16;                                       // loads in flight per thread

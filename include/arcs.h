@@ -89,7 +89,7 @@ enum {
 
 /* Limits of arcs_top_logprobs: entries per row, and V. */
 #define ARCS_MAX_TOP_LOGPROBS 64
-#define ARCS_TOP_LOGPROBS_MAX_VOCAB 131072
+#define ARCS_TOP_LOGPROBS_MAX_VOCAB 262144
 
 /*
  * Per-row sampling parameters, 32 bytes, device array of B records.

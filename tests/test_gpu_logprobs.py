@@ -135,11 +135,13 @@ def test_top_logprobs_short_rows_and_bad_temperatures(arcs):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("aligned", [True, False])
-def test_top_logprobs_many_candidates(arcs, dtype, aligned):
+@pytest.mark.parametrize("V", [131_072, 262_144])
+def test_top_logprobs_many_candidates(arcs, dtype, aligned, V):
     # 64 threads own nothing but large values, one of them only its smallest:
     # every element of the other 63 is at or above the 64th thread maximum,
-    # so about 63 * 128 elements are gathered (the rank-count path)
-    V, n = 131_072, 64
+    # so about 63 * V / 1024 elements are gathered (the rank-count path; at
+    # the largest V that is almost the whole candidate area)
+    n = 64
     E = (8 if dtype == "bf16" else 4) if aligned else 1
     rng = np.random.default_rng(9)
     z = rng.normal(0, 1, (2, V)).astype(np.float32)
@@ -150,6 +152,26 @@ def test_top_logprobs_many_candidates(arcs, dtype, aligned):
     raw = f32_to_bf16_bits(z) if dtype == "bf16" else z
     ids, lps, st = _run(arcs, raw, dtype, [1.0, 0.3], n, stride=None if aligned else V + 1)
     _check(ids, lps, st, raw, dtype, [1.0, 0.3], n, where=(dtype, aligned))
+
+
+@pytest.mark.parametrize("dtype,V,aligned", [("bf16", 262_144, True), ("bf16", 200_003, False),
+                                              ("f32", 262_140, True), ("f32", 151_936, False)])
+def test_top_logprobs_vocabularies_beyond_131072(arcs, dtype, V, aligned):
+    # up to ARCS_TOP_LOGPROBS_MAX_VOCAB: each thread then owns up to 256
+    # elements; the row kinds of _rows, every id checked against the oracle
+    B, n = 5, 33
+    z = _rows(V, B, seed=V % 1000)
+    raw = f32_to_bf16_bits(z) if dtype == "bf16" else z
+    temps = [0.7, 1.0, 1.3, 0.25, 2.0]
+    ids, lps, st = _run(arcs, raw, dtype, temps, n, stride=None if aligned else V + 3)
+    _check(ids, lps, st, raw, dtype, temps, n, where=(dtype, V))
+
+
+def test_top_logprobs_vocabulary_bound(arcs):
+    import torch
+    x = torch.zeros((1, arcs.TOP_LOGPROBS_MAX_VOCAB + 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(Exception):
+        arcs.top_logprobs(x, 4)
 
 
 def test_top_logprobs_full_size_sampled_rows(arcs):

@@ -2,6 +2,7 @@
 rejects bad host arguments before launching anything (no GPU needed)."""
 
 import ctypes
+import os
 import subprocess
 
 import numpy as np
@@ -118,13 +119,13 @@ def test_host_validation_rejects_before_launch(arcs):
     assert K(p, 0, 4, 10, 10, p, None, None, ctypes.c_void_p(base + 4), 1, p, None, None, 0, None) == -8
     assert K(p, 0, 4, 10, 10, None, None, None, p, 1, p, None, None, 0, None) == -1
     assert K(p, 0, 4, 10, 9, p, None, None, p, 0, p, None, None, 0, None) == -4
-    # top logprobs: n in [1, 64], V <= 131072, both outputs required
+    # top logprobs: n in [1, 64], V <= 262144, both outputs required
     L = lib.arcs_top_logprobs
     assert L(p, 0, 4, 10, 10, None, 5, p, None, None, None) == -1
     assert L(p, 0, 4, 10, 10, None, 5, None, p, None, None) == -1
     assert L(p, 0, 4, 10, 10, None, 0, p, p, None, None) == -10
     assert L(p, 0, 4, 10, 10, None, 65, p, p, None, None) == -10
-    assert L(p, 0, 4, 131073, 131073, None, 5, p, p, None, None) == -3
+    assert L(p, 0, 4, 262145, 262145, None, 5, p, p, None, None) == -3
     assert L(p, 0, 4, 10, 10, ctypes.c_void_p(base + 2), 5, p, p, None, None) == -8
     assert L(p, 0, 4, 10, 9, None, 5, p, p, None, None) == -4
     assert L(p, 2, 4, 10, 10, None, 5, p, p, None, None) == -5
@@ -138,3 +139,14 @@ def test_host_validation_rejects_before_launch(arcs):
     assert C(p, 4, 10, None, p, p, 0, p, p, p, None) == -11
     assert C(p, 4, 10, None, ctypes.c_void_p(base + 4), p, 2, p, p, p, None) == -8
     assert C(ctypes.c_void_p(base + 2), 4, 10, None, p, p, 2, p, p, p, None) == -8
+
+
+def test_binding_constants_match_the_header():
+    """The limits the Python binding exports are the header's #defines."""
+    import re
+    import decode_step_token_row_amd as arcs
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "arcs.h")).read()
+    defs = {k: int(v) for k, v in re.findall(r"#define (ARCS_[A-Z_]+) (\d+)", src)}
+    assert defs["ARCS_MAX_HISTORY"] == arcs.MAX_HISTORY
+    assert defs["ARCS_MAX_PENALTY_VOCAB"] == arcs.MAX_PENALTY_VOCAB
+    assert defs["ARCS_TOP_LOGPROBS_MAX_VOCAB"] == arcs.TOP_LOGPROBS_MAX_VOCAB
