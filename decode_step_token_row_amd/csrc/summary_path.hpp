@@ -1568,8 +1568,28 @@ __device__ __forceinline__ bool summary_pen_tables(const SampleArgs& a, int64_t 
 // read of that slice, with the same double weights, the element.  Returns
 // false (uniformly) when a slice saw NaN or +inf, or the weights' exponent
 // range does not hold the row: the row then takes the whole-row path.
+// The row's slice partials for the first wave (lane l: slices 2l and 2l + 1,
+// P <= 128), loaded at the kernel's start together with the parameter record:
+// the record's wait then does not delay them.  Rows whose slices wrote
+// nothing (rows with filters) load stale records and never read them.
+struct SplitPre {
+  SplitPart p0, p1;
+};
+__device__ __forceinline__ SplitPre issue_split_loads(const SampleArgs& a, int64_t row) {
+  SplitPre s;
+  s.p0 = SplitPart{-__builtin_inff(), 0x7FFFFFFF, 0.0};
+  s.p1 = s.p0;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    const SplitPart* parts = a.split_parts + row * a.split_P;
+    if (2 * lane < a.split_P) s.p0 = parts[2 * lane];
+    if (2 * lane + 1 < a.split_P) s.p1 = parts[2 * lane + 1];
+  }
+  return s;
+}
+
 __device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, const arcs_row_params& P,
-                                             const RowConsts& rc, const Smem& sm, Shared& sh) {
+                                             const RowConsts& rc, const Smem& sm, Shared& sh, const SplitPre& pre) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int Pn = a.split_P;
   const int64_t V = a.V;
@@ -1579,12 +1599,9 @@ __device__ __forceinline__ bool split_finish(const SampleArgs& a, int64_t row, c
   const double c = (double)rc.chi + (double)rc.clo;
   if (wid == 0) {
     // lane l holds slices 2l and 2l + 1 (P <= 128)
-    const SplitPart* parts = a.split_parts + row * Pn;
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-    int32_t a0 = 0x7FFFFFFF, a1 = 0x7FFFFFFF;
-    double s0 = 0.0, s1 = 0.0;
-    if (2 * lane < Pn) { const SplitPart p = parts[2 * lane]; m0 = p.m; a0 = p.arg; s0 = p.s; }
-    if (2 * lane + 1 < Pn) { const SplitPart p = parts[2 * lane + 1]; m1 = p.m; a1 = p.arg; s1 = p.s; }
+    const float m0 = pre.p0.m, m1 = pre.p1.m;
+    const int32_t a0 = pre.p0.arg, a1 = pre.p1.arg;
+    const double s0 = pre.p0.s, s1 = pre.p1.s;
     const bool bad = __ballot(a0 < 0 || a1 < 0) != 0;
     const float M = dpp_wave_max_f32(max2f(m0, m1));
     const uint32_t c0 = m0 == M ? (uint32_t)a0 : 0xFFFFFFFFu, c1 = m1 == M ? (uint32_t)a1 : 0xFFFFFFFFu;
@@ -1701,13 +1718,14 @@ __global__ __launch_bounds__(kSNT) void sample_summary_kernel(SampleArgs a) {
     if (a.split_parts != nullptr) {
       // split launch: greedy rows and rows without filters finish from the
       // slice partials (this waits for the parameter record first)
+      const SplitPre pre = issue_split_loads(a, row);
       const arcs_row_params P = params_from(p0, p1);
       const bool greedy = P.temperature == 0.0f || P.top_k == 1;
       const bool nofilter = !greedy && !(P.top_k >= 1 && (int64_t)P.top_k < a.V) && !(P.top_p < 1.0f) &&
                             !(P.min_p > 0.0f);
       if (row_param_status(P) == ARCS_ROW_OK && (greedy || nofilter)) {
-        const RowConsts rc = row_consts(P, load_row_rng(a, row), row);
-        if (rc.ok && split_finish(a, row, P, rc, sm, sh)) return;
+        const RowConsts rc = row_consts(P, rng_from(a, rl), row);
+        if (rc.ok && split_finish(a, row, P, rc, sm, sh, pre)) return;
         __syncthreads();
       }
     }
