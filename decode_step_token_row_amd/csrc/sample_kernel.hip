@@ -11,11 +11,14 @@
 //     the device draw; the token id stays in device memory.
 // No full-vocabulary sort is done anywhere.
 //
-// Two kernels:
+// The kernels:
 //
-// sample_summary_kernel (bf16 rows, 16-byte aligned, V <= 131072, V % 8 == 0):
-//   the row is read from HBM exactly once, all 16 loads of 16 bytes per lane
-//   issued before any is used.  Each thread turns every group of 8 logits
+// sample_summary_kernel (bf16 rows, 16-byte aligned, V <= 131072, V % 8 == 0;
+//   512 threads, 32 rounds of 16 bytes per thread, or 1024 threads and 16
+//   rounds in launches with history arrays): the row is read from HBM
+//   exactly once, every load issued before any is used (in the penalised
+//   kernel a quarter of them before the penalty tables are built, the rest
+//   after).  Each thread turns every group of 8 logits
 //   (penalised through LDS tables when the row has active penalties) into
 //   its maximum and, for rows with top-p, its fp32 weight
 //   exp2(z*log2(e)/T - K_t) (K_t an integer reference exponent of the thread,
@@ -37,10 +40,21 @@
 //   values or temperatures, more than kCandCap candidates) run the general
 //   pipeline in the same workgroup.
 //
-// sample_kernel (everything else): the general streaming pipeline of
-//   sample_common.hpp -- pass A for max/argmax, fixed-point softmax mass,
-//   radix-select cutoff over order-preserving keys, id-order draw -- with
-//   re-walks of the row served from L2 / the Infinity Cache.
+// split_partial_kernel (batches of at most 64 bf16 rows): slices of each
+//   row read by many workgroups; the summary kernel then finishes greedy rows
+//   and rows without filters from the slice records.
+//
+// sample_f32_kernel (fp32 rows, V <= 131072): one read from HBM with a
+//   histogram of weights, one from cache gathering the crossing bin.
+//
+// long_history_prep_kernel: penalised logits of rows beyond the LDS penalty
+//   tables, written in binary32 to the caller's workspace.
+//
+// sample_kernel (everything else, and the rows the others hand back): the
+//   general streaming pipeline of sample_common.hpp -- pass A for
+//   max/argmax, fixed-point softmax mass, radix-select cutoff over
+//   order-preserving keys, id-order draw -- with re-walks of the row served
+//   from L2 / the Infinity Cache.
 #include <atomic>
 
 #include "sample_common.hpp"
