@@ -85,7 +85,7 @@ struct LpUnit {
   using Raw = typename std::conditional<VEC, u32x4, uint32_t>::type;
   static __device__ __forceinline__ Raw load(const char* rowp, int g) {
     if constexpr (VEC) {
-      return ((const u32x4*)rowp)[g];
+      return __builtin_nontemporal_load(&((const u32x4*)rowp)[g]);  // streamed: read once
     } else if constexpr (BF16) {
       return (uint32_t)((const uint16_t*)rowp)[g] << 16;
     } else {
@@ -131,12 +131,12 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   int32_t* oid = a.out_ids + row * n;
   float* olp = a.out_logprobs + row * n;
 
-  const float T = a.temperature ? a.temperature[row] : 1.0f;
-  if (!(T > 0.0f && T < __builtin_inff())) {
-    if (tid < n) { oid[tid] = -1; olp[tid] = __builtin_nanf(""); }
-    if (tid == 0 && a.out_status) a.out_status[row] = ARCS_ROW_BAD_TEMPERATURE;
-    return;
-  }
+  // the temperature is checked after the pass (a bad row runs the pass at
+  // T = 1 and drops the result), so that no branch on it sits before the
+  // row's loads
+  const float T0 = a.temperature ? a.temperature[row] : 1.0f;
+  const bool bad_t = !(T0 > 0.0f && T0 < __builtin_inff());
+  const float T = bad_t ? 1.0f : T0;
   const double cd = 1.4426950408889634 / (double)T;  // log2(e) / T
   const float c = (float)cd;
 
@@ -153,32 +153,45 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   uint32_t first = (uint32_t)tid * E;  // first id of the first unit holding mt
   for (int q0 = 0; q0 < nq; q0 += kLpBatch) {
     // unconditional loads (a lane past the row's end reads its last unit
-    // again and ignores it): a branch per load would serialise them
+    // again and ignores it), all issued before the first use: with a branch
+    // per unit, or left to the scheduler, they were spread out and waited
+    // for one by one
     typename U::Raw d[kLpBatch];
 #pragma unroll
     for (int r = 0; r < kLpBatch; ++r) {
       const int g = (q0 + r) * kLpNT + tid;
       d[r] = U::load(rowp, g < ngroups ? g : ngroups - 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // no branch on the unit: with the units' uses inside a branch the
+    // compiler moved each load into its branch, behind the previous unit's
+    // wait.  Lanes past the row's end compute on their copy of the last unit
+    // and keep nothing.
 #pragma unroll
     for (int r = 0; r < kLpBatch; ++r) {
       const int g = (q0 + r) * kLpNT + tid;
-      if (g >= ngroups) continue;
+      const bool valid = g < ngroups;
       float z[E];
       U::unpack(d[r], z);
       float gm = -__builtin_inff();
 #pragma unroll
       for (int e = 0; e < E; ++e) gm = __builtin_fmaxf(gm, z[e]);  // ignores NaN
-      if (gm > mt) {
-        s *= (double)__builtin_amdgcn_exp2f((mt - gm) * c);  // 0 when mt is -inf or gm is +inf
-        mt = gm;
-        first = (uint32_t)g * E;
-      }
+      gm = valid ? gm : -__builtin_inff();
+      const bool up = gm > mt;
+      const float f = __builtin_amdgcn_exp2f((mt - gm) * c);  // 0 when mt is -inf or gm is +inf
+      s = up ? s * (double)f : s;
+      first = up ? (uint32_t)g * E : first;
+      mt = up ? gm : mt;
       float ws = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ws += __builtin_amdgcn_exp2f((z[e] - mt) * c);
-      s += (double)ws;
+      s += valid ? (double)ws : 0.0;
     }
+  }
+  if (bad_t) {  // the same in every thread of the workgroup
+    if (tid < n) { oid[tid] = -1; olp[tid] = __builtin_nanf(""); }
+    if (tid == 0 && a.out_status) a.out_status[row] = ARCS_ROW_BAD_TEMPERATURE;
+    return;
   }
   const bool owns = tid < ngroups;
   if (owns && !(s == s && __builtin_fabsf(mt) < __builtin_inff())) {
