@@ -182,9 +182,12 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
       s = up ? s * (double)f : s;
       first = up ? (uint32_t)g * E : first;
       mt = up ? gm : mt;
+      // z c - mt c in one fma (the logprobs' error budget holds the
+      // difference of one rounding)
+      const float nmc = -(mt * c);
       float ws = 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) ws += __builtin_amdgcn_exp2f((z[e] - mt) * c);
+      for (int e = 0; e < E; ++e) ws += __builtin_amdgcn_exp2f(__builtin_fmaf(z[e], c, nmc));
       s += valid ? (double)ws : 0.0;
     }
   }
@@ -249,18 +252,22 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
 #pragma unroll
     for (int w = 1; w < kLpNW; ++w) lb = s_wbound[w] > lb ? s_wbound[w] : lb;
     {
-      // the 8th largest wave value of p8: raise lb to it (ties count once each)
-      uint64_t v[kLpNW];
+      // the 8th largest wave value of p8: raise lb to it (ties count once
+      // each).  Lane w < 16 ranks wave w's value against the others; the
+      // lane of rank 7 holds it.
+      const int wl = lane < kLpNW ? lane : 0;
+      const uint64_t vw = s_wbound8[wl];
+      int above = 0;  // values strictly above vw, and equal ones before it
 #pragma unroll
-      for (int w = 0; w < kLpNW; ++w) v[w] = s_wbound8[w];
-      uint64_t x = 0ull;
-#pragma unroll
-      for (int w = 0; w < kLpNW; ++w) {
-        int above = 0;  // values strictly above v[w], and equal ones before it
-#pragma unroll
-        for (int u = 0; u < kLpNW; ++u) above += (v[u] > v[w] || (v[u] == v[w] && u < w)) ? 1 : 0;
-        x = above == 7 ? v[w] : x;
+      for (int u = 0; u < kLpNW; ++u) {
+        const uint64_t vu = s_wbound8[u];
+        above += (vu > vw || (vu == vw && u < wl)) ? 1 : 0;
       }
+      const uint64_t sel = __ballot(lane < kLpNW && above == 7);
+      const int sl = __builtin_ctzll(sel | (1ull << 63));  // exactly one lane of rank 7
+      const uint64_t x = sel ? ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(vw >> 32), sl) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)vw, sl)
+                             : 0ull;
       lb = x > lb ? x : lb;
     }
     const bool keep = owns && tkey >= lb;
