@@ -227,8 +227,12 @@ __global__ __launch_bounds__(kLpNT, 1) void top_logprobs_kernel(LogprobArgs a) {
   if (!few) {
     const int n8 = (n + 7) / 8;
     const uint32_t th = (uint32_t)(tkey >> 32);
+    // bf16 values: the low 16 bits of every value key are equal for one sign
+    // (0 for positive values, all ones for negative ones), so the descent
+    // stops at bit 16: the bound it gives keeps the same keys
+    constexpr int kLowBit = BF16 ? 16 : 0;
 #pragma unroll
-    for (int b = 31; b >= 0; --b) {
+    for (int b = 31; b >= kLowBit; --b) {
       const uint32_t c1 = p | (1u << b), c8 = p8 | (1u << b);
       p = __builtin_popcountll(__ballot(th >= c1)) >= n ? c1 : p;
       p8 = __builtin_popcountll(__ballot(th >= c8)) >= n8 ? c8 : p8;
